@@ -1,0 +1,39 @@
+"""CPU oracle for the top-k sparse MLA decode path.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, fp64 statement of
+what the GPU path computes.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import it; the product path (the HIP
+library and its Python binding) never does, and this package imports nothing
+from the product path.
+
+Sources (page titles as published):
+  * "HiSparse" walkthrough (devpress.csdn.net) -- hot buffer, swap-in phases.
+  * "5.1.1 · 从索引到 Kernel" (PaperTrace) -- index normalisation, online
+    softmax, split-KV merge (equations (1)-(21)).
+  * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" -- decode
+    attention definition, partition combine, shifted causal mask.
+
+Pin status (what fixes each function other than itself) is listed in each
+module header.  Every function here is pinned; none is "parity unpinned".
+"""
+
+from .normalize import candidate_set, normalize, block_view
+from .hot_buffer import HotState, hot_lookup_swapin, hot_reset, backup_rows
+from .attention import (
+    bf16_bits_to_f64,
+    attend_sparse,
+    attend_partial,
+    attend_dense_masked,
+    attend_fsum,
+    shifted_causal_mask,
+    split_ranges,
+)
+from .merge import merge, merge_normalized
+
+__all__ = [
+    "candidate_set", "normalize", "block_view",
+    "HotState", "hot_lookup_swapin", "hot_reset", "backup_rows",
+    "bf16_bits_to_f64", "attend_sparse", "attend_partial", "attend_dense_masked",
+    "attend_fsum", "shifted_causal_mask", "split_ranges",
+    "merge", "merge_normalized",
+]

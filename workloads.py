@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and lays them out; it holds none of
+the method's arithmetic (no normalisation, lookup, attention or merge), so
+both the GPU path's tests and the CPU oracle may consume what it produces.
+
+Workload shapes follow the decode settings described by the pages (top-k
+sparse MLA decode over a paged latent KV cache, DeepSeek-V3.2-like shapes):
+bf16 rows of 576 values (512 latent + 64 rope), one latent KV head shared by
+all query heads, page size 64, random page tables over a shared pool, top-k
+2048 plus a 128-token local window and 4 sink tokens.  No trained weights or
+indexer traces exist here, so values are N(0, 1) and the top-k ids are
+uniform draws (or clustered runs) with the stated statistics.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+
+
+def bf16_bits(x):
+    """Round float32 values to bf16 (nearest, ties to even) and return the bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def normal_bf16(rng, shape):
+    return bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+@dataclass
+class DecodeCase:
+    """One batch of decode inputs (host numpy arrays, bf16 as uint16 bits)."""
+    name: str
+    q_bits: np.ndarray            # [T, H, 576] uint16
+    topk: np.ndarray              # [T, top_k] int32, -1 padded
+    req_id: np.ndarray            # [T] int32
+    q_pos: np.ndarray             # [T] int32
+    block_table: np.ndarray       # [R, max_blocks] int32, -1 = unmapped
+    page_size: int
+    window: int
+    num_sinks: int
+    cap: int
+    kv_rows: int                  # rows in the latent KV pool
+    pool_seed: int                # seed of the pool values (see pool_bits / pool_torch)
+    scale: float = 1.0 / math.sqrt(D_QK)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def T(self):
+        return self.q_bits.shape[0]
+
+    @property
+    def H(self):
+        return self.q_bits.shape[1]
+
+    @property
+    def top_k(self):
+        return self.topk.shape[1]
+
+
+def pool_bits(rows, seed, chunk_rows=1 << 16):
+    """Latent KV pool [rows, 576] as bf16 bits, generated on the host (numpy)."""
+    out = np.empty((rows, D_QK), dtype=np.uint16)
+    ss = np.random.SeedSequence(seed)
+    for c, child in enumerate(ss.spawn(-(-rows // chunk_rows))):
+        lo = c * chunk_rows
+        hi = min(rows, lo + chunk_rows)
+        out[lo:hi] = normal_bf16(np.random.default_rng(child), (hi - lo, D_QK))
+    return out
+
+
+def pool_torch(rows, seed, device, chunk_rows=1 << 18):
+    """Latent KV pool [rows, 576] bf16 generated directly in device memory.
+
+    Uses torch's seeded generator on the device (values N(0, 1), rounded to
+    bf16 by torch's conversion).  For pools too large to build on the host.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    pool = torch.empty((rows, D_QK), dtype=torch.bfloat16, device=device)
+    for lo in range(0, rows, chunk_rows):
+        hi = min(rows, lo + chunk_rows)
+        pool[lo:hi] = torch.randn((hi - lo, D_QK), generator=g, device=device, dtype=torch.float32)
+    return pool
+
+
+def _uniform_without_replacement(rng, n, k):
+    return rng.choice(n, size=k, replace=False).astype(np.int32)
+
+
+def tiny_case(seed=1000):
+    """One request, context 256, page 64 (4 of 16 physical pages), 16 heads.
+
+    32 dynamic ids: 28 distinct uniform draws plus 4 forced duplicates of
+    members, shuffled; window 8, sinks 4.
+    """
+    rng = np.random.default_rng(seed)
+    ctx, P, H = 256, 64, 16
+    table = rng.permutation(16)[: ctx // P].astype(np.int32)[None, :]
+    distinct = rng.choice(ctx, size=28, replace=False)
+    dups = rng.choice(distinct, size=4, replace=False)
+    topk = rng.permutation(np.concatenate([distinct, dups])).astype(np.int32)[None, :]
+    q = normal_bf16(rng, (1, H, D_QK))
+    return DecodeCase("tiny", q, topk, np.zeros(1, np.int32), np.full(1, ctx - 1, np.int32),
+                      table, P, 8, 4, 32 + 8 + 4, 16 * P, pool_seed=seed + 1)
+
+
+def deepseek_case(seed=2000, batch=32, ctx=32768, heads=128, top_k=2048, window=128,
+                  sinks=4, page_size=64, pool_pages=None, variant=0):
+    """Batch of decode tokens, one per request, shaped like DeepSeek-V3.2 MLA.
+
+    Page tables are disjoint random page sets from one shared pool; the top-k
+    ids are uniform without replacement over the causal range.  `variant`
+    changes only the top-k draws (same pool, tables and queries), so a
+    benchmark can rotate candidate sets whose union exceeds on-chip caches.
+    """
+    rng = np.random.default_rng(seed)
+    pages_per_req = -(-ctx // page_size)
+    if pool_pages is None:
+        pool_pages = batch * pages_per_req
+    tables = rng.permutation(pool_pages)[: batch * pages_per_req].astype(np.int32)
+    tables = tables.reshape(batch, pages_per_req)
+    q = normal_bf16(rng, (batch, heads, D_QK))
+    rng_k = np.random.default_rng([seed, 7919, variant])
+    topk = np.stack([_uniform_without_replacement(rng_k, ctx, top_k) for _ in range(batch)])
+    return DecodeCase(f"deepseek_b{batch}_ctx{ctx}", q, topk, np.arange(batch, dtype=np.int32),
+                      np.full(batch, ctx - 1, np.int32), tables, page_size, window, sinks,
+                      top_k + window + sinks, pool_pages * page_size, pool_seed=seed + 1,
+                      extra={"variant": variant})
+
+
+def clustered_topk(rng, ctx, top_k, run=16):
+    """top_k ids as top_k/run non-overlapping runs of `run` consecutive tokens."""
+    nruns = top_k // run
+    while True:
+        starts = np.sort(rng.integers(0, ctx - run + 1, size=nruns))
+        if np.all(np.diff(starts) >= run):
+            break
+    ids = (starts[:, None] + np.arange(run)[None, :]).reshape(-1)
+    return rng.permutation(ids).astype(np.int32)
+
+
+def locality_case(seed, clustered, batch=64, ctx=131072, heads=128, top_k=2048, page_size=64):
+    """Long-context sweep: top-k only (no window or sinks), scattered or clustered."""
+    rng = np.random.default_rng(seed)
+    pages_per_req = ctx // page_size
+    pool_pages = batch * pages_per_req
+    tables = rng.permutation(pool_pages).astype(np.int32).reshape(batch, pages_per_req)
+    q = normal_bf16(rng, (batch, heads, D_QK))
+    if clustered:
+        topk = np.stack([clustered_topk(rng, ctx, top_k) for _ in range(batch)])
+    else:
+        topk = np.stack([_uniform_without_replacement(rng, ctx, top_k) for _ in range(batch)])
+    return DecodeCase(f"locality_{'clustered' if clustered else 'scattered'}", q, topk,
+                      np.arange(batch, dtype=np.int32), np.full(batch, ctx - 1, np.int32),
+                      tables, page_size, 0, 0, top_k, pool_pages * page_size, pool_seed=seed + 1)
+
+
+def random_small_case(seed, T=3, R=2, ctx=300, heads=8, top_k=40, window=5, sinks=2,
+                      page_size=16, unmapped_frac=0.1, invalid_frac=0.1):
+    """Small ragged case with unmapped pages, invalid ids, duplicates and padding."""
+    rng = np.random.default_rng(seed)
+    max_blocks = -(-ctx // page_size)
+    pool_pages = R * max_blocks + 3
+    tables = rng.permutation(pool_pages)[: R * max_blocks].astype(np.int32).reshape(R, max_blocks)
+    tables[rng.random(tables.shape) < unmapped_frac] = -1
+    req_id = rng.integers(0, R, size=T).astype(np.int32)
+    q_pos = rng.integers(0, ctx, size=T).astype(np.int32)
+    topk = rng.integers(-1, ctx + 20, size=(T, top_k)).astype(np.int32)
+    dup = rng.random((T, top_k)) < 0.2
+    topk[dup] = topk[:, :1].repeat(top_k, axis=1)[dup]
+    topk[rng.random((T, top_k)) < invalid_frac] = -1
+    q = normal_bf16(rng, (T, heads, D_QK))
+    return DecodeCase(f"small_{seed}", q, topk, req_id, q_pos, tables, page_size, window, sinks,
+                      top_k + window + sinks, pool_pages * page_size, pool_seed=seed + 1)
+
+
+def evolve_topk(rng, prev, ctx_next, keep_frac=0.85):
+    """Next step's top-k: keep floor(keep_frac*k) of the previous ids (uniform
+    choice) plus fresh uniform draws without replacement from [0, ctx_next)
+    outside the kept set."""
+    k = len(prev)
+    nkeep = int(math.floor(keep_frac * k))
+    kept = rng.choice(prev, size=nkeep, replace=False)
+    mask = np.ones(ctx_next, dtype=bool)
+    mask[kept] = False
+    pool = np.flatnonzero(mask)
+    fresh = rng.choice(pool, size=k - nkeep, replace=False)
+    return rng.permutation(np.concatenate([kept, fresh])).astype(np.int32)
+
+
+@dataclass
+class HotSteps:
+    """Multi-step hot-buffer decode: per step, top-k sets for every request."""
+    batch: int
+    ctx0: int
+    steps: int
+    top_k: int
+    window: int
+    num_sinks: int
+    page_size: int
+    block_table: np.ndarray        # [batch, pages_per_req]
+    topk: list                     # steps x [batch, top_k] int32
+    q_bits: list                   # steps x [batch, heads, 576]
+    host_rows: int
+    pool_seed: int
+    heads: int
+
+    @property
+    def hot_size(self):
+        return 2 * self.top_k
+
+    @property
+    def region_stride(self):
+        return -(-(self.hot_size + 1) // 128) * 128
+
+    @property
+    def cap(self):
+        return self.top_k + self.window + self.num_sinks
+
+    def q_pos(self, step):
+        return np.full(self.batch, self.ctx0 + step - 1, dtype=np.int32)
+
+
+def hot_steps_case(seed=3000, batch=64, ctx0=65536, steps=16, top_k=2048, window=128,
+                   sinks=4, page_size=64, heads=128):
+    """Consecutive decode steps whose top-k keeps 85% of the previous set.
+
+    Step t decodes position ctx0 + t - 1 (context length ctx0 + t); each
+    request owns a disjoint random set of pages of one shared host pool.
+    """
+    rng = np.random.default_rng(seed)
+    ctx_max = ctx0 + steps
+    pages_per_req = -(-ctx_max // page_size)
+    pool_pages = batch * pages_per_req
+    tables = rng.permutation(pool_pages).astype(np.int32).reshape(batch, pages_per_req)
+    topk_steps, q_steps = [], []
+    cur = [_uniform_without_replacement(rng, ctx0, top_k) for _ in range(batch)]
+    for t in range(steps):
+        if t > 0:
+            cur = [evolve_topk(rng, c, ctx0 + t) for c in cur]
+        topk_steps.append(np.stack(cur))
+        q_steps.append(normal_bf16(rng, (batch, heads, D_QK)))
+    return HotSteps(batch, ctx0, steps, top_k, window, sinks, page_size, tables, topk_steps,
+                    q_steps, pool_pages * page_size, seed + 1, heads)
