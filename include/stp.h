@@ -1,0 +1,248 @@
+/*
+ * stp.h -- C ABI of the top-k sparse MLA decode path on MI355X (gfx950).
+ *
+ * The path has four stages, each one call (or a pair) below:
+ *   1. stp_normalize_indices   candidate sets S = unique(D ∪ W ∪ A), token ->
+ *                              logical block -> physical slot id, block view;
+ *   2. stp_hot_lookup_swapin   per-request hot buffer with LRU eviction and
+ *      stp_hot_reset           row-by-row swap-in from a pinned host pool,
+ *      stp_backup_rows         and the back-up of each step's new rows;
+ *   3. stp_sparse_mla_decode   attention over the selected latent rows with an
+ *                              online softmax (optionally split);
+ *   4. stp_splitkv_merge       merge of split partial states.
+ *
+ * Sources: "HiSparse" hot-buffer walkthrough (devpress.csdn.net); "5.1.1 · 从
+ * 索引到 Kernel" (PaperTrace); "PagedAttention 与 RadixAttention：上游机制与海光
+ * 实现对照"; "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)".
+ *
+ * Conventions shared by every call
+ *  - Ownership: the caller owns every buffer (device memory, pinned host
+ *    memory, workspace) and every stream.  No call allocates, frees or
+ *    synchronises; each only enqueues kernels on `stream` and returns.
+ *  - Pointers are device pointers unless stated otherwise.  A "host pool"
+ *    pointer is the device-visible address of pinned host memory
+ *    (hipHostMalloc + hipHostGetDevicePointer, or torch pin_memory()).
+ *  - bf16 data is passed as uint16_t bit patterns.  Row-major layouts.
+ *  - Padding / invalid ids are -1 everywhere.
+ *  - Data anomalies found on the device (ids out of range, causally invalid
+ *    candidates, unmapped pages) are not errors: they are dropped, and
+ *    counted where an output exists for it.  Argument errors are detected on
+ *    the host before anything is launched and return a non-zero status; the
+ *    message of the last error of the calling thread is stp_last_error().
+ *  - Calls on one stream run in order; calls that share state (hot-buffer
+ *    dgi/lru, outputs) on different streams must be ordered by the caller.
+ */
+#ifndef STP_H_
+#define STP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  STP_OK = 0,
+  STP_ERR_INVALID_ARG = 1, /* bad pointer / size / unsupported shape */
+  STP_ERR_WORKSPACE = 2,   /* workspace missing or too small: nothing launched */
+  STP_ERR_HIP = 3          /* a HIP launch or attribute call failed */
+};
+
+/* Human-readable message of the last non-zero status returned on this thread. */
+const char* stp_last_error(void);
+
+/* Library version string. */
+const char* stp_version(void);
+
+/*
+ * Device-visible address of pinned host memory (hipHostGetDevicePointer):
+ * what the host-pool arguments below expect.  STP_ERR_HIP if `host` is not
+ * pinned host memory.
+ */
+int stp_host_device_pointer(const void* host, void** dev);
+
+/*
+ * ---- Stage 1: candidate normalisation -------------------------------------
+ * "5.1.1 · 从索引到 Kernel" §1.1 eq. (1), §1.2 eq. (2), §7.3 eq. (16)-(17),
+ * §7.4 eq. (19); "HiSparse" walkthrough, token -> global slot id conversion.
+ *
+ * For every query token i (request r = req_id[i], position q = q_pos[i]):
+ *   D = entries >= 0 of topk[i, 0:top_k]      (entries < 0 are padding)
+ *   W = [max(0, q - window + 1), q]           (empty when window == 0)
+ *   A = [0, min(num_sinks, q + 1))
+ *   S = ascending unique t of D ∪ W ∪ A with t <= q, t / page_size < max_blocks
+ *       and block_table[r, t / page_size] >= 0 (and a slot that fits int32).
+ *   tok_out[i, j]  = j-th element of S, j < |S|; -1 for j >= |S|
+ *   slot_out[i, j] = block_table[r, t / P] * P + t % P for t = tok_out[i, j]
+ *   count_out[i]   = |S|
+ *   dropped_out[i] = number of D entries (with multiplicity) >= 0 that fail
+ *                    the filter (beyond q, outside the table, unmapped page).
+ *   A token whose req_id is outside [0, num_reqs) or whose q_pos < 0 is a
+ *   padding row: count 0, dropped 0, all -1.
+ * Block view (optional; pass blk_indptr == NULL to skip; then the three other
+ * block arrays are ignored):
+ *   blk_indptr[T + 1]: CSR row pointers over tokens (blk_indptr[0] = 0);
+ *   for k in [blk_indptr[i], blk_indptr[i+1]): blk_logical[k] = ascending
+ *   unique t / P over S_i, blk_page[k] = its physical page, blk_mask[k] = the
+ *   in-page membership bits (bit t % P set for each t of S_i in the block).
+ *   The block arrays must hold T * cap entries (the worst case).
+ *
+ * Layouts: topk [T, top_k] int32; req_id, q_pos [T] int32; block_table
+ * [num_reqs, max_blocks] int32 (-1 = unmapped); tok_out, slot_out [T, cap].
+ * Requirements: T >= 0, top_k >= 0, 1 <= page_size <= 64, window >= 0,
+ * num_sinks >= 0, cap >= top_k + window + num_sinks (so |S| <= cap always),
+ * max_blocks * page_size <= 1,048,576 positions (the per-token bitmap lives in
+ * LDS).  dropped_out may be NULL.
+ */
+int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                          const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                          int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t window,
+                          int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+                          int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr,
+                          int32_t* blk_logical, int32_t* blk_page, uint64_t* blk_mask,
+                          hipStream_t stream);
+
+/*
+ * ---- Stage 2: hot buffer ----------------------------------------------------
+ * "HiSparse" walkthrough: overview (SwapIn / BackUp), hot cache
+ * initialisation (per-request region of hot_size + 1 rows, 16-byte rows),
+ * sections "Phase 1" .. "Phase 5" of the swap-in kernel.
+ *
+ * Per request row r in [0, num_rows) with base = r * region_stride and
+ * G = global_ids[r, 0:cap] (unique slot ids, -1 padded -- as produced by
+ * stp_normalize_indices' slot_out):
+ *   Phase 1: G[i] < 0 -> hot_rows_out = -1; G[i] == newest_global[r] ->
+ *            hot_rows_out = base + hot_size (the reserved newest-token row);
+ *            otherwise pending.
+ *   Phase 2: walk lru[r, 0..hot_size) (least recent first); a slot s whose
+ *            dgi[r, s] is pending is a hit: hot_rows_out = base + s.
+ *   Phase 3: pending entries left are misses; in ascending i the m-th miss
+ *            takes the m-th evictable slot of the walk; dgi[r, slot] = G[i];
+ *            hot_rows_out = base + slot; miss_mask = 1.
+ *   Phase 4: lru[r] = [evictables not taken] + [slots loaded] + [hits].
+ *   Phase 5: each miss copies host_pool row G[i] (row_bytes bytes) into
+ *            hot_cache row base + slot, reading the pinned host memory from
+ *            the GPU; if G[i] >= host_rows the hot row is zeroed and
+ *            dgi[r, slot] = -1 (ownership revoked), hot_rows_out unchanged.
+ *   stats[0] += hits, stats[1] += misses (newest and -1 entries are neither).
+ *   Rows r >= num_real_rows are padding: hot_rows_out = -1, miss_mask = 0,
+ *   state untouched.
+ * Layouts: global_ids, hot_rows_out [num_rows, cap] int32; miss_mask
+ * [num_rows, cap] uint8 (nullable); newest_global [num_rows] int32; dgi
+ * [num_rows, hot_size] int32; lru [num_rows, hot_size] int16; hot_cache
+ * [num_rows * region_stride, row_bytes] bytes (device); host_pool
+ * [host_rows, row_bytes] bytes (device-visible pinned host memory); stats
+ * [2] int64 (nullable, accumulated, caller zeroes it).
+ * Requirements: row_bytes > 0 and row_bytes % 16 == 0 (else INVALID_ARG, as
+ * the coordinator's 16-byte row check); 1 <= hot_size <= 32767 (int16 LRU);
+ * region_stride >= hot_size + 1; 0 <= cap <= hot_size (so misses never
+ * exceed the evictable slots); 0 <= num_real_rows <= num_rows;
+ * num_rows * region_stride <= INT32_MAX; stp_hot_lds_bytes(cap, hot_size) > 0
+ * (the per-row LDS working set fits).  The ids of a row must be
+ * unique (stage 1 guarantees it); duplicates give unspecified slot choices.
+ * State starts as stp_hot_reset leaves it.
+ */
+int stp_hot_lookup_swapin(const void* host_pool, int64_t host_rows, void* hot_cache,
+                          int64_t row_bytes, const int32_t* global_ids, int32_t cap,
+                          const int32_t* newest_global, int32_t* dgi, int16_t* lru, int32_t hot_size,
+                          int32_t region_stride, int32_t num_real_rows, int32_t num_rows,
+                          int32_t* hot_rows_out, uint8_t* miss_mask, int64_t* stats,
+                          hipStream_t stream);
+
+/* LDS bytes stp_hot_lookup_swapin needs for (cap, hot_size); 0 if unsupported. */
+size_t stp_hot_lds_bytes(int32_t cap, int32_t hot_size);
+
+/*
+ * Drop the cached state of request rows before they are reused ("HiSparse"
+ * walkthrough, HiSparseCoordinator: a recycled slot's stale state must be
+ * dropped first): dgi[r, :] = -1, lru[r, :] = 0 .. hot_size-1 for every r in
+ * rows[0:n] (rows == NULL: r = 0 .. n-1, and n <= num_rows).  dgi / lru are
+ * [num_rows, hot_size]; row indices outside [0, num_rows) are skipped.
+ */
+int stp_hot_reset(int32_t* dgi, int16_t* lru, int32_t hot_size, int32_t num_rows,
+                  const int32_t* rows, int32_t n, hipStream_t stream);
+
+/*
+ * BackUp ("HiSparse" walkthrough, overview): copy n rows of row_bytes bytes,
+ * host_pool[dst_ids[j]] <- hot_cache[src_rows[j]], writing pinned host memory
+ * from the GPU.  Entries with src_rows[j] outside [0, hot_rows) or dst_ids[j]
+ * outside [0, host_rows) are skipped.  Two entries with the same destination
+ * race.  Requirements: row_bytes > 0, row_bytes % 16 == 0, n >= 0.
+ */
+int stp_backup_rows(const void* hot_cache, int64_t hot_rows, void* host_pool, int64_t host_rows,
+                    int64_t row_bytes, const int32_t* src_rows, const int32_t* dst_ids, int32_t n,
+                    hipStream_t stream);
+
+/*
+ * ---- Stage 3: sparse MLA decode attention -----------------------------------
+ * "5.1.1 · 从索引到 Kernel" §3.1 eq. (4)-(6), §3.2 (mask before exp, empty
+ * sets), §7.3 (sets); "PagedAttention 与 RadixAttention" §1.1 (decode
+ * attention), §1.4 (exp2 with log2 e folded into the scale; partitions).
+ *
+ * For token t and head h, over the rows R_t = { row_ids[t, j] : j < n_t,
+ * 0 <= row_ids[t, j] < kv_rows } with n_t = counts[t] (counts == NULL: n_t =
+ * cap):
+ *   z_j  = scale * <q[t, h, 0:576], kv[row_j, 0:576]>
+ *   out[t, h, :] = sum_j softmax(z)_j * kv[row_j, 0:512]     (bf16, RNE)
+ *   lse[t, h]    = log(sum_j exp(z_j))                        (natural log)
+ * Empty R_t: out = 0, lse = -inf.  Entries are a set: a repeated row id is
+ * counted twice (callers pass stage 1's unique lists).
+ * Layouts: q [T, H, 576] bf16; kv [kv_rows, 576] bf16 (the paged latent pool
+ * addressed by slot id, or the hot cache addressed by hot row); row_ids
+ * [T, cap] int32; counts [T] int32 (nullable); out [T, H, 512] bf16; lse
+ * [T, H] float (nullable).
+ * num_splits: 0 = choose automatically, otherwise the number of contiguous
+ * position ranges of ceil(n_t / num_splits) each (a performance hint: the
+ * result does not depend on it beyond float rounding).  Splits > 1 need a
+ * workspace of stp_sparse_mla_decode_workspace() bytes (STP_ERR_WORKSPACE if
+ * smaller); the workspace may be reused once the call's work has completed
+ * on `stream`.
+ * Requirements: T >= 0, H >= 1, cap >= 0, ceil(cap / splits) <= 4096,
+ * 0 < kv_rows, scale finite.
+ */
+int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+                          const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T,
+                          int32_t H, float scale, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream);
+
+/* Splits stp_sparse_mla_decode uses for num_splits (0 = auto) at this shape. */
+int32_t stp_sparse_mla_decode_splits(int32_t T, int32_t H, int32_t cap, int32_t num_splits);
+
+/* Workspace bytes stp_sparse_mla_decode needs for this shape and num_splits. */
+size_t stp_sparse_mla_decode_workspace(int32_t T, int32_t H, int32_t cap, int32_t num_splits);
+
+/*
+ * Split partial states only ("5.1.1 · 从索引到 Kernel" §3.2 eq. (7) inputs):
+ * for split s covering positions [s*c, min(n_t, (s+1)*c)), c = ceil(n_t / S):
+ *   m_part[t, s, h] = max_j z_j (natural-log units), l_part = sum_j exp(z_j - m),
+ *   o_part[t, s, h, :] = sum_j exp(z_j - m) * kv[row_j, 0:512]  (unnormalised);
+ *   an empty split has m = -inf, l = 0, o = 0.
+ * Layouts: o_part [T, S, H, 512] float, m_part / l_part [T, S, H] float.
+ * Requirements as stp_sparse_mla_decode with num_splits = S >= 1.
+ */
+int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+                                  const int32_t* row_ids, const int32_t* counts, int32_t cap,
+                                  int32_t T, int32_t H, float scale, int32_t num_splits,
+                                  float* o_part, float* m_part, float* l_part, hipStream_t stream);
+
+/*
+ * ---- Stage 4: split-KV merge -------------------------------------------------
+ * "5.1.1 · 从索引到 Kernel" §3.2 eq. (7) for any number of splits, §7.1 (an
+ * empty split, l_s = 0, takes no part); "PagedAttention 与 RadixAttention"
+ * §1.4 part 3 (combine).  With m = max over live splits of m_part:
+ *   out[t, h, :] = sum_s e^(m_s - m) o_s / sum_s e^(m_s - m) l_s   (bf16, RNE)
+ *   lse[t, h]    = m + log(sum_s e^(m_s - m) l_s);  no live split: 0 and -inf.
+ * Layouts as stp_sparse_mla_decode_partial (dv values per head instead of
+ * 512); lse nullable.  Requirements: T >= 0, S >= 1, H >= 1, 1 <= dv, dv % 4 == 0.
+ */
+int stp_splitkv_merge(const float* o_part, const float* m_part, const float* l_part, int32_t T,
+                      int32_t S, int32_t H, int32_t dv, uint16_t* out, float* lse,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STP_H_ */

@@ -1,0 +1,239 @@
+"""Top-k sparse MLA decode over a paged KV cache, native on MI355X (gfx950).
+
+Thin Python binding over libstp.so (include/stp.h): each function checks
+tensor shapes, dtypes and devices, passes raw pointers and the current HIP
+stream, and returns.  Every step of the path runs in the HIP kernels; torch
+only provides device memory, pinned host memory and streams.
+"""
+
+import torch
+
+from ._lib import STP_ERR_HIP, STP_ERR_INVALID_ARG, STP_ERR_WORKSPACE, STP_OK, StpError, check, lib
+
+D_QK = 576
+D_V = 512
+
+__all__ = [
+    "StpError", "version", "normalize_indices", "hot_lookup_swapin", "hot_reset", "backup_rows",
+    "sparse_mla_decode", "sparse_mla_decode_partial", "splitkv_merge", "decode_splits",
+    "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer",
+]
+
+
+def version():
+    return lib.stp_version().decode()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype, device):
+    return None if t is None else _dev(t, name, dtype, device)
+
+
+def host_device_pointer(t):
+    """Device-visible address of a pinned host tensor."""
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("expected a pinned host tensor (pin_memory=True)")
+    import ctypes
+    out = ctypes.c_void_p()
+    check(lib.stp_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)))
+    return out.value
+
+
+def normalize_indices(topk, req_id, q_pos, block_table, page_size, window, num_sinks, cap=None,
+                      block_view=True, out=None):
+    """Stage 1.  Returns a dict: tok, slot [T, cap], count, dropped [T] and,
+    with block_view, blk_indptr [T+1], blk_logical, blk_page, blk_mask [T*cap]."""
+    dev = topk.device
+    T, top_k = topk.shape
+    num_reqs, max_blocks = block_table.shape
+    if cap is None:
+        cap = top_k + window + num_sinks
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {
+            "tok": torch.empty((T, cap), **i32),
+            "slot": torch.empty((T, cap), **i32),
+            "count": torch.empty((T,), **i32),
+            "dropped": torch.empty((T,), **i32),
+        }
+        if block_view:
+            out["blk_indptr"] = torch.empty((T + 1,), **i32)
+            out["blk_logical"] = torch.empty((max(1, T * cap),), **i32)
+            out["blk_page"] = torch.empty((max(1, T * cap),), **i32)
+            out["blk_mask"] = torch.empty((max(1, T * cap),), dtype=torch.int64, device=dev)
+    bv = "blk_indptr" in out
+    check(lib.stp_normalize_indices(
+        _dev(topk, "topk", torch.int32, dev), top_k,
+        _dev(req_id, "req_id", torch.int32, dev), _dev(q_pos, "q_pos", torch.int32, dev), T,
+        _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size,
+        window, num_sinks, cap,
+        _dev(out["tok"], "tok", torch.int32, dev), _dev(out["slot"], "slot", torch.int32, dev),
+        _dev(out["count"], "count", torch.int32, dev),
+        _opt(out.get("dropped"), "dropped", torch.int32, dev),
+        _dev(out["blk_indptr"], "blk_indptr", torch.int32, dev) if bv else None,
+        _dev(out["blk_logical"], "blk_logical", torch.int32, dev) if bv else None,
+        _dev(out["blk_page"], "blk_page", torch.int32, dev) if bv else None,
+        _dev(out["blk_mask"], "blk_mask", torch.int64, dev) if bv else None,
+        _stream(dev)))
+    return out
+
+
+def hot_lds_bytes(cap, hot_size):
+    return lib.stp_hot_lds_bytes(cap, hot_size)
+
+
+def hot_lookup_swapin(host_pool, hot_cache, global_ids, newest_global, dgi, lru, region_stride,
+                      num_real_rows=None, hot_rows_out=None, miss_mask=None, stats=None,
+                      host_pool_ptr=None):
+    """Stage 2 lookup, LRU update and swap-in.  host_pool: pinned uint8
+    [host_rows, row_bytes]; hot_cache: device uint8 [rows*stride, row_bytes];
+    dgi int32 / lru int16 [rows, hot_size] (updated in place).
+    Returns (hot_rows_out, miss_mask, stats)."""
+    dev = hot_cache.device
+    num_rows, cap = global_ids.shape
+    hot_size = dgi.shape[1]
+    host_rows, row_bytes = host_pool.shape
+    if host_pool.dtype != torch.uint8 or hot_cache.dtype != torch.uint8:
+        raise TypeError("host_pool and hot_cache must be uint8 byte views")
+    if hot_cache.shape[1] != row_bytes or hot_cache.shape[0] < num_rows * region_stride:
+        raise ValueError("hot_cache must be [num_rows * region_stride, row_bytes]")
+    if tuple(lru.shape) != tuple(dgi.shape) or dgi.shape[0] != num_rows:
+        raise ValueError("dgi and lru must be [num_rows, hot_size]")
+    if num_real_rows is None:
+        num_real_rows = num_rows
+    if hot_rows_out is None:
+        hot_rows_out = torch.empty((num_rows, cap), dtype=torch.int32, device=dev)
+    if miss_mask is None:
+        miss_mask = torch.empty((num_rows, cap), dtype=torch.uint8, device=dev)
+    if stats is None:
+        stats = torch.zeros(2, dtype=torch.int64, device=dev)
+    if host_pool_ptr is None:
+        host_pool_ptr = host_device_pointer(host_pool)
+    if not host_pool.is_contiguous():
+        raise ValueError("host_pool must be contiguous")
+    check(lib.stp_hot_lookup_swapin(
+        host_pool_ptr, host_rows, _dev(hot_cache, "hot_cache", torch.uint8, dev), row_bytes,
+        _dev(global_ids, "global_ids", torch.int32, dev), cap,
+        _dev(newest_global, "newest_global", torch.int32, dev),
+        _dev(dgi, "dgi", torch.int32, dev), _dev(lru, "lru", torch.int16, dev), hot_size,
+        region_stride, num_real_rows, num_rows,
+        _dev(hot_rows_out, "hot_rows_out", torch.int32, dev),
+        _opt(miss_mask, "miss_mask", torch.uint8, dev), _opt(stats, "stats", torch.int64, dev),
+        _stream(dev)))
+    return hot_rows_out, miss_mask, stats
+
+
+def hot_reset(dgi, lru, rows=None):
+    """Drop the cached state of the given request rows (all when None)."""
+    dev = dgi.device
+    hot_size = dgi.shape[1]
+    n = dgi.shape[0] if rows is None else rows.numel()
+    if tuple(lru.shape) != tuple(dgi.shape):
+        raise ValueError("dgi and lru must have the same shape")
+    check(lib.stp_hot_reset(_dev(dgi, "dgi", torch.int32, dev), _dev(lru, "lru", torch.int16, dev),
+                            hot_size, dgi.shape[0], _opt(rows, "rows", torch.int32, dev), n,
+                            _stream(dev)))
+
+
+def backup_rows(hot_cache, host_pool, src_rows, dst_ids, host_pool_ptr=None):
+    """BackUp: host_pool[dst_ids[j]] <- hot_cache[src_rows[j]] (byte rows)."""
+    dev = hot_cache.device
+    if host_pool_ptr is None:
+        host_pool_ptr = host_device_pointer(host_pool)
+    check(lib.stp_backup_rows(
+        _dev(hot_cache, "hot_cache", torch.uint8, dev), hot_cache.shape[0], host_pool_ptr,
+        host_pool.shape[0], hot_cache.shape[1], _dev(src_rows, "src_rows", torch.int32, dev),
+        _dev(dst_ids, "dst_ids", torch.int32, dev), src_rows.numel(), _stream(dev)))
+
+
+def decode_splits(T, H, cap, num_splits=0):
+    return lib.stp_sparse_mla_decode_splits(T, H, cap, num_splits)
+
+
+def decode_workspace_bytes(T, H, cap, num_splits=0):
+    return lib.stp_sparse_mla_decode_workspace(T, H, cap, num_splits)
+
+
+def _decode_common(q, kv, row_ids, counts):
+    dev = q.device
+    T, H, d = q.shape
+    if d != D_QK or kv.dim() != 2 or kv.shape[1] != D_QK:
+        raise ValueError("q must be [T, H, 576] and kv [rows, 576]")
+    if row_ids.dim() != 2 or row_ids.shape[0] != T:
+        raise ValueError("row_ids must be [T, cap]")
+    return dev, T, H, row_ids.shape[1]
+
+
+def sparse_mla_decode(q, kv, row_ids, counts=None, scale=D_QK ** -0.5, num_splits=0,
+                      workspace=None, out=None, lse=None):
+    """Stage 3 (+ stage 4 when split).  q [T, H, 576] bf16, kv [rows, 576] bf16,
+    row_ids [T, cap] int32, counts [T] int32.  Returns (out [T, H, 512] bf16,
+    lse [T, H] float32)."""
+    dev, T, H, cap = _decode_common(q, kv, row_ids, counts)
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(T, H, cap, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", torch.uint8, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(lib.stp_sparse_mla_decode(
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0],
+        _dev(row_ids, "row_ids", torch.int32, dev), _opt(counts, "counts", torch.int32, dev), cap,
+        T, H, float(scale), num_splits, ws_ptr, ws_bytes,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse
+
+
+def sparse_mla_decode_partial(q, kv, row_ids, counts=None, scale=D_QK ** -0.5, num_splits=1,
+                              o_part=None, m_part=None, l_part=None):
+    """Split partial states: o [T, S, H, 512] (unnormalised), m, l [T, S, H] float32."""
+    dev, T, H, cap = _decode_common(q, kv, row_ids, counts)
+    S = num_splits
+    if o_part is None:
+        o_part = torch.empty((T, S, H, D_V), dtype=torch.float32, device=dev)
+    if m_part is None:
+        m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    check(lib.stp_sparse_mla_decode_partial(
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0],
+        _dev(row_ids, "row_ids", torch.int32, dev), _opt(counts, "counts", torch.int32, dev), cap,
+        T, H, float(scale), S, _dev(o_part, "o_part", torch.float32, dev),
+        _dev(m_part, "m_part", torch.float32, dev), _dev(l_part, "l_part", torch.float32, dev),
+        _stream(dev)))
+    return o_part, m_part, l_part
+
+
+def splitkv_merge(o_part, m_part, l_part, out=None, lse=None):
+    """Stage 4: merge split states o [T, S, H, dv], m/l [T, S, H]."""
+    dev = o_part.device
+    T, S, H, dv = o_part.shape
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    check(lib.stp_splitkv_merge(
+        _dev(o_part, "o_part", torch.float32, dev), _dev(m_part, "m_part", torch.float32, dev),
+        _dev(l_part, "l_part", torch.float32, dev), T, S, H, dv,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse

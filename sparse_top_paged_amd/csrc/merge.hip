@@ -1,0 +1,92 @@
+// Stage 4: split-KV merge on gfx950.
+//
+// "5.1.1 · 从索引到 Kernel" §3.2 eq. (7) (rescale every split to the common
+// maximum; the partial numerators must be unnormalised), §7.1 eq. (14) (an
+// empty split, l_s = 0, takes no part); "PagedAttention 与 RadixAttention：
+// 上游机制与海光实现对照" §1.4 part 3 (the combine kernel, one small block per
+// head and sequence).
+//
+// Design: memory-bound.  One 256-thread workgroup covers two heads of one
+// token; 128 threads per head each own 4 consecutive output values and read
+// the splits' float4 slices (coalesced 2 KiB per split and head).
+
+#include "stp_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerHead = 128;
+
+__global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ m_part,
+    const float* __restrict__ l_part, int S, int H, int dv, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * 2 + (threadIdx.x / kPerHead);
+  if (h >= H) return;
+  const int c0 = (threadIdx.x % kPerHead) * 4;
+  // common maximum over live splits
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    const int64_t k = ((int64_t)t * S + s) * H + h;
+    if (l_part[k] > 0.f) M = fmaxf(M, m_part[k]);
+  }
+  uint16_t* orow = out + ((int64_t)t * H + h) * dv;
+  if (M == -INFINITY) {  // no live split
+    for (int c = c0; c < dv; c += 4 * kPerHead)
+      *(uint2*)(orow + c) = make_uint2(0u, 0u);
+    if (lse && c0 == 0) lse[(int64_t)t * H + h] = -INFINITY;
+    return;
+  }
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const int64_t k = ((int64_t)t * S + s) * H + h;
+    const float l = l_part[k];
+    if (l > 0.f) L += expf(m_part[k] - M) * l;
+  }
+  const float inv = 1.f / L;
+  for (int c = c0; c < dv; c += 4 * kPerHead) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < S; ++s) {
+      const int64_t k = ((int64_t)t * S + s) * H + h;
+      const float l = l_part[k];
+      if (!(l > 0.f)) continue;
+      const float w = expf(m_part[k] - M);
+      const float4 o = *(const float4*)(o_part + k * dv + c);
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+    }
+    const uint32_t lo = stp::f32_to_bf16_rne(acc.x * inv) | ((uint32_t)stp::f32_to_bf16_rne(acc.y * inv) << 16);
+    const uint32_t hi = stp::f32_to_bf16_rne(acc.z * inv) | ((uint32_t)stp::f32_to_bf16_rne(acc.w * inv) << 16);
+    *(uint2*)(orow + c) = make_uint2(lo, hi);
+  }
+  if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
+}
+
+}  // namespace
+
+namespace stp {
+
+int launch_merge(const float* o_part, const float* m_part, const float* l_part, int T, int S,
+                 int H, int dv, uint16_t* out, float* lse, hipStream_t stream) {
+  dim3 grid(T, (H + 1) / 2);
+  splitkv_merge_kernel<<<grid, kThreads, 0, stream>>>(o_part, m_part, l_part, S, H, dv, out, lse);
+  return check_launch("splitkv_merge_kernel");
+}
+
+}  // namespace stp
+
+extern "C" int stp_splitkv_merge(const float* o_part, const float* m_part, const float* l_part,
+                                 int32_t T, int32_t S, int32_t H, int32_t dv, uint16_t* out,
+                                 float* lse, hipStream_t stream) {
+  using stp::fail;
+  if (T < 0 || S < 1 || H < 1 || dv < 1 || dv % 4 != 0)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge: bad sizes T=%d S=%d H=%d dv=%d", T, S, H, dv);
+  if (H > 2 * 65535) return fail(STP_ERR_INVALID_ARG, "splitkv_merge: H %d too large", H);
+  if (T == 0) return STP_OK;
+  if (!o_part || !m_part || !l_part || !out)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge: null pointer");
+  return stp::launch_merge(o_part, m_part, l_part, T, S, H, dv, out, lse, stream);
+}

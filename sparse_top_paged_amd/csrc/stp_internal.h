@@ -1,0 +1,59 @@
+// Internal helpers shared by the HIP sources of libstp (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "stp.h"
+
+namespace stp {
+
+// Records the message returned by stp_last_error() and passes the status through.
+int fail(int status, const char* fmt, ...);
+
+// Checks the launch that was just enqueued.
+int check_launch(const char* what);
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Block-wide exclusive scan of one int per thread (blockDim.x == 256).
+// `scratch` holds at least 8 ints of LDS.  Returns the exclusive prefix and
+// writes the block total to *total.
+__device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // inclusive scan inside the wave
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int wave_off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int s = scratch[w];
+    if (w < wave) wave_off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return wave_off + x - v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Split-KV merge launcher shared by the decode entry point (merge.hip).
+int launch_merge(const float* o_part, const float* m_part, const float* l_part, int T, int S,
+                 int H, int dv, uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace stp

@@ -1,0 +1,80 @@
+"""The C-ABI library loads and exports every symbol include/stp.h declares (CPU only).
+
+No compute call is made: only host-side argument validation, which returns
+before anything touches a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stp.h")
+LIB = os.path.join(ROOT, "sparse_top_paged_amd", "libstp.so")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(stp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared()
+    for n in ["stp_normalize_indices", "stp_hot_lookup_swapin", "stp_backup_rows",
+              "stp_sparse_mla_decode", "stp_splitkv_merge", "stp_hot_reset",
+              "stp_sparse_mla_decode_partial", "stp_sparse_mla_decode_workspace"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "libstp.so not built"
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_binding_declares_every_symbol():
+    from sparse_top_paged_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == declared()
+
+
+def test_host_side_validation():
+    import sparse_top_paged_amd as stp
+    from sparse_top_paged_amd._lib import STP_ERR_INVALID_ARG, STP_ERR_WORKSPACE, lib
+
+    # page size outside [1, 64]
+    assert lib.stp_normalize_indices(None, 0, None, None, 1, None, 0, 0, 65, 0, 0, 0, None, None,
+                                     None, None, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    assert b"page_size" in lib.stp_last_error()
+    # cap smaller than top_k + window + sinks
+    assert lib.stp_normalize_indices(None, 8, None, None, 1, None, 0, 0, 16, 4, 4, 10, None, None,
+                                     None, None, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    # 16-byte row rule of the hot buffer (656 passes, 1000 fails)
+    assert lib.stp_hot_lookup_swapin(None, 0, None, 1000, None, 0, None, None, None, 16, 17, 0, 0,
+                                     None, None, None, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_hot_lookup_swapin(None, 0, None, 656, None, 0, None, None, None, 16, 17, 0, 0,
+                                     None, None, None, None) == 0  # zero rows: nothing to launch
+    # cap > hot_size could need more evictable slots than exist
+    assert lib.stp_hot_lookup_swapin(None, 0, None, 1152, None, 20, None, None, None, 16, 17, 0, 1,
+                                     None, None, None, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_backup_rows(None, 0, None, 0, 24, None, None, 1, None) == STP_ERR_INVALID_ARG
+    # split decode without workspace is rejected before any launch
+    fake = ctypes.c_void_p(16)
+    assert lib.stp_sparse_mla_decode(fake, fake, 100, fake, None, 2180, 32, 128, 0.04, 4, None, 0,
+                                     fake, None, None) == STP_ERR_WORKSPACE
+    assert lib.stp_sparse_mla_decode(fake, fake, 100, fake, None, 64, 1, 16, float("nan"), 1,
+                                     None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_splitkv_merge(None, None, None, 1, 1, 1, 6, None, None, None) == STP_ERR_INVALID_ARG
+    assert stp.decode_splits(32, 128, 2180) >= 1
+    assert stp.decode_workspace_bytes(1, 16, 44) == 0          # tiny shape runs unsplit
+    assert stp.hot_lds_bytes(2180, 4096) > 0
+    assert stp.hot_lds_bytes(40000, 32767) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from sparse_top_paged_amd import _lib
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "libstp.so"))

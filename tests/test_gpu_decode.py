@@ -1,0 +1,210 @@
+"""GPU parity: sparse MLA decode (stage 3), its partial states and the merge (stage 4).
+
+The oracle computes in fp64 from the same bf16 inputs; the GPU output is bf16.
+Tolerance (helpers.assert_attention_close): |err| <= 2e-2 per element, per
+(token, head) max error <= 1e-2 of the reference's largest magnitude, and
+|lse err| <= 1e-2.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_attention_close, bf16_bits_of, bf16_dev, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(q_bits, kv, ids, counts, scale, splits):
+    import sparse_top_paged_amd as stp
+    out, lse = stp.sparse_mla_decode(bf16_dev(q_bits), kv, to_dev(ids),
+                                     None if counts is None else to_dev(counts), scale, splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _tiny():
+    c = workloads.tiny_case()
+    kv_bits = workloads.pool_bits(c.kv_rows, c.pool_seed)
+    ref = oracle.normalize(c.topk, c.req_id, c.q_pos, c.window, c.num_sinks, c.block_table,
+                           c.page_size, c.cap)
+    return c, kv_bits, ref
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7])
+def test_tiny_case(splits):
+    c, kv_bits, ref = _tiny()
+    out, lse = _decode(c.q_bits, bf16_dev(kv_bits), ref["slot"], ref["count"], c.scale, splits)
+    o_ref, l_ref = oracle.attend_sparse(c.q_bits, kv_bits, ref["slot"], ref["count"], c.scale)
+    assert_attention_close(out, lse, o_ref, l_ref, f"tiny splits={splits}")
+
+
+@pytest.mark.parametrize("H", [8, 16, 64, 80, 128, 192])
+@pytest.mark.parametrize("cap", [1, 31, 33, 100])
+def test_head_counts_and_ragged_tiles(H, cap):
+    rng = np.random.default_rng(H * 1000 + cap)
+    T, rows = 3, 500
+    kv_bits = workloads.normal_bf16(rng, (rows, 576))
+    q_bits = workloads.normal_bf16(rng, (T, H, 576))
+    ids = np.full((T, cap), -1, np.int32)
+    counts = np.zeros(T, np.int32)
+    for t in range(T):
+        n = [cap, max(1, cap // 2), max(0, cap - 7)][t]
+        ids[t, :n] = rng.choice(rows, size=n, replace=False)
+        counts[t] = n
+    for splits in (1, 2):
+        out, lse = _decode(q_bits, bf16_dev(kv_bits), ids, counts, 1 / 24, splits)
+        o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, counts, 1 / 24)
+        assert_attention_close(out, lse, o_ref, l_ref, f"H={H} cap={cap} splits={splits}")
+
+
+def test_invalid_ids_and_no_counts():
+    rng = np.random.default_rng(5)
+    rows = 300
+    kv_bits = workloads.normal_bf16(rng, (rows, 576))
+    q_bits = workloads.normal_bf16(rng, (4, 16, 576))
+    ids = rng.integers(-3, rows + 40, size=(4, 70)).astype(np.int32)  # -ids, out of range
+    ids[2] = -1                                                        # an all-invalid row
+    for splits in (1, 3):
+        out, lse = _decode(q_bits, bf16_dev(kv_bits), ids, None, 0.05, splits)
+        o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, None, 0.05)
+        assert_attention_close(out, lse, o_ref, l_ref, f"invalid ids splits={splits}")
+        assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
+
+
+def test_empty_single_and_equal_logits():
+    rng = np.random.default_rng(6)
+    rows = 64
+    kv_bits = workloads.normal_bf16(rng, (rows, 576))
+    q_bits = workloads.normal_bf16(rng, (3, 32, 576))
+    q_bits[2] = 0                                      # every logit equal -> mean of V rows
+    ids = np.full((3, 40), -1, np.int32)
+    ids[1, 0] = 17                                     # a single candidate
+    ids[2, :40] = np.arange(40)
+    counts = np.asarray([0, 1, 40], np.int32)          # row 0 is empty
+    out, lse = _decode(q_bits, bf16_dev(kv_bits), ids, counts, 1 / 24, 1)
+    o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, counts, 1 / 24)
+    assert_attention_close(out, lse, o_ref, l_ref, "edge rows")
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    # one candidate: the output is its V row exactly (bf16 in, bf16 out)
+    v = kv_bits[17, :512]
+    assert np.array_equal(bf16_bits_of(out[1]), np.broadcast_to(v, (32, 512)))
+    assert abs(float(lse[2, 0]) - math.log(40)) < 1e-5
+
+
+@pytest.mark.parametrize("gain", [8.0, 40.0])
+def test_extreme_logits(gain):
+    """Large logits: the online max must move by far more than the rescale threshold."""
+    rng = np.random.default_rng(int(gain))
+    rows = 400
+    kv_bits = workloads.normal_bf16(rng, (rows, 576))
+    q = rng.standard_normal((2, 64, 576)).astype(np.float32) * gain
+    q_bits = workloads.bf16_bits(q)
+    ids = np.stack([rng.permutation(rows)[:300] for _ in range(2)]).astype(np.int32)
+    # token 0 lists its rows by ascending head-0 logit, so that head's running
+    # max rises tile after tile (input construction only)
+    z0 = workloads.bf16_bits(q[0, 0:1]).astype(np.uint32) << 16
+    qv = z0.view(np.float32).astype(np.float64)[0]
+    kvf = (kv_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ids[0] = ids[0][np.argsort(kvf[ids[0]] @ qv)]
+    for splits in (1, 4):
+        out, lse = _decode(q_bits, bf16_dev(kv_bits), ids, None, 1 / 24, splits)
+        o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, None, 1 / 24)
+        assert_attention_close(out, lse, o_ref, l_ref, f"gain={gain} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 8])
+def test_partial_states(splits):
+    import sparse_top_paged_amd as stp
+    c, kv_bits, ref = _tiny()
+    o, m, l = stp.sparse_mla_decode_partial(bf16_dev(c.q_bits), bf16_dev(kv_bits),
+                                            to_dev(ref["slot"]), to_dev(ref["count"]), c.scale,
+                                            splits)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = oracle.attend_partial(c.q_bits, kv_bits, ref["slot"], ref["count"], c.scale,
+                                          splits)
+    o, m, l = (x.cpu().numpy().astype(np.float64) for x in (o, m, l))
+    live = l_r > 0
+    assert np.array_equal(l > 0, live)
+    assert np.all(np.isneginf(m[~live])) and np.all(o[~live] == 0)
+    assert np.max(np.abs(m[live] - m_r[live])) < 1e-4           # the split's max logit
+    assert np.max(np.abs(np.log(l[live]) - np.log(l_r[live]))) < 1e-2
+    norm = o[live] / l[live][:, None]
+    norm_r = o_r[live] / l_r[live][:, None]
+    assert np.max(np.abs(norm - norm_r)) < 2e-2
+    # the library merge of these states equals the single pass
+    out, lse = stp.splitkv_merge(*(torch.from_numpy(x.astype(np.float32)).to(dev()) for x in (o, m, l)))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attend_sparse(c.q_bits, kv_bits, ref["slot"], ref["count"], c.scale)
+    assert_attention_close(out, lse, o_ref, l_ref, f"partial+merge splits={splits}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 8, 33])
+def test_merge_against_oracle(S):
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(S)
+    T, H, dv = 3, 20, 512
+    m = (rng.standard_normal((T, S, H)) * 4).astype(np.float32)
+    l = rng.uniform(0.5, 30, size=(T, S, H)).astype(np.float32)
+    o = (rng.standard_normal((T, S, H, dv)) * l[..., None] * 0.1).astype(np.float32)
+    l[0, 0, :] = 0.0                     # an empty split: its m must be ignored
+    m[0, 0, :] = 1e30
+    o[0, 0] = 0.0
+    l[2, :, 3] = 0.0                     # a head with no live split
+    o[2, :, 3] = 0.0
+    out, lse = stp.splitkv_merge(*(torch.from_numpy(x).to(dev()) for x in (o, m, l)))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge(o.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
+    assert_attention_close(out, lse, o_ref, l_ref, f"merge S={S}")
+    assert torch.all(out[2, 3] == 0) and torch.isneginf(lse[2, 3])
+
+
+def _sampled_check(case, kv, out, lse, tokens, where):
+    """Oracle over sampled tokens at full size, from rows copied back from the pool."""
+    ref = oracle.normalize(case.topk[tokens], case.req_id[tokens], case.q_pos[tokens], case.window,
+                           case.num_sinks, case.block_table, case.page_size, case.cap)
+    for j, t in enumerate(tokens):
+        n = ref["count"][j]
+        rows = ref["slot"][j, :n]
+        kv_rows = bf16_bits_of(kv[torch.from_numpy(rows.astype(np.int64)).to(kv.device)])
+        o_ref, l_ref = oracle.attend_sparse(case.q_bits[t:t + 1], kv_rows,
+                                            np.arange(n, dtype=np.int32)[None, :], None, case.scale)
+        assert_attention_close(out[t:t + 1], lse[t:t + 1], o_ref, l_ref, f"{where} token {t}")
+
+
+def test_deepseek_shape_full_size():
+    """Batch 32, 128 heads, context 32768, top-k 2048 + window 128 + 4 sinks, page 64, in the
+    benchmark's launch configuration (normalise, then decode with automatic splits)."""
+    import sparse_top_paged_amd as stp
+    c = workloads.deepseek_case()
+    kv = workloads.pool_torch(c.kv_rows, c.pool_seed, dev())
+    norm = stp.normalize_indices(to_dev(c.topk), to_dev(c.req_id), to_dev(c.q_pos),
+                                 to_dev(c.block_table), c.page_size, c.window, c.num_sinks, c.cap,
+                                 block_view=False)
+    out, lse = stp.sparse_mla_decode(bf16_dev(c.q_bits), kv, norm["slot"], norm["count"], c.scale)
+    torch.cuda.synchronize()
+    _sampled_check(c, kv, out, lse, [0, 13, 31], "deepseek")
+    # every token: finite output, lse finite
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    del kv
+
+
+@pytest.mark.parametrize("clustered", [False, True])
+def test_long_context_eight_splits(clustered):
+    """Batch 64, context 131072 (9.7 GB pool), top-k only, 8-way split then merge."""
+    import sparse_top_paged_amd as stp
+    c = workloads.locality_case(4002 if clustered else 4001, clustered)
+    kv = workloads.pool_torch(c.kv_rows, c.pool_seed, dev())
+    norm = stp.normalize_indices(to_dev(c.topk), to_dev(c.req_id), to_dev(c.q_pos),
+                                 to_dev(c.block_table), c.page_size, c.window, c.num_sinks, c.cap,
+                                 block_view=False)
+    out, lse = stp.sparse_mla_decode(bf16_dev(c.q_bits), kv, norm["slot"], norm["count"], c.scale,
+                                     num_splits=8)
+    torch.cuda.synchronize()
+    _sampled_check(c, kv, out, lse, [5, 63], "long context")
+    del kv
+    torch.cuda.empty_cache()
