@@ -1,0 +1,250 @@
+"""Decode-step benchmark of the top-k sparse MLA path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (DeepSeek-V3.2-shaped decode, one layer): 32 requests x 1 query
+token, 128 query heads, one latent KV head of bf16 rows of 576 (1152 B),
+context 32768, page size 64 over a shared 1,048,576-row pool (1.2 GB, in
+HBM), top-k 2048 uniform over the causal range + 128-token window + 4 sinks.
+
+A step is one pass of the hot path over one batch: candidate normalisation
+(with the block view) -> sparse MLA decode (split partial states) -> split
+merge.  Inputs are resident in HBM before timing starts.  Eight candidate
+sets (same pool, tables and queries, different top-k draws) rotate step by
+step, so a set's ~80 MB of rows is not still in the 256 MB Infinity Cache
+when it comes round again.
+
+Prints one JSON line.  `value` is query tokens per second over the timed
+steps; `roofline` is the decode kernel's algorithmic bytes per launch over
+its average duration (HIP events on its stream, inside the timed region);
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROW_BYTES = 1152
+METRIC = "decode query-tokens/sec and effective KV GB/s (% HBM/MFMA roofline), 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sets", type=int, default=8, help="candidate sets rotated step by step")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic choice")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg_bytes):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    valid only while the kernel source is the one they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != source_sha(DECODE_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def rows_bits(kv, rows):
+    """Selected pool rows copied to the host as bf16 bit patterns."""
+    import torch
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(kv.device)
+    return kv[idx].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def cpu_baseline(cases, kv, budget_s):
+    """Time the oracle (normalise + fp64 attention) on as many query tokens of
+    the workload as fit the budget; rows are copied to the host first."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    c = cases[0]
+    # host copies of every candidate row of the first 8 tokens (untimed)
+    tokens = list(range(min(8, c.T)))
+    ref = oracle.normalize(c.topk[tokens], c.req_id[tokens], c.q_pos[tokens], c.window,
+                           c.num_sinks, c.block_table, c.page_size, c.cap)
+    rows = [ref["slot"][j, :ref["count"][j]] for j in range(len(tokens))]
+    host_rows = [rows_bits(kv, r) for r in rows]
+    done, t0 = 0, time.perf_counter()
+    for j, t in enumerate(tokens):
+        oracle.normalize(c.topk[t:t + 1], c.req_id[t:t + 1], c.q_pos[t:t + 1], c.window,
+                         c.num_sinks, c.block_table, c.page_size, c.cap)
+        n = len(rows[j])
+        oracle.attend_sparse(c.q_bits[t:t + 1], host_rows[j], np.arange(n, dtype=np.int32)[None, :],
+                             None, c.scale)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": done / el,
+        "unit": "query-tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of the {c.T} query tokens of the timed batch (all 128 heads each), "
+                  f"normalisation + fp64 attention, {el:.1f} s on the host",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cases = [workloads.deepseek_case(variant=v) for v in range(args.sets)]
+    c0 = cases[0]
+    T, H, cap = c0.T, c0.H, c0.cap
+    kv = workloads.pool_torch(c0.kv_rows, c0.pool_seed, dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q = t(c0.q_bits.view(np.int16)).view(torch.bfloat16)
+    req, qpos, table = t(c0.req_id), t(c0.q_pos), t(c0.block_table)
+    topks = [t(c.topk) for c in cases]
+
+    S = stp.decode_splits(T, H, cap, args.splits)
+    norm = [stp.normalize_indices(tk, req, qpos, table, c0.page_size, c0.window, c0.num_sinks,
+                                  cap) for tk in topks]
+    o_part = torch.empty((T, S, H, 512), dtype=torch.float32, device=dev)
+    m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    counts = [n["count"].cpu().numpy().astype(np.int64) for n in norm]
+
+    def step(i, ev=None):
+        k = i % args.sets
+        nb = stp.normalize_indices(topks[k], req, qpos, table, c0.page_size, c0.window,
+                                   c0.num_sinks, cap, out=norm[k])
+        if ev is not None:
+            ev[0].record()
+        if S > 1:
+            stp.sparse_mla_decode_partial(q, kv, nb["slot"], nb["count"], c0.scale, S,
+                                          o_part, m_part, l_part)
+            if ev is not None:
+                ev[1].record()
+            stp.splitkv_merge(o_part, m_part, l_part, out, lse)
+        else:
+            stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
+            if ev is not None:
+                ev[1].record()
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    dec_us = np.asarray([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    merge_us = np.asarray([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+
+    # algorithmic bytes / flops of one decode launch (average over the rotated sets)
+    q_bytes = T * H * 576 * 2
+    o_bytes = T * H * (512 * 2 + 4)
+    sel = np.asarray([cnt.sum() for cnt in counts], dtype=np.float64)  # sum of |S_i| per set
+    per_set_steps = np.bincount((args.warmup + np.arange(args.steps)) % args.sets,
+                                minlength=args.sets)
+    mean_sel = float((sel * per_set_steps).sum() / per_set_steps.sum())
+    kv_bytes = mean_sel * ROW_BYTES
+    dec_bytes = kv_bytes + q_bytes + mean_sel * 4 + (o_bytes if S == 1 else 0)
+    flops = 2.0 * H * mean_sel * (576 + 512)
+    dec_avg_s = float(dec_us.mean()) * 1e-6
+    step_s = total_ms * 1e-3 / args.steps
+    achieved = dec_bytes / dec_avg_s / 1e9
+    traffic = load_traffic(dec_bytes)
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / step_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "deepseek-v3.2-shaped sparse MLA decode, one layer",
+            "batch": T, "query_heads": H, "context": 32768, "page_size": c0.page_size,
+            "top_k": c0.top_k, "window": c0.window, "sinks": c0.num_sinks, "row_bytes": ROW_BYTES,
+            "kv_pool_rows": c0.kv_rows, "splits": S, "candidate_sets": args.sets,
+            "mean_selected_rows_per_token": round(mean_sel / T, 2),
+        },
+        "roofline": {
+            "kernel": "sparse_mla_decode_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+            "avg_launch_us": round(float(dec_us.mean()), 3),
+            "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
+        "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
+        "kernel_us": {
+            "decode_median": round(float(np.median(dec_us)), 3),
+            "decode_p95": round(float(np.percentile(dec_us, 95)), 3),
+            "decode_p99": round(float(np.percentile(dec_us, 99)), 3),
+            "merge_median": round(float(np.median(merge_us)), 3),
+        },
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cases, kv, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
