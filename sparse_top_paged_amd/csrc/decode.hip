@@ -102,6 +102,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would drain the tile ring
+// at each barrier; the tile loads are waited for explicitly instead.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
@@ -132,9 +141,11 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const int lo = min(n, s * chunk);
   const int len = min(n, lo + chunk) - lo;
 
+  // candidate ids of this split, -1 for invalid ones and up to the tile edge
   const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
-  for (int j = tid; j < len; j += kThreads) {
-    const int32_t id = src_ids[j];
+  const int len_pad = (len + kTileRows - 1) / kTileRows * kTileRows;
+  for (int j = tid; j < len_pad; j += kThreads) {
+    const int32_t id = j < len ? src_ids[j] : -1;
     ids[j] = (id >= 0 && id < a.kv_rows) ? id : -1;
   }
 
@@ -165,8 +176,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       const int slot = (wave * kSlotsPerThread + it) * 64 + lane;
       const int r = slot / kChunks;
       const int c = (slot - r * kChunks) ^ swz(r);
-      const int pos = i * kTileRows + r;
-      const int id = pos < len ? ids[pos] : -1;
+      const int id = ids[i * kTileRows + r];
       const uint8_t* src = id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes + c * 16
                                    : g_zero_row + c * 16;
       __builtin_amdgcn_global_load_lds((const void*)src,
@@ -190,11 +200,10 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       wait_vmcnt<kSlotsPerThread>();
     else
       wait_vmcnt<0>();
-    __syncthreads();  // tile i landed for every wave; stage (i-1) % 3 is free
+    lds_barrier();  // tile i landed for every wave; stage (i-1) % 3 is free
     if (i + kStages - 1 < ntiles) issue(i + kStages - 1, (i + kStages - 1) % kStages);
 
-    const int prow = i * kTileRows + (lane & 31);
-    const bool row_valid = prow < len && ids[prow] >= 0;
+    const bool row_valid = ids[i * kTileRows + (lane & 31)] >= 0;
     const uint32_t vmask = (uint32_t)__ballot(row_valid);
     if (vmask == 0) continue;  // same for every wave of the workgroup
 
@@ -214,7 +223,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     for (int j = 0; j < 4; ++j)
       *(float4*)(xchg + ((wave * 4 + j) * 64 + lane) * 4) =
           make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 p = *(const float4*)(xchg + (((wave ^ 2) * 4 + j) * 64 + lane) * 4);
@@ -238,7 +247,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const bool need = mt > m_ref + kRescaleLog2;
     if (__ballot(need)) {
       const float m_new = need ? mt : m_ref;
-      const float alpha = need ? exp2f(m_ref - m_new) : 1.f;
+      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;
       m_ref = m_new;
       lsum *= alpha;
 #pragma unroll
@@ -248,7 +257,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(sv[r] - m_ref);
+      const float p = fast_exp2(sv[r] - m_ref);
       psum += p;
       pk[r >> 3][r & 7] = (__bf16)p;
     }
@@ -282,7 +291,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const int dv_lane = 256 * dh + 4 * (lane >> 5);
   if (kSplit) {
     const bool live = m_true != -INFINITY;
-    const float f = live ? exp2f(m_ref - m_true) : 0.f;  // rebase to the true maximum
+    const float f = live ? fast_exp2(m_ref - m_true) : 0.f;  // rebase to the true maximum
     float* orow = a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)

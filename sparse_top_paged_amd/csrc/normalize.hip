@@ -19,10 +19,12 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxPositions = 1 << 20;  // bitmap of 128 KiB LDS
+constexpr int kMaxPositions = 1 << 20;     // bitmap of 128 KiB LDS
+constexpr int kLdsBudget = 150 * 1024;     // dynamic LDS a normalise workgroup may use
+constexpr int kBlockViewMaxCap = 12000;    // block fill keeps 12 bytes per candidate in LDS
 
 struct TokenView {
-  const int32_t* table;
+  const int32_t* table;  // the request's page-table row (LDS copy or global)
   int max_blocks;
   int P;
   int q;
@@ -40,24 +42,30 @@ __device__ __forceinline__ bool visible(const TokenView& v, int t) {
   return slot <= INT32_MAX;
 }
 
+__device__ __forceinline__ void set_bit(uint64_t* bm, int t) {
+  atomicOr((unsigned long long*)&bm[t >> 6], 1ull << (t & 63));
+}
+
 // Bits of positions [lo, hi) (hi - lo <= 64) taken from the bitmap.
 __device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, int hi, int nwords) {
   uint64_t acc = 0;
   const int w0 = lo >> 6, w1 = (hi - 1) >> 6;
   for (int w = w0; w <= w1 && w < nwords; ++w) {
     const int a = max(lo, w * 64) - w * 64;
-    const int b = min(hi, w * 64 + 64) - w * 64;  // (a, b] within word
-    uint64_t m = (b - a == 64) ? ~0ull : (((1ull << (b - a)) - 1) << a);
+    const int b = min(hi, w * 64 + 64) - w * 64;
+    const uint64_t m = (b - a == 64) ? ~0ull : (((1ull << (b - a)) - 1) << a);
     acc |= (bm[w] & m);
   }
   return acc;
 }
 
+// One workgroup per query token.  LDS: the position bitmap (nwords 64-bit
+// words), then, when table_in_lds, the request's page-table row.
 __global__ __launch_bounds__(kThreads) void normalize_kernel(
     const int32_t* __restrict__ topk, int top_k, const int32_t* __restrict__ req_id,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ block_table, int num_reqs,
-    int max_blocks, int P, int window, int num_sinks, int cap, int32_t* __restrict__ tok_out,
-    int32_t* __restrict__ slot_out, int32_t* __restrict__ count_out,
+    int max_blocks, int P, int window, int num_sinks, int cap, int nwords_alloc, int table_in_lds,
+    int32_t* __restrict__ tok_out, int32_t* __restrict__ slot_out, int32_t* __restrict__ count_out,
     int32_t* __restrict__ dropped_out, int32_t* __restrict__ blk_count) {
   extern __shared__ uint64_t bitmap[];
   __shared__ int s_scan[8];
@@ -84,36 +92,51 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(
     return;
   }
 
-  TokenView v{block_table + (int64_t)r * max_blocks, max_blocks, P, q};
+  const int32_t* g_table = block_table + (int64_t)r * max_blocks;
   const int limit = min(q, max_blocks * P - 1);  // last position that can be visible
   const int nwords = (limit >> 6) + 1;
+  const int used_blocks = limit / P + 1;           // table entries that can matter
+  int32_t* l_table = (int32_t*)(bitmap + nwords_alloc);
   for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
+  if (table_in_lds)
+    for (int b = tid; b < used_blocks; b += kThreads) l_table[b] = g_table[b];
   if (tid == 0) {
     s_dropped = 0;
     s_blocks = 0;
   }
   __syncthreads();
+  const TokenView v{table_in_lds ? l_table : g_table, max_blocks, P, q};
 
-  // D: the dynamic top-k entries; invalid ones are dropped and counted.
+  // D: the dynamic top-k entries, four independent loads in flight per
+  // thread; invalid ones are dropped and counted.
   int my_dropped = 0;
   const int32_t* drow = topk + (int64_t)i * top_k;
-  for (int j = tid; j < top_k; j += kThreads) {
-    const int t = drow[j];
-    if (t < 0) continue;
-    if (visible(v, t))
-      atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
-    else
-      ++my_dropped;
+  for (int j0 = tid; j0 < top_k; j0 += 4 * kThreads) {
+    int tv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kThreads;
+      tv[u] = j < top_k ? drow[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tv[u];
+      if (t < 0) continue;
+      if (visible(v, t))
+        set_bit(bitmap, t);
+      else
+        ++my_dropped;
+    }
   }
   // W: the local window ending at the query's own position.
   if (window > 0) {
     for (int t = max(0, q - window + 1) + tid; t <= q; t += kThreads)
-      if (visible(v, t)) atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
+      if (visible(v, t)) set_bit(bitmap, t);
   }
   // A: the sink positions.
   const int na = min(num_sinks, q + 1);
   for (int t = tid; t < na; t += kThreads)
-    if (visible(v, t)) atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
+    if (visible(v, t)) set_bit(bitmap, t);
   if (my_dropped) atomicAdd(&s_dropped, my_dropped);
   __syncthreads();
 
@@ -142,9 +165,8 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(
 
   // Number of touched logical blocks (for the CSR block view).
   if (blk_count) {
-    const int nblocks = limit / P + 1;
     int nb = 0;
-    for (int b = tid; b < nblocks; b += kThreads) {
+    for (int b = tid; b < used_blocks; b += kThreads) {
       const int lo = b * P, hi = min(lo + P, limit + 1);
       if (bits_in_range(bitmap, lo, hi, nwords)) ++nb;
     }
@@ -174,43 +196,50 @@ __global__ __launch_bounds__(kThreads) void indptr_scan_kernel(int32_t* indptr, 
   if (threadIdx.x == 0) indptr[0] = 0;
 }
 
-// Per token: walk the sorted S and write one entry per touched logical block.
+// Per token: one entry per touched logical block of the sorted S.  The
+// token's list is staged in LDS; block k of the token collects its in-page
+// bits with LDS atomics, so no thread walks a block serially.
 __global__ __launch_bounds__(kThreads) void block_fill_kernel(
     const int32_t* __restrict__ tok_out, const int32_t* __restrict__ count_out,
     const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table, int max_blocks,
     int P, int cap, const int32_t* __restrict__ indptr, int32_t* __restrict__ blk_logical,
     int32_t* __restrict__ blk_page, uint64_t* __restrict__ blk_mask) {
+  extern __shared__ uint64_t lmask[];  // [cap] block masks, then [cap] tokens
   __shared__ int s_scan[8];
   const int i = blockIdx.x;
   const int n = count_out[i];
   if (n == 0) return;
+  int32_t* ltok = (int32_t*)(lmask + cap);
   const int32_t* tok = tok_out + (int64_t)i * cap;
   const int32_t* table = block_table + (int64_t)req_id[i] * max_blocks;
   const int out0 = indptr[i];
-  int carry = 0;
+  const int nb = indptr[i + 1] - out0;
+  for (int j = threadIdx.x; j < n; j += kThreads) ltok[j] = tok[j];
+  for (int k = threadIdx.x; k < nb; k += kThreads) lmask[k] = 0;
+  __syncthreads();
+  int carry = 0;  // blocks started before this chunk
   for (int base = 0; base < n; base += kThreads) {
     const int j = base + threadIdx.x;
     int start = 0, t = 0, b = 0;
     if (j < n) {
-      t = tok[j];
+      t = ltok[j];
       b = t / P;
-      start = (j == 0) || (tok[j - 1] / P != b);
+      start = (j == 0) || (ltok[j - 1] / P != b);
     }
     int total;
-    const int k = stp::block_exclusive_scan_256(start, s_scan, &total);
-    if (start) {
-      uint64_t mask = 0;
-      for (int jj = j; jj < n; ++jj) {
-        const int tt = tok[jj];
-        if (tt / P != b) break;
-        mask |= 1ull << (tt - b * P);
+    const int ex = stp::block_exclusive_scan_256(start, s_scan, &total);
+    if (j < n) {
+      const int k = carry + ex + start - 1;  // this token's block
+      atomicOr((unsigned long long*)&lmask[k], 1ull << (t - b * P));
+      if (start) {
+        blk_logical[out0 + k] = b;
+        blk_page[out0 + k] = table[b];
       }
-      blk_logical[out0 + carry + k] = b;
-      blk_page[out0 + carry + k] = table[b];
-      blk_mask[out0 + carry + k] = mask;
     }
     carry += total;
   }
+  __syncthreads();
+  for (int k = threadIdx.x; k < nb; k += kThreads) blk_mask[out0 + k] = lmask[k];
 }
 
 }  // namespace
@@ -246,28 +275,35 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
     num_reqs = 0;
   }
 
+  if (blk_indptr && cap > kBlockViewMaxCap)
+    return fail(STP_ERR_INVALID_ARG, "normalize_indices: the block view supports cap <= %d",
+                kBlockViewMaxCap);
+
   const int nwords = max(1, (int)(((int64_t)max_blocks * page_size + 63) / 64));
-  const size_t lds = (size_t)nwords * sizeof(uint64_t);
+  const size_t bitmap_bytes = (size_t)nwords * sizeof(uint64_t);
+  const bool table_in_lds = bitmap_bytes + (size_t)max_blocks * 4 <= (size_t)kLdsBudget;
+  const size_t lds = bitmap_bytes + (table_in_lds ? (size_t)max_blocks * 4 : 0);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)normalize_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(kMaxPositions / 8)) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)block_fill_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess)
       return fail(STP_ERR_HIP, "normalize_indices: hipFuncSetAttribute failed");
     attr_set = true;
   }
   int32_t* blk_count = blk_indptr ? blk_indptr + 1 : nullptr;
-  normalize_kernel<<<T, kThreads, lds, stream>>>(topk, top_k, req_id, q_pos, block_table, num_reqs,
-                                                 max_blocks, page_size, window, num_sinks, cap,
-                                                 tok_out, slot_out, count_out, dropped_out,
-                                                 blk_count);
+  normalize_kernel<<<T, kThreads, lds, stream>>>(
+      topk, top_k, req_id, q_pos, block_table, num_reqs, max_blocks, page_size, window, num_sinks,
+      cap, nwords, table_in_lds ? 1 : 0, tok_out, slot_out, count_out, dropped_out, blk_count);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
   if (blk_indptr) {
     indptr_scan_kernel<<<1, kThreads, 0, stream>>>(blk_indptr, T);
     if (int rc = stp::check_launch("indptr_scan_kernel")) return rc;
-    block_fill_kernel<<<T, kThreads, 0, stream>>>(tok_out, count_out, req_id, block_table,
-                                                  max_blocks, page_size, cap, blk_indptr,
-                                                  blk_logical, blk_page, blk_mask);
+    block_fill_kernel<<<T, kThreads, (size_t)cap * 12, stream>>>(
+        tok_out, count_out, req_id, block_table, max_blocks, page_size, cap, blk_indptr,
+        blk_logical, blk_page, blk_mask);
     if (int rc = stp::check_launch("block_fill_kernel")) return rc;
   }
   return STP_OK;
