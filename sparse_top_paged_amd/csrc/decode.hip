@@ -31,11 +31,9 @@
 //     read), B = P^T taken straight from the logit registers: the k-slot to
 //     row mapping of the V reads is chosen to match the accumulator layout,
 //     so P never moves between lanes.
-// Rows are staged in a 3-deep LDS ring of 32-row tiles (36 KiB each) with
-// global_load_lds_dwordx4, so no VGPRs hold KV data in flight; chunks are
-// XOR-swizzled per row so both the K reads (ds_read_b128) and the V transpose
-// reads are free of bank conflicts.  Invalid candidates load a zero row and
-// are masked to -inf before the exponent.
+// Rows are staged in a 3-deep LDS ring of 32-row tiles (36.5 KiB each) with
+// global_load_lds_dwordx4, so no VGPRs hold KV data in flight.  Invalid
+// candidates load a zero row and are masked to -inf before the exponent.
 
 #include "stp_internal.h"
 
@@ -47,7 +45,9 @@ constexpr int kDV = 512;
 constexpr int kRowBytes = kDQK * 2;                             // 1152
 constexpr int kChunks = kRowBytes / 16;                         // 72 x 16 B
 constexpr int kTileRows = 32;
-constexpr int kTileBytes = kTileRows * kRowBytes;               // 36 KiB
+constexpr int kGroupRows = 8;                                   // rows loaded by one wave
+constexpr int kGroupBytes = kGroupRows * kRowBytes + 128;       // 9344 (+128: bank offset)
+constexpr int kTileBytes = 4 * kGroupBytes;                     // 37376
 constexpr int kStages = 3;
 constexpr int kSlotsPerThread = kTileRows * kChunks / kThreads; // 9
 constexpr int kHeadsPerWG = 64;
@@ -62,6 +62,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
 
 static_assert(kTileRows * kChunks % kThreads == 0, "tile slots per thread");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -73,13 +74,13 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // Source of every masked-out row: loads stay in bounds and bring zeros.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytes] = {};
 
-// Per-row XOR on the 16-byte chunk index (search over both 32- and 64-bank
-// LDS models: conflict-free for the K and the V-transpose read patterns).
-__device__ __forceinline__ int swz(int r) {
-  return (((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1);
-}
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
-
+// LDS tile layout: four groups of 8 rows (one group per wave when loading);
+// inside a group the 16-byte chunks are chunk-major, so chunk c of group row
+// rl sits at group + (c * 8 + rl) * 16.  One load instruction of a wave then
+// fills 8 consecutive chunks of its 8 rows (1 KiB of LDS, 8 x 128 B of HBM),
+// every lane keeps one row for the whole tile, and every LDS read address
+// below is a per-lane base plus a compile-time offset.  Groups are padded by
+// 128 B so that rows r and r + 8 fall in different halves of the 64 banks.
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kv;
@@ -105,19 +106,57 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
 // every outstanding global load (vmcnt(0)), which would drain the tile ring
 // at each barrier; the tile loads are waited for explicitly instead.
+// The signal fences only stop the compiler from moving memory accesses across
+// the barrier; the hardware wait is lgkmcnt(0) (LDS) alone.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool kSplit>
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): global address vaddr + offset, LDS address
+// m0 + offset + 16 * lane -- the immediate offset applies to both sides.
+// Issued from inline asm so that the compiler's
+// wait-count pass does not track these loads: the tile ring waits for them
+// explicitly (wait_vmcnt), and the compiler would otherwise drain the ring
+// before every LDS access it cannot prove disjoint from the loads in flight.
+template <int kOffset>
+__device__ __forceinline__ void load_lds_16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off offset:%1" ::"v"(gptr), "n"(kOffset),
+               "{m0}"(lds_addr));
+}
+
+template <int It>
+__device__ __forceinline__ void load_row_chunks(const uint8_t* src, uint32_t lds_addr) {
+  if constexpr (It < kSlotsPerThread) {
+    // chunk column It: global src + 128 It, LDS lds_addr + 1024 It
+    load_lds_16<It * 128>(src, lds_addr + It * (1024 - 128));
+    load_row_chunks<It + 1>(src, lds_addr);
+  }
+}
+
+// Output modes of the decode kernel.
+enum OutMode : int {
+  kOutFinal = 0,       // out = o / l (bf16), lse
+  kOutPartialF32 = 1,  // per split: o (unnormalised, fp32), m (natural log), l
+  kOutPartialBf16 = 2  // per split: o / l (bf16), m (natural log), l -- the internal split path
+};
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  lds_t* lds = (lds_t*)smem;
-  int32_t* ids = (int32_t*)(smem + kLdsIds);
-  float* xchg = (float*)(smem + kLdsXchg);
+  // Three separate LDS objects: the compiler can then tell that the exchange
+  // buffer and the id list never alias the tile ring.
+  __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_xchg[kXchgBytes / 4];
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
+  lds_t* lds = (lds_t*)s_tiles;
+  int32_t* ids = s_ids;
+  float* xchg = s_xchg;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,14 +179,31 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const int chunk = (n + a.S - 1) / a.S;
   const int lo = min(n, s * chunk);
   const int len = min(n, lo + chunk) - lo;
+  const int ntiles = (len + kTileRows - 1) / kTileRows;
 
   // candidate ids of this split, -1 for invalid ones and up to the tile edge
   const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
-  const int len_pad = (len + kTileRows - 1) / kTileRows * kTileRows;
-  for (int j = tid; j < len_pad; j += kThreads) {
+  for (int j = tid; j < ntiles * kTileRows; j += kThreads) {
     const int32_t id = j < len ? src_ids[j] : -1;
     ids[j] = (id >= 0 && id < a.kv_rows) ? id : -1;
   }
+  __syncthreads();  // ids visible
+
+  // Enqueue the 32 rows of tile i into ring stage st: lane keeps row
+  // 8 * wave + lane % 8 and chunks 8 * it + lane / 8, it = 0..8.
+  const int ld_row = wave * kGroupRows + (lane & 7);
+  const int ld_col = (lane >> 3) * 16;
+  auto issue = [&](int i, int st) {
+    const int id = ids[i * kTileRows + ld_row];
+    const uint8_t* src =
+        (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds + st * kTileBytes + wave * kGroupBytes));
+    load_row_chunks<0>(src, dst);
+  };
+  // The first two tiles are in flight while Q is fetched.
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
 
   // Q^T fragments: lane holds Q[head][288 dh + 16 ks + 8 (lane / 32) + 0..7].
   const int head = hg * kHeadsPerWG + hq * 32 + (lane & 31);
@@ -163,67 +219,88 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  __syncthreads();  // ids visible
 
-  const int ntiles = (len + kTileRows - 1) / kTileRows;
-
-  // Enqueue the 32 rows of tile i into ring stage st: slot (wave*9+it)*64+lane
-  // of the tile holds chunk (slot % 72) ^ swz(row) of row slot / 72.
-  auto issue = [&](int i, int st) {
-    lds_t* stage = lds + st * kTileBytes;
-#pragma unroll
-    for (int it = 0; it < kSlotsPerThread; ++it) {
-      const int slot = (wave * kSlotsPerThread + it) * 64 + lane;
-      const int r = slot / kChunks;
-      const int c = (slot - r * kChunks) ^ swz(r);
-      const int id = ids[i * kTileRows + r];
-      const uint8_t* src = id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes + c * 16
-                                   : g_zero_row + c * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (lds_t*)(stage + (wave * kSlotsPerThread + it) * 1024), 16,
-                                       0, 0);
-    }
-  };
+  // Per-lane LDS read bases (see the layout note above).
+  //  K fragment of k-step ks: row lane % 32, chunk 36 dh + 2 ks + lane / 32.
+  const int kr = lane & 31;
+  const int k_base = (kr >> 3) * kGroupBytes + (kr & 7) * 16 + (36 * dh + (lane >> 5)) * 128;
+  //  V^T fragment (transpose read): rows 16 kap + 4 (g / 2) + j / 4 (+ 8),
+  //  values 256 dh + 32 mb + 16 (g % 2) + 4 (j % 4) .. + 3, g = lane / 16, j = lane % 16.
+  const int vg = lane >> 4, vj = lane & 15;
+  const int v_base = (4 * (vg >> 1) + (vj >> 2)) * 16 +
+                     (32 * dh + 2 * (vg & 1) + ((vj & 3) >> 1)) * 128 + 8 * (vj & 1);
 
   floatx16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = floatx16{};
   float m_ref = -INFINITY, m_true = -INFINITY, lsum = 0.f;
 
+  // Pipeline (one barrier per tile).  At the top of iteration i the K
+  // fragments of tile i are in registers and tiles i+1, i+2 are in the ring
+  // or in flight.  Iteration i: QK MFMAs of tile i under the V transpose
+  // reads of tile i; publish the logit half; wait for tile i+1 and barrier
+  // (which also frees ring stage i % 3); enqueue tile i+3 there; softmax;
+  // PV MFMAs of tile i under the K reads of tile i+1.
+  shortx8 kf[kKSteps];
+  wait_vmcnt<0>();  // tiles 0 and 1 (and Q)
+  lds_barrier();
+  if (ntiles > 2) issue(2, 2);
+  if (ntiles > 0) {
+    const lds_t* kp = lds + k_base;
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (i < ntiles) issue(i, i);
+    for (int ks = 0; ks < kKSteps; ++ks)
+      kf[ks] = *(const __attribute__((address_space(3))) shortx8*)(kp + 256 * ks);
+  }
 
   for (int i = 0; i < ntiles; ++i) {
     const int st = i % kStages;
-    if (i + 1 < ntiles)
-      wait_vmcnt<kSlotsPerThread>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();  // tile i landed for every wave; stage (i-1) % 3 is free
-    if (i + kStages - 1 < ntiles) issue(i + kStages - 1, (i + kStages - 1) % kStages);
-
+    const lds_t* stage = lds + st * kTileBytes;
     const bool row_valid = ids[i * kTileRows + (lane & 31)] >= 0;
     const uint32_t vmask = (uint32_t)__ballot(row_valid);
-    if (vmask == 0) continue;  // same for every wave of the workgroup
 
-    const lds_t* stage = lds + st * kTileBytes;
-
-    // S^T partial = K_tile[:, 288 dh .. +288] Q^T
-    floatx16 acc = floatx16{};
+    // S^T partial = K_tile[:, 288 dh .. +288] Q^T, with the tile's V^T
+    // fragments read meanwhile.
+    // two independent accumulator chains (dependent MFMAs issue ~1.5x slower)
+    floatx16 acc = floatx16{}, acc2 = floatx16{};
+    shortx4 v0[2][8], v1[2][8];
+    const lds_t* vp = stage + v_base;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const int c = 36 * dh + 2 * ks + (lane >> 5);
-      const shortx8 kraw = *(const __attribute__((address_space(3))) shortx8*)(stage + tile_off(lane & 31, c));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw), qf[ks], acc,
+    for (int kap = 0; kap < 2; ++kap)
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4*)(vp + 2 * kap * kGroupBytes + 512 * mb));
+        v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4*)(vp + (2 * kap + 1) * kGroupBytes + 512 * mb));
+      }
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ks += 2) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], acc,
                                                     0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks + 1]),
+                                                     qf[ks + 1], acc2, 0, 0, 0);
     }
-    // exchange halves with the partner wave (same heads, other dims)
+    // interleave: one MFMA, then two transpose reads
+#pragma unroll
+    for (int g = 0; g < kKSteps; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    acc += acc2;
+
+    // publish this wave's half of the logits
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *(float4*)(xchg + ((wave * 4 + j) * 64 + lane) * 4) =
           make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-    lds_barrier();
+    // tile i+1 must have landed (tile i+2 may still be in flight)
+    if (i + 2 < ntiles)
+      wait_vmcnt<kSlotsPerThread>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // halves visible; tile i+1 visible; stage i % 3 read by every wave
+    if (i + 3 < ntiles) issue(i + 3, st);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float4 p = *(const float4*)(xchg + (((wave ^ 2) * 4 + j) * 64 + lane) * 4);
@@ -233,7 +310,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       acc[4 * j + 3] += p.w;
     }
 
-    // mask, then the online softmax of this lane's head (base 2)
+    // mask, then the online softmax of this lane's head (base 2).  A tile
+    // with no valid row leaves the state untouched (p = 0, no rescale).
     float sv[16];
     float mt = -INFINITY;
 #pragma unroll
@@ -257,40 +335,44 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(sv[r] - m_ref);
+      const float p = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - m_ref);
       psum += p;
       pk[r >> 3][r & 7] = (__bf16)p;
     }
     lsum += psum;
 
-    // O^T[256 dh + 32 mb + m][head] += V^T P^T
-    const int g = lane >> 4;
-    const int j16 = lane & 15;
+    // O^T[256 dh + 32 mb + m][head] += V^T P^T, with the next tile's K
+    // fragments read meanwhile.
 #pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-      const int row0 = 16 * kap + 4 * (g >> 1) + (j16 >> 2);
+    for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const int dvi = 256 * dh + 32 * mb + 16 * (g & 1) + 4 * (j16 & 3);
-        const int cc = dvi >> 3;
-        const int boff = (dvi & 7) * 2;
-        const shortx4 v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(stage + tile_off(row0, cc) + boff));
-        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_shortx4*)(stage + tile_off(row0 + 8, cc) + boff));
-        const shortx8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const shortx8 vv = {v0[kap][mb][0], v0[kap][mb][1], v0[kap][mb][2], v0[kap][mb][3],
+                            v1[kap][mb][0], v1[kap][mb][1], v1[kap][mb][2], v1[kap][mb][3]};
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pk[kap],
                                                         o[mb], 0, 0, 0);
       }
+    {
+      // (on the last tile this reads a stale stage: in bounds and unused)
+      const lds_t* kp = lds + ((i + 1) % kStages) * kTileBytes + k_base;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        kf[ks] = *(const __attribute__((address_space(3))) shortx8*)(kp + 256 * ks);
     }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   const float l_tot = lsum + __shfl_xor(lsum, 32);
   if (!head_ok) return;
   // lane holds O^T[256 dh + 32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][head]
   const int dv_lane = 256 * dh + 4 * (lane >> 5);
-  if (kSplit) {
-    const bool live = m_true != -INFINITY;
+  const bool live = m_true != -INFINITY;
+  if (kMode == kOutPartialF32) {
     const float f = live ? fast_exp2(m_ref - m_true) : 0.f;  // rebase to the true maximum
     float* orow = a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
 #pragma unroll
@@ -306,8 +388,11 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       a.l_part[k] = l_tot * f;
     }
   } else {
+    // bf16 o / l: the final output, or a normalised split partial
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = a.out + ((int64_t)t * a.H + head) * kDV;
+    uint16_t* orow = kMode == kOutFinal
+                         ? a.out + ((int64_t)t * a.H + head) * kDV
+                         : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -318,8 +403,17 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
                             ((uint32_t)stp::f32_to_bf16_rne(o[mb][4 * rq + 3] * inv) << 16);
         *(uint2*)(orow + dv_lane + 32 * mb + 8 * rq) = make_uint2(w0, w1);
       }
-    if (a.lse && dh == 0 && lane < 32)
-      a.lse[(int64_t)t * a.H + head] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (dh == 0 && lane < 32) {
+      if (kMode == kOutFinal) {
+        if (a.lse)
+          a.lse[(int64_t)t * a.H + head] = live ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        // normalised partial: l relative to m_ref, m reported as m_ref
+        const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
+        a.m_part[k] = live ? m_ref * kLn2 : -INFINITY;
+        a.l_part[k] = live ? l_tot : 0.f;
+      }
+    }
   }
 }
 
@@ -339,19 +433,10 @@ int32_t choose_splits(int32_t T, int32_t H, int32_t cap, int32_t requested) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int launch_decode(bool split, const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                   const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T, int32_t H,
                   float scale, int32_t S, float* o_part, float* m_part, float* l_part,
                   uint16_t* out, float* lse, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)sparse_mla_decode_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess ||
-        hipFuncSetAttribute((const void*)sparse_mla_decode_kernel<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
-      return stp::fail(STP_ERR_HIP, "sparse_mla_decode: hipFuncSetAttribute failed");
-    attr_set = true;
-  }
   DecodeArgs a;
   a.q = q;
   a.kv = kv;
@@ -372,10 +457,12 @@ int launch_decode(bool split, const uint16_t* q, const uint16_t* kv, int64_t kv_
   a.lse = lse;
   const int64_t blocks = (int64_t)8 * a.G * ((a.ntasks + 7) / 8);
   if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: grid too large");
-  if (split)
-    sparse_mla_decode_kernel<true><<<(unsigned)blocks, kThreads, kLdsBytes, stream>>>(a);
+  if (mode == kOutPartialF32)
+    sparse_mla_decode_kernel<kOutPartialF32><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+  else if (mode == kOutPartialBf16)
+    sparse_mla_decode_kernel<kOutPartialBf16><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   else
-    sparse_mla_decode_kernel<false><<<(unsigned)blocks, kThreads, kLdsBytes, stream>>>(a);
+    sparse_mla_decode_kernel<kOutFinal><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   return stp::check_launch("sparse_mla_decode_kernel");
 }
 
@@ -405,7 +492,7 @@ extern "C" size_t stp_sparse_mla_decode_workspace(int32_t T, int32_t H, int32_t 
   const int32_t S = stp_sparse_mla_decode_splits(T, H, cap, num_splits);
   if (S <= 1) return 0;
   const size_t n = (size_t)T * S * H;
-  return align256(n * kDV * 4) + 2 * align256(n * 4);
+  return align256(n * kDV * 2) + 2 * align256(n * 4);  // bf16 o / l, then m and l
 }
 
 extern "C" int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
@@ -419,21 +506,23 @@ extern "C" int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int6
   if (!out) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: null out");
   const int32_t S = choose_splits(T, H, cap, num_splits);
   if (S == 1)
-    return launch_decode(false, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, 1, nullptr,
+    return launch_decode(kOutFinal, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, 1, nullptr,
                          nullptr, nullptr, out, lse, stream);
   const size_t need = stp_sparse_mla_decode_workspace(T, H, cap, num_splits);
   if (!workspace || workspace_bytes < need)
     return stp::fail(STP_ERR_WORKSPACE, "sparse_mla_decode: workspace of %zu bytes needed, %zu given",
                      need, workspace_bytes);
+  // split path: normalised bf16 partial outputs, merged with the
+  // partition-combine weights l_s e^(m_s - M) / L
   const size_t n = (size_t)T * S * H;
   char* ws = (char*)workspace;
-  float* o_part = (float*)ws;
-  float* m_part = (float*)(ws + align256(n * kDV * 4));
-  float* l_part = (float*)(ws + align256(n * kDV * 4) + align256(n * 4));
-  if (int rc = launch_decode(true, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S, o_part,
-                             m_part, l_part, nullptr, nullptr, stream))
+  uint16_t* o_norm = (uint16_t*)ws;
+  float* m_part = (float*)(ws + align256(n * kDV * 2));
+  float* l_part = (float*)(ws + align256(n * kDV * 2) + align256(n * 4));
+  if (int rc = launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S,
+                             (float*)o_norm, m_part, l_part, nullptr, nullptr, stream))
     return rc;
-  return stp::launch_merge(o_part, m_part, l_part, T, S, H, kDV, out, lse, stream);
+  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, kDV, out, lse, stream);
 }
 
 extern "C" int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* kv,
@@ -451,6 +540,6 @@ extern "C" int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* 
   if (T == 0) return STP_OK;
   if (!o_part || !m_part || !l_part)
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial: null output");
-  return launch_decode(true, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, num_splits,
+  return launch_decode(kOutPartialF32, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, num_splits,
                        o_part, m_part, l_part, nullptr, nullptr, stream);
 }

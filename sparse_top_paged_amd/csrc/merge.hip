@@ -65,9 +65,65 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(
   if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
 }
 
+// Same merge from normalised bf16 split outputs O_s = o_s / l_s: the weight of
+// split s is l_s e^(m_s - M) / L (the partition-combine form).
+__global__ __launch_bounds__(kThreads) void splitkv_merge_norm_kernel(
+    const uint16_t* __restrict__ o_norm, const float* __restrict__ m_part,
+    const float* __restrict__ l_part, int S, int H, int dv, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * 2 + (threadIdx.x / kPerHead);
+  if (h >= H) return;
+  const int c0 = (threadIdx.x % kPerHead) * 4;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    const int64_t k = ((int64_t)t * S + s) * H + h;
+    if (l_part[k] > 0.f) M = fmaxf(M, m_part[k]);
+  }
+  uint16_t* orow = out + ((int64_t)t * H + h) * dv;
+  if (M == -INFINITY) {
+    for (int c = c0; c < dv; c += 4 * kPerHead) *(uint2*)(orow + c) = make_uint2(0u, 0u);
+    if (lse && c0 == 0) lse[(int64_t)t * H + h] = -INFINITY;
+    return;
+  }
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const int64_t k = ((int64_t)t * S + s) * H + h;
+    const float l = l_part[k];
+    if (l > 0.f) L += expf(m_part[k] - M) * l;
+  }
+  const float invL = 1.f / L;
+  for (int c = c0; c < dv; c += 4 * kPerHead) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < S; ++s) {
+      const int64_t k = ((int64_t)t * S + s) * H + h;
+      const float l = l_part[k];
+      if (!(l > 0.f)) continue;
+      const float w = expf(m_part[k] - M) * l * invL;
+      const uint2 raw = *(const uint2*)(o_norm + k * dv + c);
+      acc.x += w * __uint_as_float(raw.x << 16);
+      acc.y += w * __uint_as_float(raw.x & 0xffff0000u);
+      acc.z += w * __uint_as_float(raw.y << 16);
+      acc.w += w * __uint_as_float(raw.y & 0xffff0000u);
+    }
+    const uint32_t lo = stp::f32_to_bf16_rne(acc.x) | ((uint32_t)stp::f32_to_bf16_rne(acc.y) << 16);
+    const uint32_t hi = stp::f32_to_bf16_rne(acc.z) | ((uint32_t)stp::f32_to_bf16_rne(acc.w) << 16);
+    *(uint2*)(orow + c) = make_uint2(lo, hi);
+  }
+  if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
+}
+
 }  // namespace
 
 namespace stp {
+
+int launch_merge_normalized(const uint16_t* o_norm, const float* m_part, const float* l_part, int T,
+                            int S, int H, int dv, uint16_t* out, float* lse, hipStream_t stream) {
+  dim3 grid(T, (H + 1) / 2);
+  splitkv_merge_norm_kernel<<<grid, kThreads, 0, stream>>>(o_norm, m_part, l_part, S, H, dv, out,
+                                                           lse);
+  return check_launch("splitkv_merge_norm_kernel");
+}
 
 int launch_merge(const float* o_part, const float* m_part, const float* l_part, int T, int S,
                  int H, int dv, uint16_t* out, float* lse, hipStream_t stream) {

@@ -52,8 +52,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Split-KV merge launcher shared by the decode entry point (merge.hip).
+// Split-KV merge launchers (merge.hip).  launch_merge takes un-normalised
+// fp32 numerators; launch_merge_normalized takes bf16 o_s / l_s, the form the
+// decode entry point's split path writes.
 int launch_merge(const float* o_part, const float* m_part, const float* l_part, int T, int S,
                  int H, int dv, uint16_t* out, float* lse, hipStream_t stream);
+int launch_merge_normalized(const uint16_t* o_norm, const float* m_part, const float* l_part, int T,
+                            int S, int H, int dv, uint16_t* out, float* lse, hipStream_t stream);
 
 }  // namespace stp
