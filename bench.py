@@ -8,8 +8,10 @@ context 32768, page size 64 over a shared 1,048,576-row pool (1.2 GB, in
 HBM), top-k 2048 uniform over the causal range + 128-token window + 4 sinks.
 
 A step is one pass of the hot path over one batch: candidate normalisation
-(with the block view) -> sparse MLA decode (split partial states) -> split
-merge.  Inputs are resident in HBM before timing starts.  Eight candidate
+(with the block view) -> sparse MLA decode (normalised bf16 split partial
+states) -> split merge, i.e. stp_normalize_indices followed by the two
+launches stp_sparse_mla_decode makes, called one by one so that the decode
+kernel can be timed alone.  Inputs are resident in HBM before timing starts.  Eight candidate
 sets (same pool, tables and queries, different top-k draws) rotate step by
 step, so a set's ~80 MB of rows is not still in the 256 MB Infinity Cache
 when it comes round again.
@@ -137,7 +139,9 @@ def main():
     S = stp.decode_splits(T, H, cap, args.splits)
     norm = [stp.normalize_indices(tk, req, qpos, table, c0.page_size, c0.window, c0.num_sinks,
                                   cap) for tk in topks]
-    o_part = torch.empty((T, S, H, 512), dtype=torch.float32, device=dev)
+    # the split path of stp_sparse_mla_decode, called stage by stage so that the
+    # decode kernel can be timed on its own: normalised bf16 partials + merge
+    o_norm = torch.empty((T, S, H, 512), dtype=torch.bfloat16, device=dev)
     m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
     l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
@@ -152,11 +156,11 @@ def main():
         if ev is not None:
             ev[0].record()
         if S > 1:
-            stp.sparse_mla_decode_partial(q, kv, nb["slot"], nb["count"], c0.scale, S,
-                                          o_part, m_part, l_part)
+            stp.sparse_mla_decode_partial_normalized(q, kv, nb["slot"], nb["count"], c0.scale, S,
+                                                     o_norm, m_part, l_part)
             if ev is not None:
                 ev[1].record()
-            stp.splitkv_merge(o_part, m_part, l_part, out, lse)
+            stp.splitkv_merge_normalized(o_norm, m_part, l_part, out, lse)
         else:
             stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
             if ev is not None:

@@ -228,6 +228,22 @@ int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* kv, int64_t
                                   float* o_part, float* m_part, float* l_part, hipStream_t stream);
 
 /*
+ * Split partial states in normalised form (the partition outputs of
+ * "PagedAttention 与 RadixAttention" §1.4, what stp_sparse_mla_decode's own
+ * split path writes): for split s of token t and head h,
+ *   o_norm[t, s, h, :] = (sum_j exp(z_j - m) kv[row_j, 0:512]) / l  (bf16, RNE)
+ *   m_part, l_part as in stp_sparse_mla_decode_partial; an empty split has
+ *   o_norm = 0, m = -inf, l = 0.
+ * Layouts: o_norm [T, S, H, 512] bf16, m_part / l_part [T, S, H] float.
+ */
+int stp_sparse_mla_decode_partial_normalized(const uint16_t* q, const uint16_t* kv,
+                                             int64_t kv_rows, const int32_t* row_ids,
+                                             const int32_t* counts, int32_t cap, int32_t T,
+                                             int32_t H, float scale, int32_t num_splits,
+                                             uint16_t* o_norm, float* m_part, float* l_part,
+                                             hipStream_t stream);
+
+/*
  * ---- Stage 4: split-KV merge -------------------------------------------------
  * "5.1.1 · 从索引到 Kernel" §3.2 eq. (7) for any number of splits, §7.1 (an
  * empty split, l_s = 0, takes no part); "PagedAttention 与 RadixAttention"
@@ -240,6 +256,17 @@ int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* kv, int64_t
 int stp_splitkv_merge(const float* o_part, const float* m_part, const float* l_part, int32_t T,
                       int32_t S, int32_t H, int32_t dv, uint16_t* out, float* lse,
                       hipStream_t stream);
+
+/*
+ * The same merge from normalised bf16 split outputs O_s = o_s / l_s: with
+ * M = max over live splits of m_s and w_s = l_s e^(m_s - M) / sum_s' (...),
+ *   out = sum_s w_s O_s (bf16, RNE), lse = M + log(sum_s l_s e^(m_s - M))
+ * ("PagedAttention 与 RadixAttention" §1.4 part 3, the combine derivation).
+ * Layouts: o_norm [T, S, H, dv] bf16, m_part / l_part [T, S, H] float.
+ */
+int stp_splitkv_merge_normalized(const uint16_t* o_norm, const float* m_part,
+                                 const float* l_part, int32_t T, int32_t S, int32_t H, int32_t dv,
+                                 uint16_t* out, float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

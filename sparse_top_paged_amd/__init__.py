@@ -15,7 +15,8 @@ D_V = 512
 
 __all__ = [
     "StpError", "version", "normalize_indices", "hot_lookup_swapin", "hot_reset", "backup_rows",
-    "sparse_mla_decode", "sparse_mla_decode_partial", "splitkv_merge", "decode_splits",
+    "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
+    "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer",
 ]
 
@@ -234,6 +235,42 @@ def splitkv_merge(o_part, m_part, l_part, out=None, lse=None):
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     check(lib.stp_splitkv_merge(
         _dev(o_part, "o_part", torch.float32, dev), _dev(m_part, "m_part", torch.float32, dev),
+        _dev(l_part, "l_part", torch.float32, dev), T, S, H, dv,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse
+
+
+def sparse_mla_decode_partial_normalized(q, kv, row_ids, counts=None, scale=D_QK ** -0.5,
+                                         num_splits=1, o_norm=None, m_part=None, l_part=None):
+    """Split partial states in normalised form: o_norm [T, S, H, 512] bf16
+    (o / l), m, l [T, S, H] float32 -- the split path of sparse_mla_decode."""
+    dev, T, H, cap = _decode_common(q, kv, row_ids, counts)
+    S = num_splits
+    if o_norm is None:
+        o_norm = torch.empty((T, S, H, D_V), dtype=torch.bfloat16, device=dev)
+    if m_part is None:
+        m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    if l_part is None:
+        l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+    check(lib.stp_sparse_mla_decode_partial_normalized(
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0],
+        _dev(row_ids, "row_ids", torch.int32, dev), _opt(counts, "counts", torch.int32, dev), cap,
+        T, H, float(scale), S, _dev(o_norm, "o_norm", torch.bfloat16, dev),
+        _dev(m_part, "m_part", torch.float32, dev), _dev(l_part, "l_part", torch.float32, dev),
+        _stream(dev)))
+    return o_norm, m_part, l_part
+
+
+def splitkv_merge_normalized(o_norm, m_part, l_part, out=None, lse=None):
+    """Stage 4 from normalised bf16 split outputs o_norm [T, S, H, dv]."""
+    dev = o_norm.device
+    T, S, H, dv = o_norm.shape
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    check(lib.stp_splitkv_merge_normalized(
+        _dev(o_norm, "o_norm", torch.bfloat16, dev), _dev(m_part, "m_part", torch.float32, dev),
         _dev(l_part, "l_part", torch.float32, dev), T, S, H, dv,
         _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
     return out, lse

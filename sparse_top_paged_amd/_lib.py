@@ -38,7 +38,10 @@ SIGNATURES = {
     "stp_sparse_mla_decode_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "stp_sparse_mla_decode_partial": (ctypes.c_int, [
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
+    "stp_sparse_mla_decode_partial_normalized": (ctypes.c_int, [
+        _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "stp_splitkv_merge": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "stp_splitkv_merge_normalized": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
 }
 
 

@@ -6,8 +6,8 @@
 // un-normalised numerator; empty tiles skipped), §3.2 (masks act before the
 // exponent; split partial states, eq. (7)); "PagedAttention 与 RadixAttention：
 // 上游机制与海光实现对照" §1.4 (exp2 with log2 e folded into the scale; split
-// partitions), §1.4 part 4 and §5.2 (load each K/V row once for every query
-// head that shares it).
+// partitions; the normalised partition combine), §1.4 part 4 and §5.2 (load
+// each K/V row once for every query head that shares it).
 //
 // Data: q [T, H, 576] bf16, kv [rows, 576] bf16 (latent 512 first, rope 64
 // last; V is the first 512 values of the same row), row_ids [T, cap].
@@ -16,24 +16,29 @@
 // a workgroup owns 64 heads of one token and one contiguous range of its
 // candidate positions (a split); the two head groups of a (token, split) run
 // on the same XCD (blockIdx % 8 picks the XCD) so the second reads the rows
-// from that XCD's L2.  Four wave64s per workgroup, one per SIMD:
-//   wave w: head half hq = w & 1 (32 heads), dimension half dh = w >> 1.
-//   Logits, transposed:  S^T[32 rows x 32 heads] = K[rows x 576] Q^T, each
-//     wave contracting its 288 of the 576 dims with v_mfma_f32_32x32x16_bf16
-//     (A = K fragment from LDS, B = Q^T fragment kept in 72 VGPRs), the two
-//     halves exchanged through LDS and added (a + b == b + a, so both waves
-//     hold bit-identical logits).  In this layout a lane owns one head.
-//   Online softmax per lane (head) in base 2; the running reference max only
-//     moves when a tile's max exceeds it by 2^8, so most tiles skip the
-//     128-register rescale.
-//   Output, transposed: O^T[256 dims x 32 heads] += V^T P^T over the tile,
-//     A = V^T fragments read with ds_read_b64_tr_b16 (the LDS transpose
-//     read), B = P^T taken straight from the logit registers: the k-slot to
-//     row mapping of the V reads is chosen to match the accumulator layout,
-//     so P never moves between lanes.
+// from that XCD's L2.  Four wave64s per workgroup, one per SIMD, in two roles:
+//   score waves (0, 1): wave j owns heads 32 j .. 32 j + 31 of the group and
+//     keeps their Q^T for all 576 dims in 144 VGPRs.  Per 32-row tile it
+//     forms S^T[32 rows x 32 heads] = K Q^T with 36 v_mfma_f32_32x32x16_bf16
+//     (A = K fragment read from LDS), runs the online softmax of its heads
+//     (a lane owns one head; base 2; the reference max moves only when a
+//     tile beats it by 2^8) and publishes P^T (bf16) and the per-head rescale
+//     factor of the tile in LDS.
+//   output waves (2, 3): wave j owns values 256 j .. 256 j + 255 of all 64
+//     heads, O^T[256 x 64] in 256 AGPRs.  One tile behind the score waves it
+//     rescales O^T when a factor is not 1 and adds V^T P^T with 32 MFMAs
+//     (A = V^T fragments read with ds_read_b64_tr_b16, the LDS transpose
+//     read; B = the published P^T, one ds_read_b128 per fragment).
+//   The V^T k-slot to row mapping matches the score waves' accumulator
+//   layout, so lane l of a score wave writes exactly the P^T fragment that
+//   lane l of an output wave reads.  The QK and PV products (576 and 512 MACs
+//   per row and head) keep the four SIMDs equally busy, and the softmax of
+//   one tile overlaps the PV products of the previous one.
 // Rows are staged in a 3-deep LDS ring of 32-row tiles (36.5 KiB each) with
-// global_load_lds_dwordx4, so no VGPRs hold KV data in flight.  Invalid
-// candidates load a zero row and are masked to -inf before the exponent.
+// global_load_lds_dwordx4, so no VGPRs hold KV data in flight; one workgroup
+// barrier per tile hands over P^T, publishes the next tile and frees a ring
+// stage.  Invalid candidates load a zero row and are masked to -inf before
+// the exponent.
 
 #include "stp_internal.h"
 
@@ -52,35 +57,38 @@ constexpr int kStages = 3;
 constexpr int kSlotsPerThread = kTileRows * kChunks / kThreads; // 9
 constexpr int kHeadsPerWG = 64;
 constexpr int kIdsMax = 4096;
-constexpr int kLdsXchg = kStages * kTileBytes;                  // 110592
-constexpr int kXchgBytes = 4 * 64 * 16 * 4;                     // 16 KiB
-constexpr int kLdsIds = kLdsXchg + kXchgBytes;                  // 126976
-constexpr int kLdsBytes = kLdsIds + kIdsMax * 4;                // 143360
-constexpr int kKSteps = kDQK / 2 / 16;                          // 18 per wave
+constexpr int kQKSteps = kDQK / 16;                             // 36
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
 
 static_assert(kTileRows * kChunks % kThreads == 0, "tile slots per thread");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) shortx8 lds_shortx8;
 
 // Source of every masked-out row: loads stay in bounds and bring zeros.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytes] = {};
 
-// LDS tile layout: four groups of 8 rows (one group per wave when loading);
-// inside a group the 16-byte chunks are chunk-major, so chunk c of group row
-// rl sits at group + (c * 8 + rl) * 16.  One load instruction of a wave then
-// fills 8 consecutive chunks of its 8 rows (1 KiB of LDS, 8 x 128 B of HBM),
-// every lane keeps one row for the whole tile, and every LDS read address
-// below is a per-lane base plus a compile-time offset.  Groups are padded by
-// 128 B so that rows r and r + 8 fall in different halves of the 64 banks.
+// LDS tile layout: four groups of 8 rows (one group per wave when loading),
+// each group nine 1 KiB blocks; block b holds chunks 8 b .. 8 b + 7 (one
+// 128-byte line) of each of the 8 rows, row-major, with the chunk position
+// XOR-swizzled by the row: chunk c of group row rl sits at
+//   group + (c / 8) * 1024 + rl * 128 + ((c % 8) ^ rl) * 16.
+// One load instruction of a wave fills one block: each run of 8 consecutive
+// lanes reads one row's 128-byte line (the access pattern the vector memory
+// path coalesces best), and every LDS read below is a per-lane base plus a
+// compile-time offset.  The swizzle keeps both the K reads (ds_read_b128) and
+// the V transpose reads free of bank conflicts; groups are padded by 128 B so
+// that rows r and r + 8 fall in different halves of the 64 banks.
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kv;
@@ -90,11 +98,18 @@ struct DecodeArgs {
   int cap, T, H;
   float scale_log2;
   int S, G, ntasks;
-  float* o_part;   // split mode: [T, S, H, 512], m/l in natural-log units
-  float* m_part;
+  void* o_part;    // split modes: [T, S, H, 512] fp32 or bf16
+  float* m_part;   // [T, S, H], natural-log units
   float* l_part;
-  uint16_t* out;   // direct mode: [T, H, 512] bf16
+  uint16_t* out;   // final mode: [T, H, 512] bf16
   float* lse;
+};
+
+// Output modes of the decode kernel.
+enum OutMode : int {
+  kOutFinal = 0,       // out = o / l (bf16), lse
+  kOutPartialF32 = 1,  // per split: o (unnormalised, fp32), m, l
+  kOutPartialBf16 = 2  // per split: o / l (bf16), m, l
 };
 
 template <int N>
@@ -103,11 +118,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
-// every outstanding global load (vmcnt(0)), which would drain the tile ring
-// at each barrier; the tile loads are waited for explicitly instead.
-// The signal fences only stop the compiler from moving memory accesses across
-// the barrier; the hardware wait is lgkmcnt(0) (LDS) alone.
+// Workgroup barrier that orders LDS only (__syncthreads() would also wait
+// for every tile load in flight).  The signal fences stop the compiler from
+// moving memory accesses across it; the hardware wait is lgkmcnt(0) alone.
 __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
@@ -117,13 +130,41 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc *= f for an MFMA accumulator kept in AGPRs.  Written as inline asm on
+// AGPR operands so that the compiler keeps the accumulators in AGPRs (a plain
+// VALU multiply makes it move all 256 of them through VGPRs).
+__device__ __forceinline__ void scale_acc(floatx16& acc, float f) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(acc[r]), "=&v"(t)
+        : "v"(f));
+  }
+}
+
+// max / sum of x over the lane pair (l, l ^ 32), identical in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): global address vaddr + offset, LDS address
 // m0 + offset + 16 * lane -- the immediate offset applies to both sides.
-// Issued from inline asm so that the compiler's
-// wait-count pass does not track these loads: the tile ring waits for them
-// explicitly (wait_vmcnt), and the compiler would otherwise drain the ring
-// before every LDS access it cannot prove disjoint from the loads in flight.
+// Issued from inline asm so that the compiler's wait-count pass does not
+// track these loads: the tile ring waits for them explicitly (wait_vmcnt),
+// and the compiler would otherwise drain the ring before every LDS access it
+// cannot prove disjoint from the loads in flight.
 template <int kOffset>
 __device__ __forceinline__ void load_lds_16(const void* gptr, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:%1" ::"v"(gptr), "n"(kOffset),
@@ -139,30 +180,103 @@ __device__ __forceinline__ void load_row_chunks(const uint8_t* src, uint32_t lds
   }
 }
 
-// Output modes of the decode kernel.
-enum OutMode : int {
-  kOutFinal = 0,       // out = o / l (bf16), lse
-  kOutPartialF32 = 1,  // per split: o (unnormalised, fp32), m (natural log), l
-  kOutPartialBf16 = 2  // per split: o / l (bf16), m (natural log), l -- the internal split path
+// LDS objects of one workgroup.  Separate variables let the compiler see
+// that the hand-off buffers and the id list never alias the tile ring.
+struct DecodeLds {
+  lds_t* tiles;        // [3][37376]
+  lds_t* pbuf;         // [2 buffers][2 head blocks][2 k-steps][64 lanes][16 B]
+  float* alpha;        // [2 buffers][64 heads]
+  float* stat;         // [3][64]: m_ref, m_true (log2 units), l
+  int32_t* ids;        // [kIdsMax]
 };
+
+// Score-wave view of one tile: S^T = K Q^T (2 accumulator chains), mask,
+// online softmax, publish P^T and the rescale factor.
+struct ScoreState {
+  float m_ref, m_true, lsum;
+};
+
+__device__ __forceinline__ void score_tile(const DecodeLds& L, const lds_t* stage,
+                                           const int (&k_base)[4],
+                                           const bf16x8 (&qf)[kQKSteps], uint32_t vmask,
+                                           float scale_log2, int buf, int j, int lane,
+                                           ScoreState& st) {
+  // K fragments stream through an 8-deep register ring: each slot is re-read
+  // for k-step ks + 8 right after the MFMA of k-step ks has consumed it.
+  constexpr int kRing = 8;
+  floatx16 acc0 = floatx16{}, acc1 = floatx16{};
+  shortx8 kf[kRing];
+  auto kaddr = [&](int ks) { return stage + k_base[ks & 3] + 1024 * (ks >> 2); };
+#pragma unroll
+  for (int ks = 0; ks < kRing; ++ks) kf[ks] = *(const lds_shortx8*)kaddr(ks);
+#pragma unroll
+  for (int ks = 0; ks < kQKSteps; ++ks) {
+    const bf16x8 kfrag = __builtin_bit_cast(bf16x8, kf[ks % kRing]);
+    if (ks & 1)
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc1, 0, 0, 0);
+    else
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc0, 0, 0, 0);
+    if (ks + kRing < kQKSteps) kf[ks % kRing] = *(const lds_shortx8*)kaddr(ks + kRing);
+  }
+  // keep kRing reads in flight: 8 reads, then MFMA / read pairs, then 8 MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+  for (int g = 0; g < kQKSteps - kRing; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const floatx16 acc = acc0 + acc1;
+
+  // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of head lane % 32
+  float sv[16];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    sv[r] = ((vmask >> rr) & 1u) ? acc[r] * scale_log2 : -INFINITY;
+    mt = fmaxf(mt, sv[r]);
+  }
+  mt = pair_max(mt);
+  st.m_true = fmaxf(st.m_true, mt);
+  float alpha = 1.f;
+  if (mt > st.m_ref + kRescaleLog2) {  // also the first non-empty tile (m_ref = -inf)
+    alpha = fast_exp2(st.m_ref - mt);
+    st.m_ref = mt;
+    st.lsum *= alpha;
+  }
+  bf16x8 pk[2];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float p = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - st.m_ref);
+    psum += p;
+    pk[r >> 3][r & 7] = (__bf16)p;
+  }
+  st.lsum += psum;
+  // P^T fragments for k-steps 0 and 1 (rows 0-15 and 16-31 of the tile)
+  lds_t* pb = L.pbuf + ((buf * 2 + j) * 2) * 1024 + lane * 16;
+  *(__attribute__((address_space(3))) bf16x8*)(pb) = pk[0];
+  *(__attribute__((address_space(3))) bf16x8*)(pb + 1024) = pk[1];
+  if (lane < 32) L.alpha[buf * 64 + 32 * j + lane] = alpha;
+}
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
-  // Three separate LDS objects: the compiler can then tell that the exchange
-  // buffer and the id list never alias the tile ring.
   __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_xchg[kXchgBytes / 4];
+  __shared__ __attribute__((aligned(16))) char s_pbuf[2 * 2 * 2 * 1024];
+  __shared__ __attribute__((aligned(16))) float s_alpha[2 * 64];
+  __shared__ __attribute__((aligned(16))) float s_stat[3 * 64];
   __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
-  lds_t* lds = (lds_t*)s_tiles;
-  int32_t* ids = s_ids;
-  float* xchg = s_xchg;
+  const DecodeLds L{(lds_t*)s_tiles, (lds_t*)s_pbuf, s_alpha, s_stat, s_ids};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hq = wave & 1;
-  const int dh = wave >> 1;
+  const bool score = wave < 2;
+  const int j = wave & 1;
 
   // XCD-aware task map: the G head groups of one (token, split) get block
   // ids that agree mod 8 and are adjacent in dispatch order.
@@ -183,235 +297,258 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
 
   // candidate ids of this split, -1 for invalid ones and up to the tile edge
   const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
-  for (int j = tid; j < ntiles * kTileRows; j += kThreads) {
-    const int32_t id = j < len ? src_ids[j] : -1;
-    ids[j] = (id >= 0 && id < a.kv_rows) ? id : -1;
+  for (int i = tid; i < ntiles * kTileRows; i += kThreads) {
+    const int32_t id = i < len ? src_ids[i] : -1;
+    L.ids[i] = (id >= 0 && id < a.kv_rows) ? id : -1;
   }
   __syncthreads();  // ids visible
 
   // Enqueue the 32 rows of tile i into ring stage st: lane keeps row
-  // 8 * wave + lane % 8 and chunks 8 * it + lane / 8, it = 0..8.
-  const int ld_row = wave * kGroupRows + (lane & 7);
-  const int ld_col = (lane >> 3) * 16;
+  // 8 * wave + lane / 8 and, in block it = 0..8, chunk 8 it + ((lane % 8) ^ (lane / 8)).
+  const int ld_row = wave * kGroupRows + (lane >> 3);
+  const int ld_col = ((lane & 7) ^ (lane >> 3)) * 16;
   auto issue = [&](int i, int st) {
-    const int id = ids[i * kTileRows + ld_row];
+    const int id = L.ids[i * kTileRows + ld_row];
     const uint8_t* src =
         (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds + st * kTileBytes + wave * kGroupBytes));
+        (uint32_t)(uintptr_t)(L.tiles + st * kTileBytes + wave * kGroupBytes));
     load_row_chunks<0>(src, dst);
   };
-  // The first two tiles are in flight while Q is fetched.
+  auto tile_mask = [&](int i) {
+    return (uint32_t)__ballot(L.ids[i * kTileRows + (lane & 31)] >= 0);
+  };
   if (ntiles > 0) issue(0, 0);
   if (ntiles > 1) issue(1, 1);
 
-  // Q^T fragments: lane holds Q[head][288 dh + 16 ks + 8 (lane / 32) + 0..7].
-  const int head = hg * kHeadsPerWG + hq * 32 + (lane & 31);
-  const bool head_ok = head < a.H;
-  bf16x8 qf[kKSteps];
-  {
-    const uint16_t* qrow =
-        a.q + ((int64_t)t * a.H + (head_ok ? head : 0)) * kDQK + 288 * dh + 8 * (lane >> 5);
+  // Pipeline, with P(i) the published P^T of tile i in pbuf[i % 2]:
+  //   prologue: tiles 0, 1 land; tile 2 issued; score waves publish P(0),
+  //   output waves read V(0); tile 1 lands; barrier.
+  //   iteration i: enqueue tile i+3 into stage i % 3 (free: tile i was read
+  //   during iteration i-1); score waves publish P(i+1) from stage
+  //   (i+1) % 3; output waves apply P(i) to V(i) (in registers) and read
+  //   V(i+1); tile i+2 lands; barrier.
+  if (score) {
+    const int head = hg * kHeadsPerWG + 32 * j + (lane & 31);
+    bf16x8 qf[kQKSteps];
+    {
+      const uint16_t* qrow =
+          a.q + ((int64_t)t * a.H + (head < a.H ? head : 0)) * kDQK + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      shortx8 v = *(const shortx8*)(qrow + 16 * ks);
-      if (!head_ok) v = shortx8{0, 0, 0, 0, 0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      for (int ks = 0; ks < kQKSteps; ++ks) {
+        shortx8 v = *(const shortx8*)(qrow + 16 * ks);
+        if (head >= a.H) v = shortx8{0, 0, 0, 0, 0, 0, 0, 0};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
     }
+    //  K fragment of k-step ks: row lane % 32, chunk 2 ks + lane / 32; chunk
+    //  c = 2 (ks % 4) + lane / 32 + 8 (ks / 4), so four per-lane bases cover
+    //  every k-step with an immediate offset of 1024 (ks / 4).
+    const int kr = lane & 31;
+    int k_base[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      k_base[q4] = (kr >> 3) * kGroupBytes + (kr & 7) * 128 +
+                   (((2 * q4 + (lane >> 5)) ^ (kr & 7)) << 4);
+    ScoreState st{-INFINITY, -INFINITY, 0.f};
+    wait_vmcnt<0>();
+    lds_barrier();  // tiles 0, 1 visible
+    if (ntiles > 2) issue(2, 2);
+    if (ntiles > 0) score_tile(L, L.tiles, k_base, qf, tile_mask(0), a.scale_log2, 0, j, lane, st);
+    if (ntiles > 2)
+      wait_vmcnt<kSlotsPerThread>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // P(0) published
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 3 < ntiles) issue(i + 3, i % kStages);
+      if (i + 1 < ntiles)
+        score_tile(L, L.tiles + ((i + 1) % kStages) * kTileBytes, k_base, qf, tile_mask(i + 1),
+                   a.scale_log2, (i + 1) & 1, j, lane, st);
+      if (i + 3 < ntiles)
+        wait_vmcnt<kSlotsPerThread>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+    }
+    const float l_tot = pair_sum(st.lsum);
+    if (lane < 32) {
+      L.stat[0 * 64 + 32 * j + lane] = st.m_ref;
+      L.stat[1 * 64 + 32 * j + lane] = st.m_true;
+      L.stat[2 * 64 + 32 * j + lane] = l_tot;
+    }
+    lds_barrier();  // statistics published
+    if (kMode != kOutPartialF32) lds_barrier();  // output rows staged by the output waves
+    return;
   }
 
-  // Per-lane LDS read bases (see the layout note above).
-  //  K fragment of k-step ks: row lane % 32, chunk 36 dh + 2 ks + lane / 32.
-  const int kr = lane & 31;
-  const int k_base = (kr >> 3) * kGroupBytes + (kr & 7) * 16 + (36 * dh + (lane >> 5)) * 128;
-  //  V^T fragment (transpose read): rows 16 kap + 4 (g / 2) + j / 4 (+ 8),
-  //  values 256 dh + 32 mb + 16 (g % 2) + 4 (j % 4) .. + 3, g = lane / 16, j = lane % 16.
+  // ---- output waves ----
+  //  V^T fragment (transpose read): rows 16 kap + 4 (g / 2) + j16 / 4 (+ 8),
+  //  values 256 j + 32 mb + 16 (g % 2) + 4 (j16 % 4) .. + 3, g = lane / 16.
+  //  Chunk cc = 32 j + 4 mb + cc0 with cc0 = 2 (g % 2) + (j16 % 4) / 2 < 4, so
+  //  two per-lane bases (mb parity) plus immediates cover every read.
   const int vg = lane >> 4, vj = lane & 15;
-  const int v_base = (4 * (vg >> 1) + (vj >> 2)) * 16 +
-                     (32 * dh + 2 * (vg & 1) + ((vj & 3) >> 1)) * 128 + 8 * (vj & 1);
-
-  floatx16 o[8];
+  const int v_rl = 4 * (vg >> 1) + (vj >> 2);
+  const int v_cc0 = 2 * (vg & 1) + ((vj & 3) >> 1);
+  int v_base[2];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) o[mb] = floatx16{};
-  float m_ref = -INFINITY, m_true = -INFINITY, lsum = 0.f;
-
-  // Pipeline (one barrier per tile).  At the top of iteration i the K
-  // fragments of tile i are in registers and tiles i+1, i+2 are in the ring
-  // or in flight.  Iteration i: QK MFMAs of tile i under the V transpose
-  // reads of tile i; publish the logit half; wait for tile i+1 and barrier
-  // (which also frees ring stage i % 3); enqueue tile i+3 there; softmax;
-  // PV MFMAs of tile i under the K reads of tile i+1.
-  shortx8 kf[kKSteps];
-  wait_vmcnt<0>();  // tiles 0 and 1 (and Q)
-  lds_barrier();
-  if (ntiles > 2) issue(2, 2);
-  if (ntiles > 0) {
-    const lds_t* kp = lds + k_base;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      kf[ks] = *(const __attribute__((address_space(3))) shortx8*)(kp + 256 * ks);
-  }
-
-  for (int i = 0; i < ntiles; ++i) {
-    const int st = i % kStages;
-    const lds_t* stage = lds + st * kTileBytes;
-    const bool row_valid = ids[i * kTileRows + (lane & 31)] >= 0;
-    const uint32_t vmask = (uint32_t)__ballot(row_valid);
-
-    // S^T partial = K_tile[:, 288 dh .. +288] Q^T, with the tile's V^T
-    // fragments read meanwhile.
-    // two independent accumulator chains (dependent MFMAs issue ~1.5x slower)
-    floatx16 acc = floatx16{}, acc2 = floatx16{};
-    shortx4 v0[2][8], v1[2][8];
-    const lds_t* vp = stage + v_base;
+  for (int par = 0; par < 2; ++par)
+    v_base[par] = 4 * j * 1024 + v_rl * 128 + (((v_cc0 + 4 * par) ^ v_rl) << 4) + 8 * (vj & 1);
+  auto vaddr = [&](const lds_t* stage, int kap, int half, int mb) {
+    return (lds_shortx4*)(stage + v_base[mb & 1] + (2 * kap + half) * kGroupBytes +
+                          1024 * (mb >> 1));
+  };
+  auto read_v = [&](const lds_t* stage, shortx4 (&v0)[2][8], shortx4 (&v1)[2][8]) {
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_shortx4*)(vp + 2 * kap * kGroupBytes + 512 * mb));
-        v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_shortx4*)(vp + (2 * kap + 1) * kGroupBytes + 512 * mb));
+        v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(stage, kap, 0, mb));
+        v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(stage, kap, 1, mb));
       }
+  };
+  floatx16 o[2][8];  // O^T[256 j + 32 mb + m][32 hb + head]
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ks += 2) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), qf[ks], acc,
-                                                    0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks + 1]),
-                                                     qf[ks + 1], acc2, 0, 0, 0);
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) o[hb][mb] = floatx16{};
+  shortx4 v0[2][8], v1[2][8];
+  wait_vmcnt<0>();
+  lds_barrier();  // tiles 0, 1 visible
+  if (ntiles > 2) issue(2, 2);
+  if (ntiles > 0) read_v(L.tiles, v0, v1);
+  if (ntiles > 2)
+    wait_vmcnt<kSlotsPerThread>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();  // P(0) published
+  for (int i = 0; i < ntiles; ++i) {
+    if (i + 3 < ntiles) issue(i + 3, i % kStages);
+    const int buf = i & 1;
+    const float a0 = L.alpha[buf * 64 + (lane & 31)];
+    const float a1 = L.alpha[buf * 64 + 32 + (lane & 31)];
+    if (__ballot(a0 != 1.f || a1 != 1.f)) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        scale_acc(o[0][mb], a0);
+        scale_acc(o[1][mb], a1);
+      }
     }
-    // interleave: one MFMA, then two transpose reads
+    bf16x8 pf[2][2];
 #pragma unroll
-    for (int g = 0; g < kKSteps; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    acc += acc2;
-
-    // publish this wave's half of the logits
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *(float4*)(xchg + ((wave * 4 + j) * 64 + lane) * 4) =
-          make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
-    // tile i+1 must have landed (tile i+2 may still be in flight)
-    if (i + 2 < ntiles)
-      wait_vmcnt<kSlotsPerThread>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();  // halves visible; tile i+1 visible; stage i % 3 read by every wave
-    if (i + 3 < ntiles) issue(i + 3, st);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 p = *(const float4*)(xchg + (((wave ^ 2) * 4 + j) * 64 + lane) * 4);
-      acc[4 * j] += p.x;
-      acc[4 * j + 1] += p.y;
-      acc[4 * j + 2] += p.z;
-      acc[4 * j + 3] += p.w;
-    }
-
-    // mask, then the online softmax of this lane's head (base 2).  A tile
-    // with no valid row leaves the state untouched (p = 0, no rescale).
-    float sv[16];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      sv[r] = ((vmask >> rr) & 1u) ? acc[r] * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sv[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    m_true = fmaxf(m_true, mt);
-    const bool need = mt > m_ref + kRescaleLog2;
-    if (__ballot(need)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;
-      m_ref = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-    }
-    bf16x8 pk[2];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - m_ref);
-      psum += p;
-      pk[r >> 3][r & 7] = (__bf16)p;
-    }
-    lsum += psum;
-
-    // O^T[256 dh + 32 mb + m][head] += V^T P^T, with the next tile's K
-    // fragments read meanwhile.
+      for (int kap = 0; kap < 2; ++kap)
+        pf[hb][kap] = *(const __attribute__((address_space(3))) bf16x8*)(
+            L.pbuf + ((buf * 2 + hb) * 2 + kap) * 1024 + lane * 16);
+    // PV MFMAs of tile i; each V^T fragment register pair is refilled from
+    // tile i+1 right after its last use (on the last tile the reads hit a
+    // stale stage: in bounds and unused).
+    const lds_t* vn = L.tiles + ((i + 1) % kStages) * kTileBytes;
 #pragma unroll
     for (int kap = 0; kap < 2; ++kap)
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
         const shortx8 vv = {v0[kap][mb][0], v0[kap][mb][1], v0[kap][mb][2], v0[kap][mb][3],
                             v1[kap][mb][0], v1[kap][mb][1], v1[kap][mb][2], v1[kap][mb][3]};
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pk[kap],
-                                                        o[mb], 0, 0, 0);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          o[hb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                              pf[hb][kap], o[hb][mb], 0, 0, 0);
+        v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 0, mb));
+        v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 1, mb));
       }
-    {
-      // (on the last tile this reads a stale stage: in bounds and unused)
-      const lds_t* kp = lds + ((i + 1) % kStages) * kTileBytes + k_base;
+    if (i + 3 < ntiles)
+      wait_vmcnt<kSlotsPerThread>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+  }
+  lds_barrier();  // statistics published
+
+  // lane holds O^T[256 j + 32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][32 hb + lane % 32]
+  const int dv_lane = 256 * j + 4 * (lane >> 5);
+  if (kMode == kOutPartialF32) {
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
-        kf[ks] = *(const __attribute__((address_space(3))) shortx8*)(kp + 256 * ks);
-    }
+    for (int hb = 0; hb < 2; ++hb) {
+      const int hl = 32 * hb + (lane & 31);
+      const int head = hg * kHeadsPerWG + hl;
+      if (head >= a.H) continue;
+      const float m_ref = L.stat[hl], m_true = L.stat[64 + hl], l_tot = L.stat[128 + hl];
+      const bool live = m_true != -INFINITY;
+      const float f = live ? fast_exp2(m_ref - m_true) : 0.f;  // rebase to the true maximum
+      float* orow = (float*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(float4*)(orow + dv_lane + 32 * mb + 8 * rq) =
+              make_float4(o[hb][mb][4 * rq] * f, o[hb][mb][4 * rq + 1] * f,
+                          o[hb][mb][4 * rq + 2] * f, o[hb][mb][4 * rq + 3] * f);
+      if (j == 0 && lane < 32) {
+        const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
+        a.m_part[k] = live ? m_true * kLn2 : -INFINITY;
+        a.l_part[k] = l_tot * f;
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    return;
   }
 
-  const float l_tot = lsum + __shfl_xor(lsum, 32);
-  if (!head_ok) return;
-  // lane holds O^T[256 dh + 32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][head]
-  const int dv_lane = 256 * dh + 4 * (lane >> 5);
-  const bool live = m_true != -INFINITY;
-  if (kMode == kOutPartialF32) {
-    const float f = live ? fast_exp2(m_ref - m_true) : 0.f;  // rebase to the true maximum
-    float* orow = a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+  // bf16 o / l (the final output, or a normalised split partial), staged
+  // through the idle tile ring as [64 heads][512] rows (head stride 1040 B,
+  // so the 32 heads of a store hit different banks), then written back one
+  // whole 1 KiB head row per store instruction.
+  constexpr int kHeadStride = kDV * 2 + 16;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        *(float4*)(orow + dv_lane + 32 * mb + 8 * rq) =
-            make_float4(o[mb][4 * rq] * f, o[mb][4 * rq + 1] * f, o[mb][4 * rq + 2] * f,
-                        o[mb][4 * rq + 3] * f);
-    if (dh == 0 && lane < 32) {
-      const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
-      a.m_part[k] = live ? m_true * kLn2 : -INFINITY;
-      a.l_part[k] = l_tot * f;
-    }
-  } else {
-    // bf16 o / l: the final output, or a normalised split partial
+  for (int hb = 0; hb < 2; ++hb) {
+    const int hl = 32 * hb + (lane & 31);
+    const float l_tot = L.stat[128 + hl];
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = kMode == kOutFinal
-                         ? a.out + ((int64_t)t * a.H + head) * kDV
-                         : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+    lds_t* hrow = L.tiles + hl * kHeadStride + dv_lane * 2;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const uint32_t w0 = stp::f32_to_bf16_rne(o[mb][4 * rq] * inv) |
-                            ((uint32_t)stp::f32_to_bf16_rne(o[mb][4 * rq + 1] * inv) << 16);
-        const uint32_t w1 = stp::f32_to_bf16_rne(o[mb][4 * rq + 2] * inv) |
-                            ((uint32_t)stp::f32_to_bf16_rne(o[mb][4 * rq + 3] * inv) << 16);
-        *(uint2*)(orow + dv_lane + 32 * mb + 8 * rq) = make_uint2(w0, w1);
+        const uint32_t w0 = stp::f32_to_bf16_rne(o[hb][mb][4 * rq] * inv) |
+                            ((uint32_t)stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 1] * inv) << 16);
+        const uint32_t w1 = stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 2] * inv) |
+                            ((uint32_t)stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 3] * inv) << 16);
+        *(__attribute__((address_space(3))) uintx2*)(hrow + (32 * mb + 8 * rq) * 2) =
+            uintx2{w0, w1};
       }
-    if (dh == 0 && lane < 32) {
+  }
+  lds_barrier();  // output rows staged (the score waves take part before returning)
+  {
+    const int ot = tid - 128;  // 0..127: two output waves copy the 64 rows
+#pragma unroll 4
+    for (int it = 0; it < 64 * 64 / 128; ++it) {
+      const int idx = it * 128 + ot;          // 64 lanes per head row of 1 KiB
+      const int hl = idx >> 6, c = idx & 63;  // head, 16-byte chunk
+      const int head = hg * kHeadsPerWG + hl;
+      if (head >= a.H) continue;
+      const uintx4 v =
+          *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
+      uint16_t* orow = kMode == kOutFinal
+                           ? a.out + ((int64_t)t * a.H + head) * kDV
+                           : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+      *(uintx4*)(orow + c * 8) = v;
+    }
+  }
+  if (lane < 32) {
+    // lse / (m, l): output wave j covers heads 32 j .. 32 j + 31, one lane each
+    const int hl = 32 * j + (lane & 31);
+    const int head = hg * kHeadsPerWG + hl;
+    if (head < a.H) {
+      const float m_ref = L.stat[hl], m_true = L.stat[64 + hl], l_tot = L.stat[128 + hl];
+      const bool live = m_true != -INFINITY;
       if (kMode == kOutFinal) {
         if (a.lse)
           a.lse[(int64_t)t * a.H + head] = live ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       } else {
-        // normalised partial: l relative to m_ref, m reported as m_ref
+        // m = the split's max logit, l = sum of exp(z - m)
         const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
-        a.m_part[k] = live ? m_ref * kLn2 : -INFINITY;
-        a.l_part[k] = live ? l_tot : 0.f;
+        a.m_part[k] = live ? m_true * kLn2 : -INFINITY;
+        a.l_part[k] = live ? l_tot * fast_exp2(m_ref - m_true) : 0.f;
       }
     }
   }
@@ -542,4 +679,23 @@ extern "C" int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* 
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial: null output");
   return launch_decode(kOutPartialF32, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, num_splits,
                        o_part, m_part, l_part, nullptr, nullptr, stream);
+}
+
+extern "C" int stp_sparse_mla_decode_partial_normalized(
+    const uint16_t* q, const uint16_t* kv, int64_t kv_rows, const int32_t* row_ids,
+    const int32_t* counts, int32_t cap, int32_t T, int32_t H, float scale, int32_t num_splits,
+    uint16_t* o_norm, float* m_part, float* l_part, hipStream_t stream) {
+  if (int rc = check_common(q, kv, kv_rows, row_ids, cap, T, H, scale)) return rc;
+  if (num_splits < 1)
+    return stp::fail(STP_ERR_INVALID_ARG,
+                     "sparse_mla_decode_partial_normalized: num_splits must be >= 1");
+  if ((cap + num_splits - 1) / num_splits > kIdsMax)
+    return stp::fail(STP_ERR_INVALID_ARG,
+                     "sparse_mla_decode_partial_normalized: ceil(cap / num_splits) exceeds %d",
+                     kIdsMax);
+  if (T == 0) return STP_OK;
+  if (!o_norm || !m_part || !l_part)
+    return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial_normalized: null output");
+  return launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale,
+                       num_splits, (float*)o_norm, m_part, l_part, nullptr, nullptr, stream);
 }

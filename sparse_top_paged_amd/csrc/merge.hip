@@ -66,7 +66,60 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(
 }
 
 // Same merge from normalised bf16 split outputs O_s = o_s / l_s: the weight of
-// split s is l_s e^(m_s - M) / L (the partition-combine form).
+// split s is l_s e^(m_s - M) / L (the partition-combine form).  Up to
+// eight splits, every split's (m, l) and output slice are loaded before any
+// is used, so the loads of one thread overlap.
+
+template <int S>
+__device__ __forceinline__ void merge_norm_fixed(const uint16_t* __restrict__ o_norm,
+                                                 const float* __restrict__ m_part,
+                                                 const float* __restrict__ l_part, int t, int h,
+                                                 int H, int dv, int c0, uint16_t* __restrict__ orow,
+                                                 float* __restrict__ lse) {
+  float m[S], l[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t k = ((int64_t)t * S + s) * H + h;
+    m[s] = m_part[k];
+    l[s] = l_part[k];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (l[s] > 0.f) M = fmaxf(M, m[s]);
+  if (M == -INFINITY) {
+    for (int c = c0; c < dv; c += 4 * kPerHead) *(uint2*)(orow + c) = make_uint2(0u, 0u);
+    if (lse && c0 == 0) lse[(int64_t)t * H + h] = -INFINITY;
+    return;
+  }
+  float w[S], L = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    w[s] = l[s] > 0.f ? expf(m[s] - M) * l[s] : 0.f;
+    L += w[s];
+  }
+  const float invL = 1.f / L;
+  for (int c = c0; c < dv; c += 4 * kPerHead) {
+    uint2 raw[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      raw[s] = *(const uint2*)(o_norm + (((int64_t)t * S + s) * H + h) * dv + c);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float ws = w[s] * invL;
+      acc.x += ws * __uint_as_float(raw[s].x << 16);
+      acc.y += ws * __uint_as_float(raw[s].x & 0xffff0000u);
+      acc.z += ws * __uint_as_float(raw[s].y << 16);
+      acc.w += ws * __uint_as_float(raw[s].y & 0xffff0000u);
+    }
+    const uint32_t lo = stp::f32_to_bf16_rne(acc.x) | ((uint32_t)stp::f32_to_bf16_rne(acc.y) << 16);
+    const uint32_t hi = stp::f32_to_bf16_rne(acc.z) | ((uint32_t)stp::f32_to_bf16_rne(acc.w) << 16);
+    *(uint2*)(orow + c) = make_uint2(lo, hi);
+  }
+  if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
+}
+
 __global__ __launch_bounds__(kThreads) void splitkv_merge_norm_kernel(
     const uint16_t* __restrict__ o_norm, const float* __restrict__ m_part,
     const float* __restrict__ l_part, int S, int H, int dv, uint16_t* __restrict__ out,
@@ -75,12 +128,24 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_norm_kernel(
   const int h = blockIdx.y * 2 + (threadIdx.x / kPerHead);
   if (h >= H) return;
   const int c0 = (threadIdx.x % kPerHead) * 4;
+  uint16_t* orow = out + ((int64_t)t * H + h) * dv;
+  switch (S) {
+    case 1: return merge_norm_fixed<1>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 2: return merge_norm_fixed<2>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 3: return merge_norm_fixed<3>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 4: return merge_norm_fixed<4>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 5: return merge_norm_fixed<5>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 6: return merge_norm_fixed<6>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 7: return merge_norm_fixed<7>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    case 8: return merge_norm_fixed<8>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
+    default: break;
+  }
+  // any number of splits: two passes over (m, l), then the weighted sum
   float M = -INFINITY;
   for (int s = 0; s < S; ++s) {
     const int64_t k = ((int64_t)t * S + s) * H + h;
     if (l_part[k] > 0.f) M = fmaxf(M, m_part[k]);
   }
-  uint16_t* orow = out + ((int64_t)t * H + h) * dv;
   if (M == -INFINITY) {
     for (int c = c0; c < dv; c += 4 * kPerHead) *(uint2*)(orow + c) = make_uint2(0u, 0u);
     if (lse && c0 == 0) lse[(int64_t)t * H + h] = -INFINITY;
@@ -145,4 +210,19 @@ extern "C" int stp_splitkv_merge(const float* o_part, const float* m_part, const
   if (!o_part || !m_part || !l_part || !out)
     return fail(STP_ERR_INVALID_ARG, "splitkv_merge: null pointer");
   return stp::launch_merge(o_part, m_part, l_part, T, S, H, dv, out, lse, stream);
+}
+
+extern "C" int stp_splitkv_merge_normalized(const uint16_t* o_norm, const float* m_part,
+                                            const float* l_part, int32_t T, int32_t S, int32_t H,
+                                            int32_t dv, uint16_t* out, float* lse,
+                                            hipStream_t stream) {
+  using stp::fail;
+  if (T < 0 || S < 1 || H < 1 || dv < 1 || dv % 4 != 0)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge_normalized: bad sizes T=%d S=%d H=%d dv=%d", T,
+                S, H, dv);
+  if (H > 2 * 65535) return fail(STP_ERR_INVALID_ARG, "splitkv_merge_normalized: H %d too large", H);
+  if (T == 0) return STP_OK;
+  if (!o_norm || !m_part || !l_part || !out)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge_normalized: null pointer");
+  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, dv, out, lse, stream);
 }

@@ -143,6 +143,56 @@ def test_partial_states(splits):
     assert_attention_close(out, lse, o_ref, l_ref, f"partial+merge splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_partial_states_normalized(splits):
+    """The split path of sparse_mla_decode: bf16 o / l per split, then the
+    partition-combine merge."""
+    import sparse_top_paged_amd as stp
+    c, kv_bits, ref = _tiny()
+    o, m, l = stp.sparse_mla_decode_partial_normalized(bf16_dev(c.q_bits), bf16_dev(kv_bits),
+                                                       to_dev(ref["slot"]), to_dev(ref["count"]),
+                                                       c.scale, splits)
+    torch.cuda.synchronize()
+    o_r, m_r, l_r = oracle.attend_partial(c.q_bits, kv_bits, ref["slot"], ref["count"], c.scale,
+                                          splits)
+    on = o.float().cpu().numpy().astype(np.float64)
+    m, l = (x.cpu().numpy().astype(np.float64) for x in (m, l))
+    live = l_r > 0
+    assert np.array_equal(l > 0, live)
+    assert np.all(np.isneginf(m[~live])) and np.all(on[~live] == 0)
+    assert np.max(np.abs(m[live] - m_r[live])) < 1e-4
+    assert np.max(np.abs(np.log(l[live]) - np.log(l_r[live]))) < 1e-2
+    norm_r = o_r[live] / l_r[live][:, None]
+    assert np.max(np.abs(on[live] - norm_r)) < 2e-2
+    out, lse = stp.splitkv_merge_normalized(
+        o, *(torch.from_numpy(x.astype(np.float32)).to(dev()) for x in (m, l)))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attend_sparse(c.q_bits, kv_bits, ref["slot"], ref["count"], c.scale)
+    assert_attention_close(out, lse, o_ref, l_ref, f"normalized partial+merge splits={splits}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 8, 33])
+def test_merge_normalized_against_oracle(S):
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(100 + S)
+    T, H, dv = 3, 20, 512
+    m = (rng.standard_normal((T, S, H)) * 4).astype(np.float32)
+    l = rng.uniform(0.5, 30, size=(T, S, H)).astype(np.float32)
+    on_bits = workloads.normal_bf16(rng, (T, S, H, dv))
+    l[0, 0, :] = 0.0
+    m[0, 0, :] = 1e30
+    on_bits[0, 0] = 0
+    l[2, :, 3] = 0.0
+    on_bits[2, :, 3] = 0
+    out, lse = stp.splitkv_merge_normalized(bf16_dev(on_bits),
+                                            *(torch.from_numpy(x).to(dev()) for x in (m, l)))
+    torch.cuda.synchronize()
+    on = oracle.bf16_bits_to_f64(on_bits)
+    o_ref, l_ref = oracle.merge_normalized(on, m.astype(np.float64), l.astype(np.float64))
+    assert_attention_close(out, lse, o_ref, l_ref, f"merge normalized S={S}")
+    assert torch.all(out[2, 3] == 0) and torch.isneginf(lse[2, 3])
+
+
 @pytest.mark.parametrize("S", [1, 2, 8, 33])
 def test_merge_against_oracle(S):
     import sparse_top_paged_amd as stp
