@@ -303,23 +303,30 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // ids visible
 
-  // Enqueue the 32 rows of tile i into ring stage st: lane keeps row
-  // 8 * wave + lane / 8 and, in block it = 0..8, chunk 8 it + ((lane % 8) ^ (lane / 8)).
-  const int ld_row = wave * kGroupRows + (lane >> 3);
+  // Enqueue row group grp (8 rows) of tile i into ring stage st: lane keeps
+  // row 8 grp + lane / 8 and, in block it = 0..8, chunk 8 it + ((lane % 8) ^ (lane / 8)).
   const int ld_col = ((lane & 7) ^ (lane >> 3)) * 16;
-  auto issue = [&](int i, int st) {
-    const int id = L.ids[i * kTileRows + ld_row];
+  auto issue_group = [&](int i, int st, int grp) {
+    const int id = L.ids[i * kTileRows + grp * kGroupRows + (lane >> 3)];
     const uint8_t* src =
         (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(L.tiles + st * kTileBytes + wave * kGroupBytes));
+        (uint32_t)(uintptr_t)(L.tiles + st * kTileBytes + grp * kGroupBytes));
     load_row_chunks<0>(src, dst);
+  };
+  // Only the output waves load tiles (two row groups each), so the score
+  // waves -- the longer path per tile -- never wait on load issue.
+  auto issue = [&](int i, int st) {
+    issue_group(i, st, 2 * j);
+    issue_group(i, st, 2 * j + 1);
   };
   auto tile_mask = [&](int i) {
     return (uint32_t)__ballot(L.ids[i * kTileRows + (lane & 31)] >= 0);
   };
-  if (ntiles > 0) issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
+  if (!score) {
+    if (ntiles > 0) issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+  }
 
   // Pipeline, with P(i) the published P^T of tile i in pbuf[i % 2]:
   //   prologue: tiles 0, 1 land; tile 2 issued; score waves publish P(0),
@@ -351,24 +358,14 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       k_base[q4] = (kr >> 3) * kGroupBytes + (kr & 7) * 128 +
                    (((2 * q4 + (lane >> 5)) ^ (kr & 7)) << 4);
     ScoreState st{-INFINITY, -INFINITY, 0.f};
-    wait_vmcnt<0>();
-    lds_barrier();  // tiles 0, 1 visible
-    if (ntiles > 2) issue(2, 2);
+    wait_vmcnt<0>();  // Q
+    lds_barrier();    // tiles 0, 1 visible
     if (ntiles > 0) score_tile(L, L.tiles, k_base, qf, tile_mask(0), a.scale_log2, 0, j, lane, st);
-    if (ntiles > 2)
-      wait_vmcnt<kSlotsPerThread>();
-    else
-      wait_vmcnt<0>();
     lds_barrier();  // P(0) published
     for (int i = 0; i < ntiles; ++i) {
-      if (i + 3 < ntiles) issue(i + 3, i % kStages);
       if (i + 1 < ntiles)
         score_tile(L, L.tiles + ((i + 1) % kStages) * kTileBytes, k_base, qf, tile_mask(i + 1),
                    a.scale_log2, (i + 1) & 1, j, lane, st);
-      if (i + 3 < ntiles)
-        wait_vmcnt<kSlotsPerThread>();
-      else
-        wait_vmcnt<0>();
       lds_barrier();
     }
     const float l_tot = pair_sum(st.lsum);
@@ -417,10 +414,6 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   lds_barrier();  // tiles 0, 1 visible
   if (ntiles > 2) issue(2, 2);
   if (ntiles > 0) read_v(L.tiles, v0, v1);
-  if (ntiles > 2)
-    wait_vmcnt<kSlotsPerThread>();
-  else
-    wait_vmcnt<0>();
   lds_barrier();  // P(0) published
   for (int i = 0; i < ntiles; ++i) {
     if (i + 3 < ntiles) issue(i + 3, i % kStages);
@@ -458,8 +451,9 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
         v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 0, mb));
         v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 1, mb));
       }
+    // tile i+2 must have landed before the barrier (tile i+3 may stay in flight)
     if (i + 3 < ntiles)
-      wait_vmcnt<kSlotsPerThread>();
+      wait_vmcnt<2 * kSlotsPerThread>();
     else
       wait_vmcnt<0>();
     lds_barrier();
