@@ -39,6 +39,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 1152
 METRIC = "decode query-tokens/sec and effective KV GB/s (% HBM/MFMA roofline), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+COPY_CAL_BYTES = 256 << 20
 DECODE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode.hip")
 
 
@@ -51,6 +52,9 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain device copy of known size, so that rocprofv3 "
+                         "counter runs can scale FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -167,6 +171,15 @@ def main():
                 ev[1].record()
         if ev is not None:
             ev[2].record()
+
+    if args.copy_calibration:
+        # 256 MiB read + 256 MiB written per launch, three launches
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)

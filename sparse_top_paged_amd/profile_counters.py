@@ -1,0 +1,106 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept beside the
+benchmark (run by path, on any host; it reads CSV files only).
+
+    python sparse_top_paged_amd/profile_counters.py stats <kernel_stats.csv> <out.txt> "<command>"
+    python sparse_top_paged_amd/profile_counters.py traffic <fetch counter_collection.csv> \\
+        <write counter_collection.csv> <kernel source> <out.json> "<command>"
+
+`traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
+counters read for the benchmark's calibration copy (a 256 MiB device-to-device
+copy launched three times before warm-up), then reports the decode kernel's
+HBM bytes per launch together with a hash of the kernel source they were
+taken on, so that a later edit of the kernel invalidates them.
+"""
+
+import csv
+import hashlib
+import json
+import sys
+from collections import defaultdict
+
+DECODE_KERNEL = "sparse_mla_decode_kernel"
+COPY_BYTES = 256 << 20
+
+
+def short_name(name):
+    if name.startswith("(anonymous namespace)::"):
+        return name[len("(anonymous namespace)::"):].split("(")[0]
+    if name.startswith("void (anonymous namespace)::"):
+        return name[len("void (anonymous namespace)::"):].split("(")[0]
+    if name.startswith("__amd_rocclr"):
+        return name
+    return name.split("(")[0][:90]
+
+
+def stats(src, out, command):
+    rows = list(csv.DictReader(open(src)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "#",
+             f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        lines.append(f"{short_name(r['Name']):<58} {int(r['Calls']):>6} "
+                     f"{float(r['AverageNs']) / 1e3:>9.3f} {float(r['MinNs']) / 1e3:>9.3f} "
+                     f"{float(r['MaxNs']) / 1e3:>9.3f} {float(r['Percentage']):>6.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def per_kernel(path, counter):
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return vals
+
+
+def calibration(vals, expect_kib):
+    # the copy is a runtime blit kernel; pick the dispatches whose reading is
+    # closest to the known size (the same kernel also serves small copies)
+    cands = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs if v > expect_kib / 4]
+    if not cands:
+        raise SystemExit("no calibration copy found in the counter file")
+    got = sum(cands) / len(cands)
+    return expect_kib / got, got
+
+
+def traffic(fetch_csv, write_csv, kernel_src, out, command):
+    kib = COPY_BYTES / 1024
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, f_copy = calibration(fetch, kib)
+    w_scale, w_copy = calibration(write, kib)
+    dec_f = [v for k, vs in fetch.items() if DECODE_KERNEL in k for v in vs]
+    dec_w = [v for k, vs in write.items() if DECODE_KERNEL in k for v in vs]
+    f_avg, w_avg = sum(dec_f) / len(dec_f), sum(dec_w) / len(dec_w)
+    rec = {
+        "command": command,
+        "kernel": DECODE_KERNEL,
+        "kernel_source_sha": hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16],
+        "dispatches": [len(dec_f), len(dec_w)],
+        "fetch_kib_raw": round(f_avg, 3),
+        "write_kib_raw": round(w_avg, 3),
+        "copy_fetch_kib_raw": round(f_copy, 3),
+        "copy_write_kib_raw": round(w_copy, 3),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "hbm_read_bytes_per_launch": int(f_avg * f_scale * 1024),
+        "hbm_write_bytes_per_launch": int(w_avg * w_scale * 1024),
+    }
+    rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    others = {}
+    for k in sorted(set(fetch) | set(write)):
+        if k.startswith("__amd") or "at::native" in k or "void at" in k:
+            continue
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        others[k] = {"read_bytes": int(sum(fv) / max(len(fv), 1) * f_scale * 1024),
+                     "write_bytes": int(sum(wv) / max(len(wv), 1) * w_scale * 1024)}
+    rec["per_kernel"] = others
+    json.dump(rec, open(out, "w"), indent=1)
+    open(out, "a").write("\n")
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(*sys.argv[2:5])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:7])
+    else:
+        raise SystemExit(__doc__)
