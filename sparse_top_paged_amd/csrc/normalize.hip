@@ -6,240 +6,349 @@
 // §7.4 eq. (19) (CSR row pointers); "HiSparse" walkthrough, token -> global
 // slot id conversion (slot = table[block] * page + offset, -1 propagation).
 //
-// Design: one 256-thread workgroup per query token holds a bitmap of the
-// token's visible positions in LDS.  D, W and A set bits (an LDS atomicOr per
-// candidate, so duplicates collapse for free); a popcount scan over the words
-// then emits S in ascending order with its slot ids.  The bitmap bounds the
-// work by the context length rather than by k log k.  The CSR block view
-// needs a prefix over tokens, so it takes two more small launches: a
-// single-workgroup scan of the per-token block counts and a per-token fill.
+// The work is small (a few thousand ids per token) and latency bound, so
+// the kernels are built to keep the chain of dependent memory round trips
+// short rather than to stream bytes.
+//
+// normalize_kernel: one 256-thread workgroup per query token holds a bitmap
+// of the token's visible positions in LDS (plus the request's page-table row
+// when it fits).  The token's D entries are loaded before anything else (they
+// do not depend on the request), then D, W and A set bits with LDS atomicOr
+// (duplicates collapse for free).  S is emitted in ascending order by each
+// wave over its own run of 64-word batches: a wave scan of the words'
+// popcounts gives every word its output offset; sparse words are walked by
+// their own lane, dense ones (the window) by the whole wave, one lane per
+// bit.  Block division uses a precomputed 2^32 / P multiplier.
+//
+// block_fill_kernel (block view only): one workgroup per token rebuilds the
+// token's bitmap from its sorted S, derives the touched blocks and their
+// in-page masks, and writes them at the token's CSR offset.  The offset is a
+// prefix over the other tokens' block counts; the first kernel stores each
+// count as -(count + 1) in blk_indptr[i + 1] and this kernel replaces it by
+// the inclusive prefix, so a workgroup reading its predecessors sees, for
+// each, either the raw count or an inclusive prefix that ends the look-back.
+// Both are valid whatever the order of the workgroups, so nothing waits.
 
 #include "stp_internal.h"
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kMaxPositions = 1 << 20;     // bitmap of 128 KiB LDS
-constexpr int kLdsBudget = 150 * 1024;     // dynamic LDS a normalise workgroup may use
-constexpr int kBlockViewMaxCap = 12000;    // block fill keeps 12 bytes per candidate in LDS
+constexpr int kLdsBudget = 150 * 1024;     // dynamic LDS a workgroup may use
+constexpr int kDPerThread = 8;             // D entries in flight per thread
+constexpr int kDenseWord = 8;              // words with more bits go wave-wide
 
-struct TokenView {
-  const int32_t* table;  // the request's page-table row (LDS copy or global)
-  int max_blocks;
-  int P;
-  int q;
+struct NormArgs {
+  const int32_t* topk;
+  const int32_t* req_id;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int top_k, num_reqs, max_blocks, P, window, num_sinks, cap;
+  int nwords_alloc;
+  uint64_t pdiv;  // ceil(2^32 / P): t / P == (t * pdiv) >> 32 for t < 2^20
+  int32_t* tok_out;
+  int32_t* slot_out;
+  int32_t* count_out;
+  int32_t* dropped_out;
+  int32_t* blk_indptr;  // nullable; receives -(block count + 1) per token
 };
 
-// Position t (>= 0) is visible to the query and lies on a mapped page whose
-// slot id fits int32.
-__device__ __forceinline__ bool visible(const TokenView& v, int t) {
-  if (t > v.q) return false;
-  const int b = t / v.P;
-  if (b >= v.max_blocks) return false;
-  const int page = v.table[b];
-  if (page < 0) return false;
-  const int64_t slot = (int64_t)page * v.P + (t - b * v.P);
-  return slot <= INT32_MAX;
+__device__ __forceinline__ int div_p(int t, uint64_t pdiv) {
+  return (int)(((uint64_t)(uint32_t)t * pdiv) >> 32);
 }
 
-__device__ __forceinline__ void set_bit(uint64_t* bm, int t) {
-  atomicOr((unsigned long long*)&bm[t >> 6], 1ull << (t & 63));
-}
-
-// Bits of positions [lo, hi) (hi - lo <= 64) taken from the bitmap.
-__device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, int hi, int nwords) {
-  uint64_t acc = 0;
+// Bits of positions [lo, hi) (0 < hi - lo <= 64) taken from the bitmap.
+__device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, int hi) {
   const int w0 = lo >> 6, w1 = (hi - 1) >> 6;
-  for (int w = w0; w <= w1 && w < nwords; ++w) {
-    const int a = max(lo, w * 64) - w * 64;
-    const int b = min(hi, w * 64 + 64) - w * 64;
-    const uint64_t m = (b - a == 64) ? ~0ull : (((1ull << (b - a)) - 1) << a);
-    acc |= (bm[w] & m);
-  }
-  return acc;
+  const int a = lo & 63;
+  uint64_t acc = bm[w0] >> a;
+  if (w1 != w0) acc |= bm[w1] << (64 - a);
+  const int n = hi - lo;
+  return n == 64 ? acc : (acc & ((1ull << n) - 1));
 }
 
-// One workgroup per query token.  LDS: the position bitmap (nwords 64-bit
-// words), then, when table_in_lds, the request's page-table row.
-__global__ __launch_bounds__(kThreads) void normalize_kernel(
-    const int32_t* __restrict__ topk, int top_k, const int32_t* __restrict__ req_id,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ block_table, int num_reqs,
-    int max_blocks, int P, int window, int num_sinks, int cap, int nwords_alloc, int table_in_lds,
-    int32_t* __restrict__ tok_out, int32_t* __restrict__ slot_out, int32_t* __restrict__ count_out,
-    int32_t* __restrict__ dropped_out, int32_t* __restrict__ blk_count) {
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) s += scratch[w];
+  return s;
+}
+
+template <bool kTableLds>
+__global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   extern __shared__ uint64_t bitmap[];
-  __shared__ int s_scan[8];
-  __shared__ int s_dropped;
-  __shared__ int s_blocks;
+  __shared__ int s_red[kWaves];
+  __shared__ int s_wave_total[kWaves];
 
   const int i = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int r = req_id[i];
-  const int q = q_pos[i];
-  int32_t* tok_row = tok_out + (int64_t)i * cap;
-  int32_t* slot_row = slot_out + (int64_t)i * cap;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  if (r < 0 || r >= num_reqs || q < 0) {  // padding row (uniform branch)
-    for (int j = tid; j < cap; j += kThreads) {
+  // D first: independent of the request, so its loads overlap the rest.
+  const int32_t* drow = a.topk + (int64_t)i * a.top_k;
+  int dv[kDPerThread];
+#pragma unroll
+  for (int u = 0; u < kDPerThread; ++u) {
+    const int j = tid + u * kThreads;
+    dv[u] = j < a.top_k ? drow[j] : -1;
+  }
+  const int r = a.req_id[i];
+  const int q = a.q_pos[i];
+  int32_t* tok_row = a.tok_out + (int64_t)i * a.cap;
+  int32_t* slot_row = a.slot_out + (int64_t)i * a.cap;
+
+  if (r < 0 || r >= a.num_reqs || q < 0) {  // padding row (uniform branch)
+    for (int j = tid; j < a.cap; j += kThreads) {
       tok_row[j] = -1;
       slot_row[j] = -1;
     }
     if (tid == 0) {
-      count_out[i] = 0;
-      if (dropped_out) dropped_out[i] = 0;
-      if (blk_count) blk_count[i] = 0;
+      a.count_out[i] = 0;
+      if (a.dropped_out) a.dropped_out[i] = 0;
+      if (a.blk_indptr) a.blk_indptr[i + 1] = -1;
     }
     return;
   }
 
-  const int32_t* g_table = block_table + (int64_t)r * max_blocks;
-  const int limit = min(q, max_blocks * P - 1);  // last position that can be visible
+  const int P = a.P;
+  const int32_t* g_table = a.block_table + (int64_t)r * a.max_blocks;
+  const int limit = min(q, a.max_blocks * P - 1);  // last position that can be visible
   const int nwords = (limit >> 6) + 1;
-  const int used_blocks = limit / P + 1;           // table entries that can matter
-  int32_t* l_table = (int32_t*)(bitmap + nwords_alloc);
+  const int used_blocks = div_p(limit, a.pdiv) + 1;
+  int32_t* l_table = (int32_t*)(bitmap + a.nwords_alloc);
   for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
-  if (table_in_lds)
+  if (kTableLds)
     for (int b = tid; b < used_blocks; b += kThreads) l_table[b] = g_table[b];
-  if (tid == 0) {
-    s_dropped = 0;
-    s_blocks = 0;
-  }
   __syncthreads();
-  const TokenView v{table_in_lds ? l_table : g_table, max_blocks, P, q};
+  const int32_t* table = kTableLds ? l_table : g_table;
 
-  // D: the dynamic top-k entries, four independent loads in flight per
-  // thread; invalid ones are dropped and counted.
+  auto visible = [&](int t) -> bool {
+    if (t > limit) return false;
+    const int b = div_p(t, a.pdiv);
+    const int page = table[b];
+    if (page < 0) return false;
+    return (int64_t)page * P + (t - b * P) <= INT32_MAX;
+  };
+  auto set_bit = [&](int t) {
+    atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
+  };
+
   int my_dropped = 0;
-  const int32_t* drow = topk + (int64_t)i * top_k;
-  for (int j0 = tid; j0 < top_k; j0 += 4 * kThreads) {
-    int tv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * kThreads;
-      tv[u] = j < top_k ? drow[j] : -1;
+  for (int u = 0; u < kDPerThread; ++u) {
+    const int t = dv[u];
+    if (t < 0) continue;
+    if (visible(t))
+      set_bit(t);
+    else
+      ++my_dropped;
+  }
+  for (int j0 = kDPerThread * kThreads; j0 < a.top_k; j0 += kDPerThread * kThreads) {
+#pragma unroll
+    for (int u = 0; u < kDPerThread; ++u) {
+      const int j = j0 + tid + u * kThreads;
+      dv[u] = j < a.top_k ? drow[j] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tv[u];
+    for (int u = 0; u < kDPerThread; ++u) {
+      const int t = dv[u];
       if (t < 0) continue;
-      if (visible(v, t))
-        set_bit(bitmap, t);
+      if (visible(t))
+        set_bit(t);
       else
         ++my_dropped;
     }
   }
   // W: the local window ending at the query's own position.
-  if (window > 0) {
-    for (int t = max(0, q - window + 1) + tid; t <= q; t += kThreads)
-      if (visible(v, t)) set_bit(bitmap, t);
-  }
+  if (a.window > 0)
+    for (int t = max(0, q - a.window + 1) + tid; t <= q; t += kThreads)
+      if (visible(t)) set_bit(t);
   // A: the sink positions.
-  const int na = min(num_sinks, q + 1);
+  const int na = min(a.num_sinks, q + 1);
   for (int t = tid; t < na; t += kThreads)
-    if (visible(v, t)) set_bit(bitmap, t);
-  if (my_dropped) atomicAdd(&s_dropped, my_dropped);
-  __syncthreads();
+    if (visible(t)) set_bit(t);
+  const int dropped = block_sum(my_dropped, s_red);  // (its barriers publish the bitmap)
 
-  // Emit S in ascending order: each thread owns a contiguous run of words.
-  const int wpt = (nwords + kThreads - 1) / kThreads;
-  const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
-  int c = 0;
-  for (int w = w0; w < w1; ++w) c += __popcll(bitmap[w]);
-  int total;
-  int off = stp::block_exclusive_scan_256(c, s_scan, &total);
-  for (int w = w0; w < w1; ++w) {
-    uint64_t bits = bitmap[w];
+  // Each wave owns a contiguous run of 64-word batches.
+  const int nbatch = (nwords + 63) >> 6;
+  const int bpw = (nbatch + kWaves - 1) / kWaves;
+  const int b0 = min(nbatch, wave * bpw), b1 = min(nbatch, b0 + bpw);
+  int cnt = 0;
+  for (int bb = b0; bb < b1; ++bb) {
+    const int w = bb * 64 + lane;
+    cnt += w < nwords ? __popcll(bitmap[w]) : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  if (lane == 0) s_wave_total[wave] = cnt;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int s = s_wave_total[w];
+    base += w < wave ? s : 0;
+    total += s;
+  }
+
+  auto emit = [&](int t, int pos) {
+    const int b = div_p(t, a.pdiv);
+    tok_row[pos] = t;
+    slot_row[pos] = table[b] * P + (t - b * P);
+  };
+  for (int bb = b0; bb < b1; ++bb) {
+    const int w = bb * 64 + lane;
+    const uint64_t x = w < nwords ? bitmap[w] : 0ull;
+    const int c = __popcll(x);
+    const int incl = wave_incl_scan(c, lane);
+    int off = base + incl - c;
+    base += __shfl(incl, 63, 64);
+    // sparse words: the owning lane walks its bits
+    uint64_t bits = c < kDenseWord ? x : 0ull;
     while (bits) {
-      const int t = (w << 6) + __builtin_ctzll(bits);
+      emit(w * 64 + __builtin_ctzll(bits), off++);
       bits &= bits - 1;
-      const int b = t / P;
-      tok_row[off] = t;
-      slot_row[off] = v.table[b] * P + (t - b * P);
-      ++off;
+    }
+    // dense words: one lane per bit
+    uint64_t dense = __ballot(c >= kDenseWord);
+    while (dense) {
+      const int src = __builtin_ctzll(dense);
+      dense &= dense - 1;
+      const uint32_t xlo = __builtin_amdgcn_readlane((uint32_t)x, src);
+      const uint32_t xhi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), src);
+      const int woff = __builtin_amdgcn_readlane(off, src);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(xhi, __builtin_amdgcn_mbcnt_lo(xlo, 0u));
+      const bool mine = ((lane < 32 ? xlo >> lane : xhi >> (lane - 32)) & 1u) != 0;
+      if (mine) emit((bb * 64 + src) * 64 + lane, woff + (int)below);
     }
   }
-  for (int j = total + tid; j < cap; j += kThreads) {
+  for (int j = total + tid; j < a.cap; j += kThreads) {
     tok_row[j] = -1;
     slot_row[j] = -1;
   }
 
   // Number of touched logical blocks (for the CSR block view).
-  if (blk_count) {
-    int nb = 0;
+  int nb = 0;
+  if (a.blk_indptr) {
     for (int b = tid; b < used_blocks; b += kThreads) {
       const int lo = b * P, hi = min(lo + P, limit + 1);
-      if (bits_in_range(bitmap, lo, hi, nwords)) ++nb;
+      if (bits_in_range(bitmap, lo, hi)) ++nb;
     }
-    if (nb) atomicAdd(&s_blocks, nb);
+    nb = block_sum(nb, s_red);
   }
-  __syncthreads();
   if (tid == 0) {
-    count_out[i] = total;
-    if (dropped_out) dropped_out[i] = s_dropped;
-    if (blk_count) blk_count[i] = s_blocks;
+    a.count_out[i] = total;
+    if (a.dropped_out) a.dropped_out[i] = dropped;
+    if (a.blk_indptr) a.blk_indptr[i + 1] = -(nb + 1);
   }
 }
 
-// In place: indptr[1..T] holds per-token counts; make it the inclusive prefix
-// and set indptr[0] = 0.  One workgroup.
-__global__ __launch_bounds__(kThreads) void indptr_scan_kernel(int32_t* indptr, int T) {
-  __shared__ int s_scan[8];
-  int carry = 0;
-  for (int base = 0; base < T; base += kThreads) {
-    const int j = base + threadIdx.x;
-    const int v = j < T ? indptr[1 + j] : 0;
-    int total;
-    const int ex = stp::block_exclusive_scan_256(v, s_scan, &total);
-    if (j < T) indptr[1 + j] = carry + ex + v;
-    carry += total;
-  }
-  if (threadIdx.x == 0) indptr[0] = 0;
-}
+struct FillArgs {
+  const int32_t* tok_out;
+  const int32_t* count_out;
+  const int32_t* req_id;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int num_reqs, max_blocks, P, cap;
+  uint64_t pdiv;
+  int32_t* blk_indptr;
+  int32_t* blk_logical;
+  int32_t* blk_page;
+  uint64_t* blk_mask;
+};
 
-// Per token: one entry per touched logical block of the sorted S.  The
-// token's list is staged in LDS; block k of the token collects its in-page
-// bits with LDS atomics, so no thread walks a block serially.
-__global__ __launch_bounds__(kThreads) void block_fill_kernel(
-    const int32_t* __restrict__ tok_out, const int32_t* __restrict__ count_out,
-    const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table, int max_blocks,
-    int P, int cap, const int32_t* __restrict__ indptr, int32_t* __restrict__ blk_logical,
-    int32_t* __restrict__ blk_page, uint64_t* __restrict__ blk_mask) {
-  extern __shared__ uint64_t lmask[];  // [cap] block masks, then [cap] tokens
-  __shared__ int s_scan[8];
+// Per token: CSR offset by look-back, then the touched blocks from a bitmap
+// rebuilt out of the token's sorted S.
+__global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
+  extern __shared__ uint64_t bitmap[];
+  __shared__ int s_red[kWaves];
+  __shared__ int s_scan[kWaves];
   const int i = blockIdx.x;
-  const int n = count_out[i];
-  if (n == 0) return;
-  int32_t* ltok = (int32_t*)(lmask + cap);
-  const int32_t* tok = tok_out + (int64_t)i * cap;
-  const int32_t* table = block_table + (int64_t)req_id[i] * max_blocks;
-  const int out0 = indptr[i];
-  const int nb = indptr[i + 1] - out0;
-  for (int j = threadIdx.x; j < n; j += kThreads) ltok[j] = tok[j];
-  for (int k = threadIdx.x; k < nb; k += kThreads) lmask[k] = 0;
+  const int tid = threadIdx.x;
+
+  const int own = -a.blk_indptr[i + 1] - 1;  // written as -(count + 1); only this WG rewrites it
+  const int n = a.count_out[i];
+  const int r = a.req_id[i];
+  const int q = a.q_pos[i];
+
+  __syncthreads();  // every thread has its `own` before thread 0 rewrites the entry
+
+  // Look-back over tokens i-1, i-2, ...: raw counts until an inclusive prefix.
+  int prefix = 0;
+  for (int hi = i; hi > 0; hi -= kThreads) {
+    const int k = hi - 1 - tid;  // token index this thread reads
+    const int v = k >= 0 ? a.blk_indptr[k + 1] : -1;
+    // the newest (largest k) inclusive prefix in this window, if any
+    const int kp = (k >= 0 && v >= 0) ? k : -1;
+    int best = kp;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) best = max(best, __shfl_xor(best, d, 64));
+    __syncthreads();
+    if ((tid & 63) == 0) s_red[tid >> 6] = best;
+    __syncthreads();
+    int kstar = -1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) kstar = max(kstar, s_red[w]);
+    int contrib = 0;
+    if (k >= 0 && k > kstar) contrib = -v - 1;  // raw count after the newest prefix
+    if (k >= 0 && k == kstar) contrib = v;      // the prefix itself
+    prefix += block_sum(contrib, s_red);
+    if (kstar >= 0) break;
+  }
+
+  if (tid == 0) {
+    if (i == 0) a.blk_indptr[0] = 0;
+    a.blk_indptr[i + 1] = prefix + own;
+  }
+  if (own == 0 || r < 0 || r >= a.num_reqs || q < 0) return;
+
+  const int P = a.P;
+  const int limit = min(q, a.max_blocks * P - 1);
+  const int nwords = (limit >> 6) + 1;
+  const int used_blocks = div_p(limit, a.pdiv) + 1;
+  const int32_t* table = a.block_table + (int64_t)r * a.max_blocks;
+  const int32_t* tok = a.tok_out + (int64_t)i * a.cap;
+  for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
   __syncthreads();
-  int carry = 0;  // blocks started before this chunk
-  for (int base = 0; base < n; base += kThreads) {
-    const int j = base + threadIdx.x;
-    int start = 0, t = 0, b = 0;
-    if (j < n) {
-      t = ltok[j];
-      b = t / P;
-      start = (j == 0) || (ltok[j - 1] / P != b);
-    }
-    int total;
-    const int ex = stp::block_exclusive_scan_256(start, s_scan, &total);
-    if (j < n) {
-      const int k = carry + ex + start - 1;  // this token's block
-      atomicOr((unsigned long long*)&lmask[k], 1ull << (t - b * P));
-      if (start) {
-        blk_logical[out0 + k] = b;
-        blk_page[out0 + k] = table[b];
-      }
-    }
-    carry += total;
+  for (int j = tid; j < n; j += kThreads) {
+    const int t = tok[j];
+    atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < nb; k += kThreads) blk_mask[out0 + k] = lmask[k];
+
+  // Each thread owns a contiguous run of blocks.
+  const int bpt = (used_blocks + kThreads - 1) / kThreads;
+  const int c0 = min(used_blocks, tid * bpt), c1 = min(used_blocks, c0 + bpt);
+  int mine = 0;
+  for (int b = c0; b < c1; ++b) {
+    const int lo = b * P, hi = min(lo + P, limit + 1);
+    mine += bits_in_range(bitmap, lo, hi) != 0;
+  }
+  int tot;
+  int k = prefix + stp::block_exclusive_scan_256(mine, s_scan, &tot);
+  for (int b = c0; b < c1; ++b) {
+    const int lo = b * P, hi = min(lo + P, limit + 1);
+    const uint64_t m = bits_in_range(bitmap, lo, hi);
+    if (!m) continue;
+    a.blk_logical[k] = b;
+    a.blk_page[k] = table[b];
+    a.blk_mask[k] = m;
+    ++k;
+  }
 }
 
 }  // namespace
@@ -275,17 +384,16 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
     num_reqs = 0;
   }
 
-  if (blk_indptr && cap > kBlockViewMaxCap)
-    return fail(STP_ERR_INVALID_ARG, "normalize_indices: the block view supports cap <= %d",
-                kBlockViewMaxCap);
-
   const int nwords = max(1, (int)(((int64_t)max_blocks * page_size + 63) / 64));
   const size_t bitmap_bytes = (size_t)nwords * sizeof(uint64_t);
   const bool table_in_lds = bitmap_bytes + (size_t)max_blocks * 4 <= (size_t)kLdsBudget;
   const size_t lds = bitmap_bytes + (table_in_lds ? (size_t)max_blocks * 4 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)normalize_kernel,
+    if (hipFuncSetAttribute((const void*)normalize_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
             hipSuccess ||
         hipFuncSetAttribute((const void*)block_fill_kernel,
@@ -293,17 +401,19 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
       return fail(STP_ERR_HIP, "normalize_indices: hipFuncSetAttribute failed");
     attr_set = true;
   }
-  int32_t* blk_count = blk_indptr ? blk_indptr + 1 : nullptr;
-  normalize_kernel<<<T, kThreads, lds, stream>>>(
-      topk, top_k, req_id, q_pos, block_table, num_reqs, max_blocks, page_size, window, num_sinks,
-      cap, nwords, table_in_lds ? 1 : 0, tok_out, slot_out, count_out, dropped_out, blk_count);
+  const uint64_t pdiv = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+  NormArgs na{topk, req_id, q_pos, block_table, top_k, num_reqs, max_blocks, page_size, window,
+              num_sinks, cap, nwords, pdiv, tok_out, slot_out, count_out,
+              dropped_out, blk_indptr};
+  if (table_in_lds)
+    normalize_kernel<true><<<T, kThreads, lds, stream>>>(na);
+  else
+    normalize_kernel<false><<<T, kThreads, lds, stream>>>(na);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
   if (blk_indptr) {
-    indptr_scan_kernel<<<1, kThreads, 0, stream>>>(blk_indptr, T);
-    if (int rc = stp::check_launch("indptr_scan_kernel")) return rc;
-    block_fill_kernel<<<T, kThreads, (size_t)cap * 12, stream>>>(
-        tok_out, count_out, req_id, block_table, max_blocks, page_size, cap, blk_indptr,
-        blk_logical, blk_page, blk_mask);
+    FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,
+                cap, pdiv, blk_indptr, blk_logical, blk_page, blk_mask};
+    block_fill_kernel<<<T, kThreads, bitmap_bytes, stream>>>(fa);
     if (int rc = stp::check_launch("block_fill_kernel")) return rc;
   }
   return STP_OK;

@@ -91,3 +91,28 @@ def test_empty_and_padding_only():
                       np.zeros((1, 2), np.int32), 16, 0, 0, 4)
     assert g["count"].shape == (0,)
     check([[-1, -1]], [-1], [5], [[0, 1]], 16, 2, 2, 6)
+
+
+def test_many_tokens_lookback():
+    # more tokens than one 256-token look-back window of the block-view
+    # offsets, with padding rows (zero blocks) spread through the batch
+    c = workloads.random_small_case(77, T=600, R=5, ctx=900, top_k=60, window=7, sinks=3,
+                                    page_size=16)
+    req = c.req_id.copy()
+    req[::37] = -1
+    check(c.topk, req, c.q_pos, c.block_table, c.page_size, c.window, c.num_sinks, c.cap)
+
+
+def test_long_topk_rows():
+    # top_k beyond one round of per-thread loads (8 per thread x 256 threads)
+    c = workloads.random_small_case(78, T=3, R=2, ctx=20000, top_k=5000, window=300, sinks=4,
+                                    page_size=64)
+    check(c.topk, c.req_id, c.q_pos, c.block_table, c.page_size, c.window, c.num_sinks, c.cap)
+
+
+def test_table_in_global_memory():
+    # page size 1: the page-table row (300,000 entries) does not fit in LDS
+    # beside the bitmap, so it is read from global memory
+    c = workloads.random_small_case(79, T=4, R=2, ctx=300000, top_k=500, window=100, sinks=2,
+                                    page_size=1, unmapped_frac=0.01)
+    check(c.topk, c.req_id, c.q_pos, c.block_table, c.page_size, c.window, c.num_sinks, c.cap)
