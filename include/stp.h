@@ -199,8 +199,9 @@ int stp_backup_rows(const void* hot_cache, int64_t hot_rows, void* host_pool, in
  * workspace of stp_sparse_mla_decode_workspace() bytes (STP_ERR_WORKSPACE if
  * smaller); the workspace may be reused once the call's work has completed
  * on `stream`.
- * Requirements: T >= 0, H >= 1, cap >= 0, ceil(cap / splits) <= 4096,
- * 0 < kv_rows, scale finite.
+ * The split count is raised to at least ceil(cap / 1024) whatever is asked
+ * (a split's ids are staged in LDS).
+ * Requirements: T >= 0, H >= 1, cap >= 0, 0 < kv_rows, 0 < scale < inf.
  */
 int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                           const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T,

@@ -40,6 +40,8 @@
 // stage.  Invalid candidates load a zero row and are masked to -inf before
 // the exponent.
 
+#include <type_traits>
+
 #include "stp_internal.h"
 
 namespace {
@@ -53,10 +55,10 @@ constexpr int kTileRows = 32;
 constexpr int kGroupRows = 8;                                   // rows loaded by one wave
 constexpr int kGroupBytes = kGroupRows * kRowBytes + 128;       // 9344 (+128: bank offset)
 constexpr int kTileBytes = 4 * kGroupBytes;                     // 37376
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kSlotsPerThread = kTileRows * kChunks / kThreads; // 9
 constexpr int kHeadsPerWG = 64;
-constexpr int kIdsMax = 4096;
+constexpr int kIdsMax = 1024;
 constexpr int kQKSteps = kDQK / 16;                             // 36
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -97,7 +99,7 @@ struct DecodeArgs {
   const int32_t* counts;
   int cap, T, H;
   float scale_log2;
-  int S, G, ntasks;
+  int S, G;
   void* o_part;    // split modes: [T, S, H, 512] fp32 or bf16
   float* m_part;   // [T, S, H], natural-log units
   float* l_part;
@@ -111,6 +113,15 @@ enum OutMode : int {
   kOutPartialF32 = 1,  // per split: o (unnormalised, fp32), m, l
   kOutPartialBf16 = 2  // per split: o / l (bf16), m, l
 };
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -183,83 +194,146 @@ __device__ __forceinline__ void load_row_chunks(const uint8_t* src, uint32_t lds
 // LDS objects of one workgroup.  Separate variables let the compiler see
 // that the hand-off buffers and the id list never alias the tile ring.
 struct DecodeLds {
-  lds_t* tiles;        // [3][37376]
+  lds_t* tiles;        // [4][37376]
   lds_t* pbuf;         // [2 buffers][2 head blocks][2 k-steps][64 lanes][16 B]
   float* alpha;        // [2 buffers][64 heads]
   float* stat;         // [3][64]: m_ref, m_true (log2 units), l
   int32_t* ids;        // [kIdsMax]
 };
 
-// Score-wave view of one tile: S^T = K Q^T (2 accumulator chains), mask,
-// online softmax, publish P^T and the rescale factor.
+// Score-wave state: online softmax statistics of the wave's 32 heads (log2
+// units) and the S^T accumulators of one tile (two MFMA chains).
 struct ScoreState {
   float m_ref, m_true, lsum;
 };
+struct SAcc {
+  floatx16 c0, c1;
+};
 
-__device__ __forceinline__ void score_tile(const DecodeLds& L, const lds_t* stage,
-                                           const int (&k_base)[4],
-                                           const bf16x8 (&qf)[kQKSteps], uint32_t vmask,
-                                           float scale_log2, int buf, int j, int lane,
-                                           ScoreState& st) {
-  // K fragments stream through an 8-deep register ring: each slot is re-read
-  // for k-step ks + 8 right after the MFMA of k-step ks has consumed it.
-  constexpr int kRing = 8;
-  floatx16 acc0 = floatx16{}, acc1 = floatx16{};
-  shortx8 kf[kRing];
-  auto kaddr = [&](int ks) { return stage + k_base[ks & 3] + 1024 * (ks >> 2); };
+//  K fragment of k-step ks: row lane % 32, chunk 2 ks + lane / 32 of the
+//  tile; chunk c = 2 (ks % 4) + lane / 32 + 8 (ks / 4), so four per-lane bases
+//  cover every k-step with an immediate offset of 1024 (ks / 4).
+__device__ __forceinline__ const lds_t* k_addr(const lds_t* stage, const int (&k_base)[4],
+                                               int ks) {
+  return stage + k_base[ks & 3] + 1024 * (ks >> 2);
+}
+
+constexpr int kKRing = 8;  // K fragments in flight per score wave
+
+// S^T = K Q^T of one tile, on its own (the first tile of a split).
+__device__ __forceinline__ void qk_tile(const lds_t* stage, const int (&k_base)[4],
+                                        const bf16x8 (&qf)[kQKSteps], SAcc& acc) {
+  shortx8 kf[kKRing];
+  acc.c0 = floatx16{};
+  acc.c1 = floatx16{};
 #pragma unroll
-  for (int ks = 0; ks < kRing; ++ks) kf[ks] = *(const lds_shortx8*)kaddr(ks);
+  for (int ks = 0; ks < kKRing; ++ks) kf[ks] = *(const lds_shortx8*)k_addr(stage, k_base, ks);
 #pragma unroll
   for (int ks = 0; ks < kQKSteps; ++ks) {
-    const bf16x8 kfrag = __builtin_bit_cast(bf16x8, kf[ks % kRing]);
+    const bf16x8 kfrag = __builtin_bit_cast(bf16x8, kf[ks % kKRing]);
     if (ks & 1)
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc1, 0, 0, 0);
+      acc.c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc.c1, 0, 0, 0);
     else
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc0, 0, 0, 0);
-    if (ks + kRing < kQKSteps) kf[ks % kRing] = *(const lds_shortx8*)kaddr(ks + kRing);
+      acc.c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], acc.c0, 0, 0, 0);
+    if (ks + kKRing < kQKSteps)
+      kf[ks % kKRing] = *(const lds_shortx8*)k_addr(stage, k_base, ks + kKRing);
   }
-  // keep kRing reads in flight: 8 reads, then MFMA / read pairs, then 8 MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kKRing, 0);
 #pragma unroll
-  for (int g = 0; g < kQKSteps - kRing; ++g) {
+  for (int g = 0; g < kQKSteps - kKRing; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kKRing, 0);
   __builtin_amdgcn_sched_barrier(0);
-  const floatx16 acc = acc0 + acc1;
+}
+
+// Online softmax of the tile whose S^T is in `cur`: the reference maximum
+// moves only when the tile beats it by 2^8, P^T goes to pbuf[buf] as bf16 and
+// the tile's rescale factor to alpha[buf].  With kMasked, rows outside vmask
+// are set to -inf before the exponent (only a split's last tile or a tile
+// with invalid ids needs it).  With kNext the QK products of the next tile
+// (ring stage `next`) are computed into `nxt` at the same time.  The two are
+// independent, so the work is laid out as 36 steps, each one MFMA, the K
+// fragment read eight steps ahead and about one row's worth of softmax
+// arithmetic, fenced so that the compiler keeps that order: the VALU work
+// issues while the matrix core runs the MFMA before it.  The softmax is kept
+// to a few VALU instructions per row (the scale is applied inside the
+// exponent's FMA; exp2(-inf) = 0 covers masked rows), since VALU work beyond
+// about four instructions per MFMA slows the MFMA stream.  Branch-free.
+// Requires scale_log2 > 0, so that max(z) * scale = max(z * scale).
+template <bool kNext, bool kMasked>
+__device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next,
+                                           const int (&k_base)[4],
+                                           const bf16x8 (&qf)[kQKSteps], const SAcc& cur,
+                                           SAcc& nxt, uint32_t vmask, float scale_log2, int buf,
+                                           int j, int lane, ScoreState& st) {
+  shortx8 kf[kKRing];
+  if constexpr (kNext) {
+    nxt.c0 = floatx16{};
+    nxt.c1 = floatx16{};
+#pragma unroll
+    for (int ks = 0; ks < kKRing; ++ks) kf[ks] = *(const lds_shortx8*)k_addr(next, k_base, ks);
+  }
 
   // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of head lane % 32
-  float sv[16];
-  float mt = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    sv[r] = ((vmask >> rr) & 1u) ? acc[r] * scale_log2 : -INFINITY;
-    mt = fmaxf(mt, sv[r]);
-  }
-  mt = pair_max(mt);
-  st.m_true = fmaxf(st.m_true, mt);
-  float alpha = 1.f;
-  if (mt > st.m_ref + kRescaleLog2) {  // also the first non-empty tile (m_ref = -inf)
-    alpha = fast_exp2(st.m_ref - mt);
-    st.m_ref = mt;
-    st.lsum *= alpha;
-  }
+  float zv[16];
+  float mt = -INFINITY, psum = 0.f, alpha = 1.f, neg_m = 0.f;
   bf16x8 pk[2];
-  float psum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - st.m_ref);
+  auto row_max = [&](int r) {
+    float z = cur.c0[r] + cur.c1[r];
+    if constexpr (kMasked) {
+      const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      z = ((vmask >> rr) & 1u) ? z : -INFINITY;
+    }
+    zv[r] = z;
+    mt = fmaxf(mt, z);
+  };
+  auto rebase = [&]() {
+    mt = pair_max(mt) * scale_log2;
+    st.m_true = fmaxf(st.m_true, mt);
+    // also taken by the first non-empty tile (m_ref = -inf gives alpha = 0)
+    const bool move = mt > st.m_ref + kRescaleLog2;
+    alpha = move ? fast_exp2(st.m_ref - mt) : 1.f;
+    st.m_ref = move ? mt : st.m_ref;
+    neg_m = st.m_ref == -INFINITY ? 0.f : -st.m_ref;  // nothing seen yet: every z is -inf
+  };
+  auto row_exp = [&](int r) {
+    const float p = fast_exp2(__builtin_fmaf(zv[r], scale_log2, neg_m));
     psum += p;
     pk[r >> 3][r & 7] = (__bf16)p;
+  };
+  auto publish = [&]() {
+    st.lsum = st.lsum * alpha + psum;
+    // P^T fragments for k-steps 0 and 1 (rows 0-15 and 16-31 of the tile);
+    // the lane pair (l, l ^ 32) holds the same alpha, so both may store it.
+    lds_t* pb = L.pbuf + ((buf * 2 + j) * 2) * 1024 + lane * 16;
+    *(__attribute__((address_space(3))) bf16x8*)(pb) = pk[0];
+    *(__attribute__((address_space(3))) bf16x8*)(pb + 1024) = pk[1];
+    L.alpha[buf * 64 + 32 * j + (lane & 31)] = alpha;
+  };
+
+#pragma unroll
+  for (int ks = 0; ks < kQKSteps; ++ks) {
+    if constexpr (kNext) {
+      const bf16x8 kfrag = __builtin_bit_cast(bf16x8, kf[ks % kKRing]);
+      if (ks & 1)
+        nxt.c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], nxt.c1, 0, 0, 0);
+      else
+        nxt.c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], nxt.c0, 0, 0, 0);
+      if (ks + kKRing < kQKSteps)
+        kf[ks % kKRing] = *(const lds_shortx8*)k_addr(next, k_base, ks + kKRing);
+    }
+    if (ks < 16)
+      row_max(ks);
+    else if (ks == 16)
+      rebase();
+    else if (ks < 33)
+      row_exp(ks - 17);
+    else if (ks == 33)
+      publish();
+    if constexpr (kNext) __builtin_amdgcn_sched_barrier(0);
   }
-  st.lsum += psum;
-  // P^T fragments for k-steps 0 and 1 (rows 0-15 and 16-31 of the tile)
-  lds_t* pb = L.pbuf + ((buf * 2 + j) * 2) * 1024 + lane * 16;
-  *(__attribute__((address_space(3))) bf16x8*)(pb) = pk[0];
-  *(__attribute__((address_space(3))) bf16x8*)(pb + 1024) = pk[1];
-  if (lane < 32) L.alpha[buf * 64 + 32 * j + lane] = alpha;
 }
 
 template <int kMode>
@@ -278,15 +352,18 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const bool score = wave < 2;
   const int j = wave & 1;
 
-  // XCD-aware task map: the G head groups of one (token, split) get block
-  // ids that agree mod 8 and are adjacent in dispatch order.
+  // XCD-aware task map: every workgroup of one token (all splits, all head
+  // groups) gets a block id of the same residue mod 8, i.e. runs on the same
+  // XCD, so the token's query rows and the KV rows its head groups share are
+  // fetched into one L2.
   const int bid = blockIdx.x;
-  const int k8 = bid >> 3;
-  const int task = (k8 / a.G) * 8 + (bid & 7);
-  const int hg = k8 % a.G;
-  if (task >= a.ntasks) return;
-  const int t = task / a.S;
-  const int s = task - t * a.S;
+  const int xk = bid >> 3;
+  const int per_token = a.S * a.G;
+  const int t = (xk / per_token) * 8 + (bid & 7);
+  const int rem = xk % per_token;
+  const int s = rem / a.G;
+  const int hg = rem - s * a.G;
+  if (t >= a.T) return;
 
   int n = a.counts ? a.counts[t] : a.cap;
   n = min(max(n, 0), a.cap);
@@ -295,24 +372,44 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const int len = min(n, lo + chunk) - lo;
   const int ntiles = (len + kTileRows - 1) / kTileRows;
 
+  // Row loads go straight to LDS (global_load_lds), one 8-row group per wave
+  // instruction sequence: lane keeps row lane / 8 of the group and, in block
+  // it = 0..8, chunk 8 it + ((lane % 8) ^ (lane / 8)).
+  const int ld_col = ((lane & 7) ^ (lane >> 3)) * 16;
+  auto group_dst = [&](int st, int grp) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(L.tiles + st * kTileBytes + grp * kGroupBytes));
+  };
+  // Score wave j's 32 query rows go to ring stage 2 + j, in the tile layout
+  // (coalesced like any tile; read back as MFMA fragments before B(0), after
+  // which the stage carries tiles again).
+  if (score) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int head = hg * kHeadsPerWG + 32 * j + grp * kGroupRows + (lane >> 3);
+      const uint8_t* src =
+          (head < a.H ? (const uint8_t*)(a.q + ((int64_t)t * a.H + head) * kDQK) : g_zero_row) +
+          ld_col;
+      load_row_chunks<0>(src, group_dst(2 + j, grp));
+    }
+  }
+
   // candidate ids of this split, -1 for invalid ones and up to the tile edge
   const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
   for (int i = tid; i < ntiles * kTileRows; i += kThreads) {
     const int32_t id = i < len ? src_ids[i] : -1;
     L.ids[i] = (id >= 0 && id < a.kv_rows) ? id : -1;
   }
-  __syncthreads();  // ids visible
+  __syncthreads();  // ids visible (and, for the score waves, their query rows landed)
 
-  // Enqueue row group grp (8 rows) of tile i into ring stage st: lane keeps
-  // row 8 grp + lane / 8 and, in block it = 0..8, chunk 8 it + ((lane % 8) ^ (lane / 8)).
-  const int ld_col = ((lane & 7) ^ (lane >> 3)) * 16;
-  auto issue_group = [&](int i, int st, int grp) {
+  // source of this lane's row of group grp of tile i (the zero row for an
+  // invalid candidate)
+  auto row_src = [&](int i, int grp) {
     const int id = L.ids[i * kTileRows + grp * kGroupRows + (lane >> 3)];
-    const uint8_t* src =
-        (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(L.tiles + st * kTileBytes + grp * kGroupBytes));
-    load_row_chunks<0>(src, dst);
+    return (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
+  };
+  auto issue_group = [&](int i, int st, int grp) {
+    load_row_chunks<0>(row_src(i, grp), group_dst(st, grp));
   };
   // Only the output waves load tiles (two row groups each), so the score
   // waves -- the longer path per tile -- never wait on load issue.
@@ -328,45 +425,67 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     if (ntiles > 1) issue(1, 1);
   }
 
-  // Pipeline, with P(i) the published P^T of tile i in pbuf[i % 2]:
-  //   prologue: tiles 0, 1 land; tile 2 issued; score waves publish P(0),
-  //   output waves read V(0); tile 1 lands; barrier.
-  //   iteration i: enqueue tile i+3 into stage i % 3 (free: tile i was read
-  //   during iteration i-1); score waves publish P(i+1) from stage
-  //   (i+1) % 3; output waves apply P(i) to V(i) (in registers) and read
-  //   V(i+1); tile i+2 lands; barrier.
+  // Pipeline over the ring of kStages = 4 tiles, with P(i) the published P^T
+  // of tile i (pbuf[i % 2]) and B(i) the i-th workgroup barrier:
+  //   prologue: query rows (stages 2, 3) and tiles 0, 1 enqueued and landed;
+  //     the score waves move Q^T into registers; B(0).
+  //   score waves, iteration i (0 <= i < ntiles): softmax of tile i, whose
+  //     S^T was computed in iteration i-1 (tile 0: right after B(0)),
+  //     together with the QK products of tile i+1; ends with B(i+1), which
+  //     publishes P(i).
+  //   output waves, iteration i (1 <= i <= ntiles): see below; V(0) is read
+  //     between B(0) and B(1).
   if (score) {
-    const int head = hg * kHeadsPerWG + 32 * j + (lane & 31);
-    bf16x8 qf[kQKSteps];
-    {
-      const uint16_t* qrow =
-          a.q + ((int64_t)t * a.H + (head < a.H ? head : 0)) * kDQK + 8 * (lane >> 5);
-#pragma unroll
-      for (int ks = 0; ks < kQKSteps; ++ks) {
-        shortx8 v = *(const shortx8*)(qrow + 16 * ks);
-        if (head >= a.H) v = shortx8{0, 0, 0, 0, 0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-    //  K fragment of k-step ks: row lane % 32, chunk 2 ks + lane / 32; chunk
-    //  c = 2 (ks % 4) + lane / 32 + 8 (ks / 4), so four per-lane bases cover
-    //  every k-step with an immediate offset of 1024 (ks / 4).
     const int kr = lane & 31;
     int k_base[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
       k_base[q4] = (kr >> 3) * kGroupBytes + (kr & 7) * 128 +
                    (((2 * q4 + (lane >> 5)) ^ (kr & 7)) << 4);
+    // Q^T fragments: the query rows sit in stage 2 + j in the tile layout, so
+    // the B fragment of k-step ks is read like a K fragment.  Q^T then lives
+    // in AGPRs (MFMA takes its B operand from there), leaving the VGPRs to
+    // the K fragment ring and the softmax.
+    bf16x8 qf[kQKSteps];
+    {
+      const lds_t* qstage = L.tiles + (2 + j) * kTileBytes;
+      shortx8 qv[kQKSteps];
+#pragma unroll
+      for (int ks = 0; ks < kQKSteps; ++ks)
+        qv[ks] = *(const lds_shortx8*)k_addr(qstage, k_base, ks);
+      __builtin_amdgcn_sched_barrier(0);  // all 36 reads in flight before the first use
+#pragma unroll
+      for (int ks = 0; ks < kQKSteps; ++ks) {
+        qf[ks] = __builtin_bit_cast(bf16x8, qv[ks]);
+        asm volatile("" : "+a"(qf[ks]));
+      }
+    }
     ScoreState st{-INFINITY, -INFINITY, 0.f};
-    wait_vmcnt<0>();  // Q
-    lds_barrier();    // tiles 0, 1 visible
-    if (ntiles > 0) score_tile(L, L.tiles, k_base, qf, tile_mask(0), a.scale_log2, 0, j, lane, st);
-    lds_barrier();  // P(0) published
-    for (int i = 0; i < ntiles; ++i) {
-      if (i + 1 < ntiles)
-        score_tile(L, L.tiles + ((i + 1) % kStages) * kTileBytes, k_base, qf, tile_mask(i + 1),
-                   a.scale_log2, (i + 1) & 1, j, lane, st);
+    SAcc acc_a, acc_b;
+    lds_barrier();  // B(0): tiles 0 and 1 visible, Q^T read out of stages 2 and 3
+    if (ntiles > 0) qk_tile(L.tiles, k_base, qf, acc_a);
+    // iteration i: softmax of tile i (S^T in registers) with the QK of tile
+    // i+1; P(i) is published by the barrier B(i+1) that ends it.  Unrolled by
+    // two so that the accumulator sets swap roles without copies.
+    auto step = [&](int i, const SAcc& cur, SAcc& nxt) {
+      const uint32_t vm = tile_mask(i);
+      if (i + 1 < ntiles) {
+        const lds_t* next = L.tiles + ((i + 1) % kStages) * kTileBytes;
+        if (vm == ~0u)
+          score_step<true, false>(L, next, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j,
+                                  lane, st);
+        else
+          score_step<true, true>(L, next, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j, lane,
+                                 st);
+      } else {
+        score_step<false, true>(L, L.tiles, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j,
+                                lane, st);
+      }
       lds_barrier();
+    };
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, acc_a, acc_b);
+      if (i + 1 < ntiles) step(i + 1, acc_b, acc_a);
     }
     const float l_tot = pair_sum(st.lsum);
     if (lane < 32) {
@@ -410,23 +529,32 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) o[hb][mb] = floatx16{};
   shortx4 v0[2][8], v1[2][8];
-  wait_vmcnt<0>();
-  lds_barrier();  // tiles 0, 1 visible
-  if (ntiles > 2) issue(2, 2);
-  if (ntiles > 0) read_v(L.tiles, v0, v1);
-  lds_barrier();  // P(0) published
-  for (int i = 0; i < ntiles; ++i) {
-    if (i + 3 < ntiles) issue(i + 3, i % kStages);
-    const int buf = i & 1;
+  wait_vmcnt<0>();  // tiles 0 and 1
+  lds_barrier();    // B(0): stages 2 and 3 are free again
+  if (ntiles > 0) {
+    if (ntiles > 2) issue(2, 2);
+    read_v(L.tiles, v0, v1);
+    // tile 2 must have landed before B(1) (tile 3 may stay in flight)
+    if (ntiles > 3) {
+      issue(3, 3);
+      wait_vmcnt<2 * kSlotsPerThread>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // B(1): P(0) published
+  }
+  // iteration i (1 <= i <= ntiles): enqueue tile i+3 into the stage of tile
+  // i-1 (its V^T is in registers, its K was read two iterations ago); apply
+  // P(i-1) to V(i-1); read V(i) for the next iteration; tile i+2 lands before
+  // the barrier B(i+1) (the score waves read it in iteration i+1).  The 18
+  // load instructions of tile i+3 are spread between the MFMAs, one per MFMA
+  // pair, so that the wave never stalls on a full load queue.  Past the last
+  // tile the same loads bring zero rows into that free stage, which keeps the
+  // instruction stream and the wait counts the same in every iteration.
+  for (int i = 1; i <= ntiles; ++i) {
+    const int buf = (i - 1) & 1;
     const float a0 = L.alpha[buf * 64 + (lane & 31)];
     const float a1 = L.alpha[buf * 64 + 32 + (lane & 31)];
-    if (__ballot(a0 != 1.f || a1 != 1.f)) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        scale_acc(o[0][mb], a0);
-        scale_acc(o[1][mb], a1);
-      }
-    }
     bf16x8 pf[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -434,30 +562,53 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       for (int kap = 0; kap < 2; ++kap)
         pf[hb][kap] = *(const __attribute__((address_space(3))) bf16x8*)(
             L.pbuf + ((buf * 2 + hb) * 2 + kap) * 1024 + lane * 16);
-    // PV MFMAs of tile i; each V^T fragment register pair is refilled from
-    // tile i+1 right after its last use (on the last tile the reads hit a
-    // stale stage: in bounds and unused).
-    const lds_t* vn = L.tiles + ((i + 1) % kStages) * kTileBytes;
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap)
+    const bool real = i + 3 < ntiles;
+    const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : g_zero_row + ld_col;
+    const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : g_zero_row + ld_col;
+    const int st3 = (i + 3) % kStages;
+    const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
+    auto load_chunk = [&](auto c) {
+      constexpr int kC = decltype(c)::value;
+      if constexpr (kC < kSlotsPerThread)
+        load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
+      else
+        load_lds_16<(kC - kSlotsPerThread) * 128>(src1,
+                                                  dst1 + (kC - kSlotsPerThread) * (1024 - 128));
+    };
+    // alpha = 0 only while nothing has been accumulated (O^T is still zero)
+    if (__ballot((a0 != 1.f && a0 != 0.f) || (a1 != 1.f && a1 != 0.f))) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const shortx8 vv = {v0[kap][mb][0], v0[kap][mb][1], v0[kap][mb][2], v0[kap][mb][3],
-                            v1[kap][mb][0], v1[kap][mb][1], v1[kap][mb][2], v1[kap][mb][3]};
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          o[hb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                              pf[hb][kap], o[hb][mb], 0, 0, 0);
-        v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 0, mb));
-        v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 1, mb));
+        scale_acc(o[0][mb], a0);
+        scale_acc(o[1][mb], a1);
       }
-    // tile i+2 must have landed before the barrier (tile i+3 may stay in flight)
-    if (i + 3 < ntiles)
-      wait_vmcnt<2 * kSlotsPerThread>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
+    }
+    // PV MFMAs of tile i-1; each V^T fragment register pair is refilled from
+    // tile i right after its last use (after the last tile the reads hit a
+    // stale stage: in bounds and unused).
+    const lds_t* vn = L.tiles + (i % kStages) * kTileBytes;
+    auto pv_pair = [&](auto kc, auto mc) {
+      constexpr int kap = decltype(kc)::value, mb = decltype(mc)::value;
+      const shortx8 vv = {v0[kap][mb][0], v0[kap][mb][1], v0[kap][mb][2], v0[kap][mb][3],
+                          v1[kap][mb][0], v1[kap][mb][1], v1[kap][mb][2], v1[kap][mb][3]};
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        o[hb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                            pf[hb][kap], o[hb][mb], 0, 0, 0);
+      v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 0, mb));
+      v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 1, mb));
+      load_chunk(std::integral_constant<int, kap * 8 + mb>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<2>([&](auto kc) { static_for<8>([&](auto mc) { pv_pair(kc, mc); }); });
+    load_chunk(std::integral_constant<int, 16>{});
+    load_chunk(std::integral_constant<int, 17>{});
+    if (i == ntiles) break;
+    // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
+    wait_vmcnt<2 * kSlotsPerThread>();
+    lds_barrier();  // B(i+1)
   }
+  wait_vmcnt<0>();  // the last (zero-row) loads, before the ring is reused below
   lds_barrier();  // statistics published
 
   // lane holds O^T[256 j + 32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][32 hb + lane % 32]
@@ -580,13 +731,12 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
   a.scale_log2 = scale * kLog2e;
   a.S = S;
   a.G = (H + kHeadsPerWG - 1) / kHeadsPerWG;
-  a.ntasks = T * S;
   a.o_part = o_part;
   a.m_part = m_part;
   a.l_part = l_part;
   a.out = out;
   a.lse = lse;
-  const int64_t blocks = (int64_t)8 * a.G * ((a.ntasks + 7) / 8);
+  const int64_t blocks = (int64_t)8 * ((T + 7) / 8) * S * a.G;
   if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: grid too large");
   if (mode == kOutPartialF32)
     sparse_mla_decode_kernel<kOutPartialF32><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
@@ -603,8 +753,8 @@ int check_common(const uint16_t* q, const uint16_t* kv, int64_t kv_rows, const i
   if (T < 0 || H < 1 || cap < 0 || kv_rows <= 0)
     return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: bad sizes T=%d H=%d cap=%d kv_rows=%lld",
                 T, H, cap, (long long)kv_rows);
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
-    return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: scale is not finite");
+  if (!(scale > 0.f) || scale == INFINITY)
+    return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: scale must be positive and finite");
   if (T > 0 && (!q || !kv || (cap > 0 && !row_ids)))
     return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: null pointer");
   return STP_OK;
