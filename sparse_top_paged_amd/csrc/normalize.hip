@@ -69,18 +69,8 @@ __device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, in
   return n == 64 ? acc : (acc & ((1ull << n) - 1));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  v = stp::wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -90,7 +80,9 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
   return s;
 }
 
-template <bool kTableLds>
+// LDS of normalize_kernel: the bitmap (nwords_alloc words), then the
+// request's page-table row (kTableLds), then the emitted list S (kListLds).
+template <bool kTableLds, bool kListLds>
 __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   extern __shared__ uint64_t bitmap[];
   __shared__ int s_red[kWaves];
@@ -131,57 +123,71 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   const int nwords = (limit >> 6) + 1;
   const int used_blocks = div_p(limit, a.pdiv) + 1;
   int32_t* l_table = (int32_t*)(bitmap + a.nwords_alloc);
+  int32_t* l_list = l_table + (kTableLds ? a.max_blocks : 0);
+  if (kTableLds) {
+    // all of a thread's table loads in flight before its stores
+    for (int b0 = 0; b0 < used_blocks; b0 += 4 * kThreads) {
+      int tv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b = b0 + tid + u * kThreads;
+        tv[u] = b < used_blocks ? g_table[b] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int b = b0 + tid + u * kThreads;
+        if (b < used_blocks) l_table[b] = tv[u];
+      }
+    }
+  }
   for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
-  if (kTableLds)
-    for (int b = tid; b < used_blocks; b += kThreads) l_table[b] = g_table[b];
   __syncthreads();
   const int32_t* table = kTableLds ? l_table : g_table;
 
-  auto visible = [&](int t) -> bool {
-    if (t > limit) return false;
-    const int b = div_p(t, a.pdiv);
-    const int page = table[b];
-    if (page < 0) return false;
-    return (int64_t)page * P + (t - b * P) <= INT32_MAX;
-  };
   auto set_bit = [&](int t) {
     atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
   };
-
+  // D entries: every table read first, then branch-free visibility.
   int my_dropped = 0;
+  auto add_d = [&](const int (&tv)[kDPerThread]) {
+    int pg[kDPerThread];
 #pragma unroll
-  for (int u = 0; u < kDPerThread; ++u) {
-    const int t = dv[u];
-    if (t < 0) continue;
-    if (visible(t))
-      set_bit(t);
-    else
-      ++my_dropped;
-  }
+    for (int u = 0; u < kDPerThread; ++u) {
+      const int tc = min(max(tv[u], 0), limit);  // in-range stand-in for the read
+      pg[u] = table[div_p(tc, a.pdiv)];
+    }
+#pragma unroll
+    for (int u = 0; u < kDPerThread; ++u) {
+      const int t = tv[u];
+      const int b = div_p(max(t, 0), a.pdiv);
+      const bool ok = t >= 0 && t <= limit && pg[u] >= 0 &&
+                      (int64_t)pg[u] * P + (t - b * P) <= INT32_MAX;
+      my_dropped += (t >= 0 && !ok) ? 1 : 0;
+      if (ok) set_bit(t);
+    }
+  };
+  add_d(dv);
   for (int j0 = kDPerThread * kThreads; j0 < a.top_k; j0 += kDPerThread * kThreads) {
 #pragma unroll
     for (int u = 0; u < kDPerThread; ++u) {
       const int j = j0 + tid + u * kThreads;
       dv[u] = j < a.top_k ? drow[j] : -1;
     }
-#pragma unroll
-    for (int u = 0; u < kDPerThread; ++u) {
-      const int t = dv[u];
-      if (t < 0) continue;
-      if (visible(t))
-        set_bit(t);
-      else
-        ++my_dropped;
-    }
+    add_d(dv);
   }
+  auto visible = [&](int t) -> bool {  // 0 <= t <= limit
+    const int b = div_p(t, a.pdiv);
+    const int page = table[b];
+    return page >= 0 && (int64_t)page * P + (t - b * P) <= INT32_MAX;
+  };
   // W: the local window ending at the query's own position.
   if (a.window > 0)
     for (int t = max(0, q - a.window + 1) + tid; t <= q; t += kThreads)
-      if (visible(t)) set_bit(t);
+      if (t <= limit && visible(t)) set_bit(t);
   // A: the sink positions.
   const int na = min(a.num_sinks, q + 1);
   for (int t = tid; t < na; t += kThreads)
-    if (visible(t)) set_bit(t);
+    if (t <= limit && visible(t)) set_bit(t);
   const int dropped = block_sum(my_dropped, s_red);  // (its barriers publish the bitmap)
 
   // Each wave owns a contiguous run of 64-word batches.
@@ -193,30 +199,36 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
     const int w = bb * 64 + lane;
     cnt += w < nwords ? __popcll(bitmap[w]) : 0;
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d, 64);
+  cnt = stp::wave_sum(cnt);
   if (lane == 0) s_wave_total[wave] = cnt;
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const int s = s_wave_total[w];
-    base += w < wave ? s : 0;
-    total += s;
+    const int sw = s_wave_total[w];
+    base += w < wave ? sw : 0;
+    total += sw;
   }
 
+  // Ascending emission: into the LDS list (then written out below in one
+  // coalesced pass), or straight to global memory when the list does not
+  // fit in LDS.
   auto emit = [&](int t, int pos) {
-    const int b = div_p(t, a.pdiv);
-    tok_row[pos] = t;
-    slot_row[pos] = table[b] * P + (t - b * P);
+    if (kListLds) {
+      l_list[pos] = t;
+    } else {
+      const int b = div_p(t, a.pdiv);
+      tok_row[pos] = t;
+      slot_row[pos] = table[b] * P + (t - b * P);
+    }
   };
   for (int bb = b0; bb < b1; ++bb) {
     const int w = bb * 64 + lane;
     const uint64_t x = w < nwords ? bitmap[w] : 0ull;
     const int c = __popcll(x);
-    const int incl = wave_incl_scan(c, lane);
+    const int incl = stp::wave_incl_sum(c);
     int off = base + incl - c;
-    base += __shfl(incl, 63, 64);
+    base += __builtin_amdgcn_readlane(incl, 63);
     // sparse words: the owning lane walks its bits
     uint64_t bits = c < kDenseWord ? x : 0ull;
     while (bits) {
@@ -236,9 +248,36 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
       if (mine) emit((bb * 64 + src) * 64 + lane, woff + (int)below);
     }
   }
-  for (int j = total + tid; j < a.cap; j += kThreads) {
-    tok_row[j] = -1;
-    slot_row[j] = -1;
+  if (kListLds) {
+    __syncthreads();  // list complete
+    // one coalesced pass: tokens, slots and the -1 tail
+    for (int j0 = 0; j0 < a.cap; j0 += 4 * kThreads) {
+      int tv[4], sl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + tid + u * kThreads;
+        tv[u] = j < total ? l_list[j] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tv[u];
+        const int b = div_p(max(t, 0), a.pdiv);
+        sl[u] = t >= 0 ? table[b] * P + (t - b * P) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + tid + u * kThreads;
+        if (j < a.cap) {
+          tok_row[j] = tv[u];
+          slot_row[j] = sl[u];
+        }
+      }
+    }
+  } else {
+    for (int j = total + tid; j < a.cap; j += kThreads) {
+      tok_row[j] = -1;
+      slot_row[j] = -1;
+    }
   }
 
   // Number of touched logical blocks (for the CSR block view).
@@ -284,7 +323,14 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
   const int n = a.count_out[i];
   const int r = a.req_id[i];
   const int q = a.q_pos[i];
-
+  const int32_t* tok = a.tok_out + (int64_t)i * a.cap;
+  // the token's first 8 * 256 entries of S, loaded while the look-back runs
+  int tv[kDPerThread];
+#pragma unroll
+  for (int u = 0; u < kDPerThread; ++u) {
+    const int j = tid + u * kThreads;
+    tv[u] = j < n ? tok[j] : -1;
+  }
   __syncthreads();  // every thread has its `own` before thread 0 rewrites the entry
 
   // Look-back over tokens i-1, i-2, ...: raw counts until an inclusive prefix.
@@ -294,15 +340,13 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
     const int v = k >= 0 ? a.blk_indptr[k + 1] : -1;
     // the newest (largest k) inclusive prefix in this window, if any
     const int kp = (k >= 0 && v >= 0) ? k : -1;
-    int best = kp;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) best = max(best, __shfl_xor(best, d, 64));
+    // (an LDS atomic max over the workgroup)
     __syncthreads();
-    if ((tid & 63) == 0) s_red[tid >> 6] = best;
+    if (tid == 0) s_red[0] = -1;
     __syncthreads();
-    int kstar = -1;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) kstar = max(kstar, s_red[w]);
+    if (kp >= 0) atomicMax(&s_red[0], kp);
+    __syncthreads();
+    const int kstar = s_red[0];
     int contrib = 0;
     if (k >= 0 && k > kstar) contrib = -v - 1;  // raw count after the newest prefix
     if (k >= 0 && k == kstar) contrib = v;      // the prefix itself
@@ -321,33 +365,43 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
   const int nwords = (limit >> 6) + 1;
   const int used_blocks = div_p(limit, a.pdiv) + 1;
   const int32_t* table = a.block_table + (int64_t)r * a.max_blocks;
-  const int32_t* tok = a.tok_out + (int64_t)i * a.cap;
   for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
   __syncthreads();
-  for (int j = tid; j < n; j += kThreads) {
-    const int t = tok[j];
-    atomicOr((unsigned long long*)&bitmap[t >> 6], 1ull << (t & 63));
+  auto set_bits = [&](const int (&v)[kDPerThread]) {
+#pragma unroll
+    for (int u = 0; u < kDPerThread; ++u)
+      if (v[u] >= 0) atomicOr((unsigned long long*)&bitmap[v[u] >> 6], 1ull << (v[u] & 63));
+  };
+  set_bits(tv);
+  for (int j0 = kDPerThread * kThreads; j0 < n; j0 += kDPerThread * kThreads) {
+#pragma unroll
+    for (int u = 0; u < kDPerThread; ++u) {
+      const int j = j0 + tid + u * kThreads;
+      tv[u] = j < n ? tok[j] : -1;
+    }
+    set_bits(tv);
   }
   __syncthreads();
 
-  // Each thread owns a contiguous run of blocks.
-  const int bpt = (used_blocks + kThreads - 1) / kThreads;
-  const int c0 = min(used_blocks, tid * bpt), c1 = min(used_blocks, c0 + bpt);
-  int mine = 0;
-  for (int b = c0; b < c1; ++b) {
-    const int lo = b * P, hi = min(lo + P, limit + 1);
-    mine += bits_in_range(bitmap, lo, hi) != 0;
-  }
-  int tot;
-  int k = prefix + stp::block_exclusive_scan_256(mine, s_scan, &tot);
-  for (int b = c0; b < c1; ++b) {
-    const int lo = b * P, hi = min(lo + P, limit + 1);
-    const uint64_t m = bits_in_range(bitmap, lo, hi);
-    if (!m) continue;
-    a.blk_logical[k] = b;
-    a.blk_page[k] = table[b];
-    a.blk_mask[k] = m;
-    ++k;
+  // Blocks in chunks of 256, one per thread: in-page mask, page (its load in
+  // flight during the scan), position by a block-wide scan of the flags.
+  int k0 = prefix;
+  for (int c0 = 0; c0 < used_blocks; c0 += kThreads) {
+    const int b = c0 + tid;
+    uint64_t m = 0;
+    if (b < used_blocks) {
+      const int lo = b * P, hi = min(lo + P, limit + 1);
+      m = bits_in_range(bitmap, lo, hi);
+    }
+    const int page = m ? table[b] : 0;
+    int tot;
+    const int k = k0 + stp::block_exclusive_scan_256(m ? 1 : 0, s_scan, &tot);
+    if (m) {
+      a.blk_logical[k] = b;
+      a.blk_page[k] = page;
+      a.blk_mask[k] = m;
+    }
+    k0 += tot;
   }
 }
 
@@ -387,13 +441,21 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
   const int nwords = max(1, (int)(((int64_t)max_blocks * page_size + 63) / 64));
   const size_t bitmap_bytes = (size_t)nwords * sizeof(uint64_t);
   const bool table_in_lds = bitmap_bytes + (size_t)max_blocks * 4 <= (size_t)kLdsBudget;
-  const size_t lds = bitmap_bytes + (table_in_lds ? (size_t)max_blocks * 4 : 0);
+  size_t lds = bitmap_bytes + (table_in_lds ? (size_t)max_blocks * 4 : 0);
+  const bool list_in_lds = lds + (size_t)cap * 4 <= (size_t)kLdsBudget;
+  if (list_in_lds) lds += (size_t)cap * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)normalize_kernel<true>,
+    if (hipFuncSetAttribute((const void*)normalize_kernel<true, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
             hipSuccess ||
-        hipFuncSetAttribute((const void*)normalize_kernel<false>,
+        hipFuncSetAttribute((const void*)normalize_kernel<true, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<false, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<false, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
             hipSuccess ||
         hipFuncSetAttribute((const void*)block_fill_kernel,
@@ -405,10 +467,14 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
   NormArgs na{topk, req_id, q_pos, block_table, top_k, num_reqs, max_blocks, page_size, window,
               num_sinks, cap, nwords, pdiv, tok_out, slot_out, count_out,
               dropped_out, blk_indptr};
-  if (table_in_lds)
-    normalize_kernel<true><<<T, kThreads, lds, stream>>>(na);
+  if (table_in_lds && list_in_lds)
+    normalize_kernel<true, true><<<T, kThreads, lds, stream>>>(na);
+  else if (table_in_lds)
+    normalize_kernel<true, false><<<T, kThreads, lds, stream>>>(na);
+  else if (list_in_lds)
+    normalize_kernel<false, true><<<T, kThreads, lds, stream>>>(na);
   else
-    normalize_kernel<false><<<T, kThreads, lds, stream>>>(na);
+    normalize_kernel<false, false><<<T, kThreads, lds, stream>>>(na);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
   if (blk_indptr) {
     FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,

@@ -18,19 +18,32 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row moves
+// (no LDS round trips): shifts by 1, 2, 4, 8 inside each 16-lane row, then
+// the row totals broadcast forward (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Sum over the wave, in every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_sum(x), 63);
+}
+
 // Block-wide exclusive scan of one int per thread (blockDim.x == 256).
 // `scratch` holds at least 8 ints of LDS.  Returns the exclusive prefix and
 // writes the block total to *total.
 __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // inclusive scan inside the wave
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_incl_sum(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   int wave_off = 0, tot = 0;
