@@ -654,10 +654,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const uint32_t w0 = stp::f32_to_bf16_rne(o[hb][mb][4 * rq] * inv) |
-                            ((uint32_t)stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 1] * inv) << 16);
-        const uint32_t w1 = stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 2] * inv) |
-                            ((uint32_t)stp::f32_to_bf16_rne(o[hb][mb][4 * rq + 3] * inv) << 16);
+        const uint32_t w0 = stp::pack_bf16x2(o[hb][mb][4 * rq] * inv, o[hb][mb][4 * rq + 1] * inv);
+        const uint32_t w1 = stp::pack_bf16x2(o[hb][mb][4 * rq + 2] * inv, o[hb][mb][4 * rq + 3] * inv);
         *(__attribute__((address_space(3))) uintx2*)(hrow + (32 * mb + 8 * rq) * 2) =
             uintx2{w0, w1};
       }

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(
       acc.z += w * o.z;
       acc.w += w * o.w;
     }
-    const uint32_t lo = stp::f32_to_bf16_rne(acc.x * inv) | ((uint32_t)stp::f32_to_bf16_rne(acc.y * inv) << 16);
-    const uint32_t hi = stp::f32_to_bf16_rne(acc.z * inv) | ((uint32_t)stp::f32_to_bf16_rne(acc.w * inv) << 16);
+    const uint32_t lo = stp::pack_bf16x2(acc.x * inv, acc.y * inv);
+    const uint32_t hi = stp::pack_bf16x2(acc.z * inv, acc.w * inv);
     *(uint2*)(orow + c) = make_uint2(lo, hi);
   }
   if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
@@ -113,8 +113,8 @@ __device__ __forceinline__ void merge_norm_fixed(const uint16_t* __restrict__ o_
       acc.z += ws * __uint_as_float(raw[s].y << 16);
       acc.w += ws * __uint_as_float(raw[s].y & 0xffff0000u);
     }
-    const uint32_t lo = stp::f32_to_bf16_rne(acc.x) | ((uint32_t)stp::f32_to_bf16_rne(acc.y) << 16);
-    const uint32_t hi = stp::f32_to_bf16_rne(acc.z) | ((uint32_t)stp::f32_to_bf16_rne(acc.w) << 16);
+    const uint32_t lo = stp::pack_bf16x2(acc.x, acc.y);
+    const uint32_t hi = stp::pack_bf16x2(acc.z, acc.w);
     *(uint2*)(orow + c) = make_uint2(lo, hi);
   }
   if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_norm_kernel(
       acc.z += w * __uint_as_float(raw.y << 16);
       acc.w += w * __uint_as_float(raw.y & 0xffff0000u);
     }
-    const uint32_t lo = stp::f32_to_bf16_rne(acc.x) | ((uint32_t)stp::f32_to_bf16_rne(acc.y) << 16);
-    const uint32_t hi = stp::f32_to_bf16_rne(acc.z) | ((uint32_t)stp::f32_to_bf16_rne(acc.w) << 16);
+    const uint32_t lo = stp::pack_bf16x2(acc.x, acc.y);
+    const uint32_t hi = stp::pack_bf16x2(acc.z, acc.w);
     *(uint2*)(orow + c) = make_uint2(lo, hi);
   }
   if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);

@@ -58,11 +58,12 @@ __device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int
   return wave_off + x - v;
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+// Two fp32 values -> a packed bf16 pair (a in the low half), round to
+// nearest even, by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Split-KV merge launchers (merge.hip).  launch_merge takes un-normalised
