@@ -336,6 +336,30 @@ __device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next
   }
 }
 
+// bf16 output rows staged in the tile ring as [64 heads][512] (head stride
+// 1040 B, so the 32 heads of a staging store hit different banks).
+constexpr int kHeadStride = kDV * 2 + 16;
+
+// All four waves copy the staged rows out, one whole 1 KiB head row per
+// store instruction: the final output, or the split's normalised partial.
+template <int kMode>
+__device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeLds& L, int t,
+                                              int s, int hg, int tid) {
+#pragma unroll 4
+  for (int it = 0; it < 64 * 64 / kThreads; ++it) {
+    const int idx = it * kThreads + tid;    // 64 lanes per head row of 1 KiB
+    const int hl = idx >> 6, c = idx & 63;  // head, 16-byte chunk
+    const int head = hg * kHeadsPerWG + hl;
+    if (head >= a.H) continue;
+    const uintx4 v =
+        *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
+    uint16_t* orow = kMode == kOutFinal
+                         ? a.out + ((int64_t)t * a.H + head) * kDV
+                         : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+    *(uintx4*)(orow + c * 8) = v;
+  }
+}
+
 template <int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
@@ -494,7 +518,9 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       L.stat[2 * 64 + 32 * j + lane] = l_tot;
     }
     lds_barrier();  // statistics published
-    if (kMode != kOutPartialF32) lds_barrier();  // output rows staged by the output waves
+    if (kMode == kOutPartialF32) return;
+    lds_barrier();  // output rows staged by the output waves
+    copy_out_rows<kMode>(a, L, t, s, hg, tid);
     return;
   }
 
@@ -640,10 +666,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   }
 
   // bf16 o / l (the final output, or a normalised split partial), staged
-  // through the idle tile ring as [64 heads][512] rows (head stride 1040 B,
-  // so the 32 heads of a store hit different banks), then written back one
-  // whole 1 KiB head row per store instruction.
-  constexpr int kHeadStride = kDV * 2 + 16;
+  // through the idle tile ring, then written out by all four waves.
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int hl = 32 * hb + (lane & 31);
@@ -660,23 +683,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
             uintx2{w0, w1};
       }
   }
-  lds_barrier();  // output rows staged (the score waves take part before returning)
-  {
-    const int ot = tid - 128;  // 0..127: two output waves copy the 64 rows
-#pragma unroll 4
-    for (int it = 0; it < 64 * 64 / 128; ++it) {
-      const int idx = it * 128 + ot;          // 64 lanes per head row of 1 KiB
-      const int hl = idx >> 6, c = idx & 63;  // head, 16-byte chunk
-      const int head = hg * kHeadsPerWG + hl;
-      if (head >= a.H) continue;
-      const uintx4 v =
-          *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
-      uint16_t* orow = kMode == kOutFinal
-                           ? a.out + ((int64_t)t * a.H + head) * kDV
-                           : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
-      *(uintx4*)(orow + c * 8) = v;
-    }
-  }
+  lds_barrier();  // output rows staged
+  copy_out_rows<kMode>(a, L, t, s, hg, tid);
   if (lane < 32) {
     // lse / (m, l): output wave j covers heads 32 j .. 32 j + 31, one lane each
     const int hl = 32 * j + (lane & 31);
