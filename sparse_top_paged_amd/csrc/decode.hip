@@ -420,11 +420,16 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
 
   // candidate ids of this split, -1 for invalid ones and up to the tile edge
   const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
+  int bad = 0;
   for (int i = tid; i < ntiles * kTileRows; i += kThreads) {
     const int32_t id = i < len ? src_ids[i] : -1;
-    L.ids[i] = (id >= 0 && id < a.kv_rows) ? id : -1;
+    const bool valid = id >= 0 && id < a.kv_rows;
+    L.ids[i] = valid ? id : -1;
+    bad |= (i < len && !valid) ? 1 : 0;
   }
-  __syncthreads();  // ids visible (and, for the score waves, their query rows landed)
+  // ids visible; a split with an invalid id masks every tile, otherwise only
+  // its last tile (the rows past its end) needs a mask
+  const bool mask_all = __syncthreads_or(bad) != 0;
 
   // source of this lane's row of group grp of tile i (the zero row for an
   // invalid candidate)
@@ -472,6 +477,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     // the K fragment ring and the softmax.
     bf16x8 qf[kQKSteps];
     {
+      wait_vmcnt<0>();  // this wave's query rows
       const lds_t* qstage = L.tiles + (2 + j) * kTileBytes;
       shortx8 qv[kQKSteps];
 #pragma unroll
@@ -490,27 +496,40 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     if (ntiles > 0) qk_tile(L.tiles, k_base, qf, acc_a);
     // iteration i: softmax of tile i (S^T in registers) with the QK of tile
     // i+1; P(i) is published by the barrier B(i+1) that ends it.  Unrolled by
-    // two so that the accumulator sets swap roles without copies.
-    auto step = [&](int i, const SAcc& cur, SAcc& nxt) {
-      const uint32_t vm = tile_mask(i);
-      if (i + 1 < ntiles) {
-        const lds_t* next = L.tiles + ((i + 1) % kStages) * kTileBytes;
-        if (vm == ~0u)
-          score_step<true, false>(L, next, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j,
-                                  lane, st);
-        else
-          score_step<true, true>(L, next, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j, lane,
-                                 st);
-      } else {
-        score_step<false, true>(L, L.tiles, k_base, qf, cur, nxt, vm, a.scale_log2, i & 1, j,
-                                lane, st);
-      }
+    // two so that the accumulator sets swap roles without copies, with the
+    // last tile peeled off, so that the loop body holds one straight-line
+    // variant of the step (a branch between variants would let the compiler
+    // hoist their common softmax arithmetic out of the MFMA stream).
+    auto full = [&](auto masked, int i, const SAcc& cur, SAcc& nxt) {
+      constexpr bool kMasked = decltype(masked)::value;
+      score_step<true, kMasked>(L, L.tiles + ((i + 1) % kStages) * kTileBytes, k_base, qf, cur,
+                                nxt, kMasked ? tile_mask(i) : ~0u, a.scale_log2, i & 1, j, lane,
+                                st);
       lds_barrier();
     };
-    for (int i = 0; i < ntiles; i += 2) {
-      step(i, acc_a, acc_b);
-      if (i + 1 < ntiles) step(i + 1, acc_b, acc_a);
-    }
+    auto last = [&](int i, const SAcc& cur) {
+      SAcc none;
+      score_step<false, true>(L, L.tiles, k_base, qf, cur, none, tile_mask(i), a.scale_log2,
+                              i & 1, j, lane, st);
+      lds_barrier();
+    };
+    auto run = [&](auto masked) {
+      int i = 0;
+      for (; i + 2 < ntiles; i += 2) {
+        full(masked, i, acc_a, acc_b);
+        full(masked, i + 1, acc_b, acc_a);
+      }
+      if (ntiles - i == 2) {
+        full(masked, i, acc_a, acc_b);
+        last(i + 1, acc_b);
+      } else if (ntiles - i == 1) {
+        last(i, acc_a);
+      }
+    };
+    if (mask_all)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
     const float l_tot = pair_sum(st.lsum);
     if (lane < 32) {
       L.stat[0 * 64 + 32 * j + lane] = st.m_ref;
