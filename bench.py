@@ -19,7 +19,10 @@ when it comes round again.
 Prints one JSON line.  `value` is query tokens per second over the timed
 steps; `roofline` is the decode kernel's algorithmic bytes per launch over
 its average duration (HIP events on its stream, inside the timed region);
-`cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host.  The
+decode kernel is bracketed by events on every 7th step only: an event pair
+costs a few microseconds of queue time, which would otherwise be counted
+in every step.
 """
 
 import argparse
@@ -51,6 +54,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=8, help="candidate sets rotated step by step")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--event-every", type=int, default=7,
+                    help="bracket the decode kernel with HIP events on every n-th timed step "
+                         "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy of known size, so that rocprofv3 "
@@ -185,25 +191,29 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Event pairs cost a few microseconds of queue time each, so only every
+    # n-th step carries them (the step time is taken over all steps).
+    ev_every = max(1, args.event_every)
+    sampled = [i for i in range(args.steps) if i % ev_every == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, evs.get(i))
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
-    dec_us = np.asarray([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    merge_us = np.asarray([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    dec_us = np.asarray([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e3
+    merge_us = np.asarray([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e3
 
     # algorithmic bytes / flops of one decode launch (average over the rotated sets)
     q_bytes = T * H * 576 * 2
     o_bytes = T * H * (512 * 2 + 4)
     sel = np.asarray([cnt.sum() for cnt in counts], dtype=np.float64)  # sum of |S_i| per set
-    per_set_steps = np.bincount((args.warmup + np.arange(args.steps)) % args.sets,
+    per_set_steps = np.bincount((args.warmup + np.asarray(sampled)) % args.sets,
                                 minlength=args.sets)
     mean_sel = float((sel * per_set_steps).sum() / per_set_steps.sum())
     kv_bytes = mean_sel * ROW_BYTES
@@ -244,6 +254,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(dec_bytes),
             "avg_launch_us": round(float(dec_us.mean()), 3),
+            "launches_timed": len(sampled),
             "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
