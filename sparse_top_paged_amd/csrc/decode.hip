@@ -368,6 +368,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float s_alpha[2 * 64];
   __shared__ __attribute__((aligned(16))) float s_stat[3 * 64];
   __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
+  __shared__ int s_bad[2];
   const DecodeLds L{(lds_t*)s_tiles, (lds_t*)s_pbuf, s_alpha, s_stat, s_ids};
 
   const int tid = threadIdx.x;
@@ -375,6 +376,11 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   const int wave = tid >> 6;
   const bool score = wave < 2;
   const int j = wave & 1;
+  // the zero row's address, fetched once: inside the loops its GOT load (a
+  // scalar load, which only a full lgkmcnt(0) wait covers) would drain the
+  // LDS reads in flight
+  const uint8_t* zero_row = g_zero_row;
+  asm volatile("" : "+s"(zero_row));
 
   // XCD-aware task map: every workgroup of one token (all splits, all head
   // groups) gets a block id of the same residue mod 8, i.e. runs on the same
@@ -412,30 +418,38 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     for (int grp = 0; grp < 4; ++grp) {
       const int head = hg * kHeadsPerWG + 32 * j + grp * kGroupRows + (lane >> 3);
       const uint8_t* src =
-          (head < a.H ? (const uint8_t*)(a.q + ((int64_t)t * a.H + head) * kDQK) : g_zero_row) +
+          (head < a.H ? (const uint8_t*)(a.q + ((int64_t)t * a.H + head) * kDQK) : zero_row) +
           ld_col;
       load_row_chunks<0>(src, group_dst(2 + j, grp));
     }
   }
 
-  // candidate ids of this split, -1 for invalid ones and up to the tile edge
-  const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
-  int bad = 0;
-  for (int i = tid; i < ntiles * kTileRows; i += kThreads) {
-    const int32_t id = i < len ? src_ids[i] : -1;
-    const bool valid = id >= 0 && id < a.kv_rows;
-    L.ids[i] = valid ? id : -1;
-    bad |= (i < len && !valid) ? 1 : 0;
+  // candidate ids of this split, -1 for invalid ones and up to the tile edge;
+  // read by the output waves, whose load queue is empty here (the score
+  // waves' queue holds the query rows), and handed over with an LDS-only
+  // barrier so that nobody waits for the query rows yet
+  if (!score) {
+    const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
+    int bad = 0;
+    for (int i = tid - 128; i < ntiles * kTileRows; i += 128) {
+      const int32_t id = i < len ? src_ids[i] : -1;
+      const bool valid = id >= 0 && id < a.kv_rows;
+      L.ids[i] = valid ? id : -1;
+      bad |= (i < len && !valid) ? 1 : 0;
+    }
+    const int wbad = __ballot(bad) != 0 ? 1 : 0;
+    if (lane == 0) s_bad[j] = wbad;
   }
-  // ids visible; a split with an invalid id masks every tile, otherwise only
-  // its last tile (the rows past its end) needs a mask
-  const bool mask_all = __syncthreads_or(bad) != 0;
+  lds_barrier();
+  // a split with an invalid id masks every tile, otherwise only its last tile
+  // (the rows past its end) needs a mask
+  const bool mask_all = (s_bad[0] | s_bad[1]) != 0;
 
   // source of this lane's row of group grp of tile i (the zero row for an
   // invalid candidate)
   auto row_src = [&](int i, int grp) {
     const int id = L.ids[i * kTileRows + grp * kGroupRows + (lane >> 3)];
-    return (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : g_zero_row) + ld_col;
+    return (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : zero_row) + ld_col;
   };
   auto issue_group = [&](int i, int st, int grp) {
     load_row_chunks<0>(row_src(i, grp), group_dst(st, grp));
@@ -608,8 +622,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
         pf[hb][kap] = *(const __attribute__((address_space(3))) bf16x8*)(
             L.pbuf + ((buf * 2 + hb) * 2 + kap) * 1024 + lane * 16);
     const bool real = i + 3 < ntiles;
-    const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : g_zero_row + ld_col;
-    const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : g_zero_row + ld_col;
+    const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row + ld_col;
+    const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row + ld_col;
     const int st3 = (i + 3) % kStages;
     const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
     auto load_chunk = [&](auto c) {
