@@ -19,6 +19,9 @@ when it comes round again.
 Prints one JSON line.  `value` is query tokens per second over the timed
 steps; `roofline` is the decode kernel's algorithmic bytes per launch over
 its average duration (HIP events on its stream, inside the timed region);
+`ceilings` times, in the same run, the decode's row gather alone
+(stp_row_gather: the same rows, splits and XCD placement, no arithmetic) and
+a plain device copy, the practical ceilings the decode's rate is set against;
 `cpu_baseline` times the fp64 oracle on a bounded sample on the host.  The
 decode kernel is bracketed by events on every 7th step only: an event pair
 costs a few microseconds of queue time, which would otherwise be counted
@@ -123,6 +126,47 @@ def cpu_baseline(cases, kv, budget_s):
     }
 
 
+def median_us(fn, n, sets):
+    """Median duration of fn(k) over n launches (HIP events on the current stream)."""
+    import torch
+    for k in range(8):
+        fn(k % sets)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for k in range(n):
+        evs[k][0].record()
+        fn(k % sets)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+
+def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
+    """Practical ceilings measured in the same run: the decode's row gather with
+    nothing else (the rows of each candidate set read once per head group, as
+    the decode reads them, and read once in all), and a plain device copy."""
+    import torch
+    T = norm[0]["slot"].shape[0]
+    rows = kv.view(torch.uint8).view(kv.shape[0], -1)
+    kv_bytes = [int(nb["count"].sum().item()) * ROW_BYTES for nb in norm]
+    mean_kv = float(np.mean(kv_bytes))
+    out = {}
+    for name, parts, reps in [("row_gather_decode_placement", splits, head_groups),
+                              ("row_gather_each_row_once", splits * head_groups, 1)]:
+        cs = torch.empty((stp._lib.lib.stp_row_gather_blocks(T, parts, reps),), dtype=torch.int32,
+                         device=kv.device)
+        us = median_us(lambda k: stp.row_gather(rows, norm[k]["slot"], norm[k]["count"], parts,
+                                                reps, checksum=cs), n, sets)
+        out[name] = {"us": round(us, 3), "kv_gbs": round(mean_kv / us / 1e3, 1),
+                     "parts": parts, "replicas": reps}
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=kv.device)
+    dst = torch.empty_like(src)
+    us = median_us(lambda k: dst.copy_(src), 20, 1)
+    out["device_copy_256MiB"] = {"us": round(us, 3), "gbs": round(2 * COPY_CAL_BYTES / us / 1e3, 1)}
+    del src, dst
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -209,6 +253,8 @@ def main():
     dec_us = np.asarray([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e3
     merge_us = np.asarray([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e3
 
+    ceilings = measure_ceilings(stp, kv, norm, args.sets, S, (H + 63) // 64)
+
     # algorithmic bytes / flops of one decode launch (average over the rotated sets)
     q_bytes = T * H * 576 * 2
     o_bytes = T * H * (512 * 2 + 4)
@@ -258,6 +304,14 @@ def main():
             "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
+        "ceilings": ceilings,
+        "decode_vs_ceilings": {
+            "kv_gbs": round(kv_bytes / dec_avg_s / 1e9, 1),
+            "frac_of_row_gather_decode_placement":
+                round(ceilings["row_gather_decode_placement"]["us"] / (dec_avg_s * 1e6), 4),
+            "frac_of_row_gather_each_row_once":
+                round(ceilings["row_gather_each_row_once"]["us"] / (dec_avg_s * 1e6), 4),
+        },
         "kernel_us": {
             "decode_median": round(float(np.median(dec_us)), 3),
             "decode_p95": round(float(np.percentile(dec_us, 95)), 3),

@@ -17,7 +17,7 @@ __all__ = [
     "StpError", "version", "normalize_indices", "hot_lookup_swapin", "hot_reset", "backup_rows",
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
-    "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer",
+    "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
 ]
 
 
@@ -274,3 +274,23 @@ def splitkv_merge_normalized(o_norm, m_part, l_part, out=None, lse=None):
         _dev(l_part, "l_part", torch.float32, dev), T, S, H, dv,
         _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
     return out, lse
+
+
+def row_gather(rows, row_ids, counts=None, parts=1, replicas=1, checksum=None):
+    """Diagnostic: read the candidate rows exactly as the decode splits and
+    places them, computing only an xor per workgroup.  rows: uint8
+    [num_rows, row_bytes] (or any 2-D contiguous tensor, taken as bytes);
+    row_ids [T, cap] int32.  Returns the uint32 checksums (as int32)."""
+    dev = rows.device
+    if rows.dim() != 2 or not rows.is_contiguous() or not rows.is_cuda:
+        raise ValueError("rows must be a contiguous 2-D device tensor")
+    T, cap = row_ids.shape
+    row_bytes = rows.shape[1] * rows.element_size()
+    nblk = lib.stp_row_gather_blocks(T, parts, replicas)
+    if checksum is None:
+        checksum = torch.empty((max(1, nblk),), dtype=torch.int32, device=dev)
+    check(lib.stp_row_gather(
+        rows.data_ptr(), rows.shape[0], row_bytes, _dev(row_ids, "row_ids", torch.int32, dev),
+        _opt(counts, "counts", torch.int32, dev), cap, T, parts, replicas,
+        _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
+    return checksum

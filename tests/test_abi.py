@@ -72,6 +72,12 @@ def test_host_side_validation():
     assert stp.decode_workspace_bytes(1, 16, 44) == 0          # tiny shape runs unsplit
     assert stp.hot_lds_bytes(2180, 4096) > 0
     assert stp.hot_lds_bytes(40000, 32767) == 0
+    # row-gather diagnostic: row size must be a multiple of 16, ranges must fit its id list
+    assert lib.stp_row_gather(fake, 10, 1000, fake, None, 8, 1, 1, 1, fake, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_row_gather(fake, 10, 1152, fake, None, 8200, 1, 2, 1, fake, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_row_gather(fake, 10, 1152, fake, None, 8, 0, 1, 1, fake, None) == 0  # T = 0
+    assert lib.stp_row_gather_blocks(32, 4, 2) == 256
+    assert lib.stp_row_gather_blocks(33, 8, 1) == 320
 
 
 def test_missing_library_fails_loudly(tmp_path):
