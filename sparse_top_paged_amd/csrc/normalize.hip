@@ -33,12 +33,18 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxPositions = 1 << 20;     // bitmap of 128 KiB LDS
 constexpr int kLdsBudget = 150 * 1024;     // dynamic LDS a workgroup may use
-constexpr int kDPerThread = 8;             // D entries in flight per thread
 constexpr int kDenseWord = 8;              // words with more bits go wave-wide
+#ifndef STP_NORM_THREADS
+#define STP_NORM_THREADS 1024
+#endif
+constexpr int kNThreads = STP_NORM_THREADS;  // normalize_kernel's workgroup
+constexpr int kNWaves = kNThreads / 64;
+constexpr int kNDPer = kNThreads >= 1024 ? 2 : (kNThreads >= 512 ? 4 : 8);  // D entries per thread
+constexpr int kFThreads = 1024;            // block_fill_kernel's workgroup
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFDPer = 2;                  // entries of S per thread in flight
 
 struct NormArgs {
   const int32_t* topk;
@@ -69,6 +75,7 @@ __device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, in
   return n == 64 ? acc : (acc & ((1ull << n) - 1));
 }
 
+template <int kW>
 __device__ __forceinline__ int block_sum(int v, int* scratch) {
   v = stp::wave_sum(v);
   __syncthreads();
@@ -76,27 +83,27 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
   __syncthreads();
   int s = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += scratch[w];
+  for (int w = 0; w < kW; ++w) s += scratch[w];
   return s;
 }
 
 // LDS of normalize_kernel: the bitmap (nwords_alloc words), then the
 // request's page-table row (kTableLds), then the emitted list S (kListLds).
 template <bool kTableLds, bool kListLds>
-__global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
+__global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
   extern __shared__ uint64_t bitmap[];
-  __shared__ int s_red[kWaves];
-  __shared__ int s_wave_total[kWaves];
+  __shared__ int s_red[kNWaves];
+  __shared__ int s_wave_total[kNWaves];
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // D first: independent of the request, so its loads overlap the rest.
   const int32_t* drow = a.topk + (int64_t)i * a.top_k;
-  int dv[kDPerThread];
+  int dv[kNDPer];
 #pragma unroll
-  for (int u = 0; u < kDPerThread; ++u) {
-    const int j = tid + u * kThreads;
+  for (int u = 0; u < kNDPer; ++u) {
+    const int j = tid + u * kNThreads;
     dv[u] = j < a.top_k ? drow[j] : -1;
   }
   const int r = a.req_id[i];
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   int32_t* slot_row = a.slot_out + (int64_t)i * a.cap;
 
   if (r < 0 || r >= a.num_reqs || q < 0) {  // padding row (uniform branch)
-    for (int j = tid; j < a.cap; j += kThreads) {
+    for (int j = tid; j < a.cap; j += kNThreads) {
       tok_row[j] = -1;
       slot_row[j] = -1;
     }
@@ -126,21 +133,21 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   int32_t* l_list = l_table + (kTableLds ? a.max_blocks : 0);
   if (kTableLds) {
     // all of a thread's table loads in flight before its stores
-    for (int b0 = 0; b0 < used_blocks; b0 += 4 * kThreads) {
+    for (int b0 = 0; b0 < used_blocks; b0 += 4 * kNThreads) {
       int tv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int b = b0 + tid + u * kThreads;
+        const int b = b0 + tid + u * kNThreads;
         tv[u] = b < used_blocks ? g_table[b] : -1;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int b = b0 + tid + u * kThreads;
+        const int b = b0 + tid + u * kNThreads;
         if (b < used_blocks) l_table[b] = tv[u];
       }
     }
   }
-  for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
+  for (int w = tid; w < nwords; w += kNThreads) bitmap[w] = 0;
   __syncthreads();
   const int32_t* table = kTableLds ? l_table : g_table;
 
@@ -149,15 +156,15 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   };
   // D entries: every table read first, then branch-free visibility.
   int my_dropped = 0;
-  auto add_d = [&](const int (&tv)[kDPerThread]) {
-    int pg[kDPerThread];
+  auto add_d = [&](const int (&tv)[kNDPer]) {
+    int pg[kNDPer];
 #pragma unroll
-    for (int u = 0; u < kDPerThread; ++u) {
+    for (int u = 0; u < kNDPer; ++u) {
       const int tc = min(max(tv[u], 0), limit);  // in-range stand-in for the read
       pg[u] = table[div_p(tc, a.pdiv)];
     }
 #pragma unroll
-    for (int u = 0; u < kDPerThread; ++u) {
+    for (int u = 0; u < kNDPer; ++u) {
       const int t = tv[u];
       const int b = div_p(max(t, 0), a.pdiv);
       const bool ok = t >= 0 && t <= limit && pg[u] >= 0 &&
@@ -167,10 +174,10 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
     }
   };
   add_d(dv);
-  for (int j0 = kDPerThread * kThreads; j0 < a.top_k; j0 += kDPerThread * kThreads) {
+  for (int j0 = kNDPer * kNThreads; j0 < a.top_k; j0 += kNDPer * kNThreads) {
 #pragma unroll
-    for (int u = 0; u < kDPerThread; ++u) {
-      const int j = j0 + tid + u * kThreads;
+    for (int u = 0; u < kNDPer; ++u) {
+      const int j = j0 + tid + u * kNThreads;
       dv[u] = j < a.top_k ? drow[j] : -1;
     }
     add_d(dv);
@@ -182,17 +189,17 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   };
   // W: the local window ending at the query's own position.
   if (a.window > 0)
-    for (int t = max(0, q - a.window + 1) + tid; t <= q; t += kThreads)
+    for (int t = max(0, q - a.window + 1) + tid; t <= q; t += kNThreads)
       if (t <= limit && visible(t)) set_bit(t);
   // A: the sink positions.
   const int na = min(a.num_sinks, q + 1);
-  for (int t = tid; t < na; t += kThreads)
+  for (int t = tid; t < na; t += kNThreads)
     if (t <= limit && visible(t)) set_bit(t);
-  const int dropped = block_sum(my_dropped, s_red);  // (its barriers publish the bitmap)
+  const int dropped = block_sum<kNWaves>(my_dropped, s_red);  // (its barriers publish the bitmap)
 
   // Each wave owns a contiguous run of 64-word batches.
   const int nbatch = (nwords + 63) >> 6;
-  const int bpw = (nbatch + kWaves - 1) / kWaves;
+  const int bpw = (nbatch + kNWaves - 1) / kNWaves;
   const int b0 = min(nbatch, wave * bpw), b1 = min(nbatch, b0 + bpw);
   int cnt = 0;
   for (int bb = b0; bb < b1; ++bb) {
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   __syncthreads();
   int base = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < kNWaves; ++w) {
     const int sw = s_wave_total[w];
     base += w < wave ? sw : 0;
     total += sw;
@@ -251,11 +258,11 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   if (kListLds) {
     __syncthreads();  // list complete
     // one coalesced pass: tokens, slots and the -1 tail
-    for (int j0 = 0; j0 < a.cap; j0 += 4 * kThreads) {
+    for (int j0 = 0; j0 < a.cap; j0 += 4 * kNThreads) {
       int tv[4], sl[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int j = j0 + tid + u * kThreads;
+        const int j = j0 + tid + u * kNThreads;
         tv[u] = j < total ? l_list[j] : -1;
       }
 #pragma unroll
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int j = j0 + tid + u * kThreads;
+        const int j = j0 + tid + u * kNThreads;
         if (j < a.cap) {
           tok_row[j] = tv[u];
           slot_row[j] = sl[u];
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
       }
     }
   } else {
-    for (int j = total + tid; j < a.cap; j += kThreads) {
+    for (int j = total + tid; j < a.cap; j += kNThreads) {
       tok_row[j] = -1;
       slot_row[j] = -1;
     }
@@ -283,11 +290,11 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(NormArgs a) {
   // Number of touched logical blocks (for the CSR block view).
   int nb = 0;
   if (a.blk_indptr) {
-    for (int b = tid; b < used_blocks; b += kThreads) {
+    for (int b = tid; b < used_blocks; b += kNThreads) {
       const int lo = b * P, hi = min(lo + P, limit + 1);
       if (bits_in_range(bitmap, lo, hi)) ++nb;
     }
-    nb = block_sum(nb, s_red);
+    nb = block_sum<kNWaves>(nb, s_red);
   }
   if (tid == 0) {
     a.count_out[i] = total;
@@ -304,18 +311,41 @@ struct FillArgs {
   const int32_t* block_table;
   int num_reqs, max_blocks, P, cap;
   uint64_t pdiv;
+  int nwords_alloc;  // bitmap words; the staged table row follows them in LDS
   int32_t* blk_indptr;
   int32_t* blk_logical;
   int32_t* blk_page;
   uint64_t* blk_mask;
 };
 
+// Block-wide exclusive scan of one int per thread over kW waves; `scratch`
+// holds kW ints.  Returns the exclusive prefix and writes the total.
+template <int kW>
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = stp::wave_incl_sum(v);
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int sw = scratch[w];
+    off += w < wave ? sw : 0;
+    tot += sw;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
+}
+
 // Per token: CSR offset by look-back, then the touched blocks from a bitmap
-// rebuilt out of the token's sorted S.
-__global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
+// rebuilt out of the token's sorted S.  The request's page-table row is
+// staged in LDS (after the bitmap) while the look-back runs, when it fits.
+template <bool kTableLds>
+__global__ __launch_bounds__(kFThreads) void block_fill_kernel(FillArgs a) {
   extern __shared__ uint64_t bitmap[];
-  __shared__ int s_red[kWaves];
-  __shared__ int s_scan[kWaves];
+  __shared__ int s_red[kFWaves];
+  __shared__ int s_scan[kFWaves];
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
 
@@ -323,21 +353,48 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
   const int n = a.count_out[i];
   const int r = a.req_id[i];
   const int q = a.q_pos[i];
+  const bool pad = r < 0 || r >= a.num_reqs || q < 0;
   const int32_t* tok = a.tok_out + (int64_t)i * a.cap;
-  // the token's first 8 * 256 entries of S, loaded while the look-back runs
-  int tv[kDPerThread];
+  // the token's first entries of S and its table row, loaded while the
+  // look-back runs
+  int tv[kFDPer];
 #pragma unroll
-  for (int u = 0; u < kDPerThread; ++u) {
-    const int j = tid + u * kThreads;
+  for (int u = 0; u < kFDPer; ++u) {
+    const int j = tid + u * kFThreads;
     tv[u] = j < n ? tok[j] : -1;
+  }
+  const int P = a.P;
+  const int limit = pad ? 0 : min(q, a.max_blocks * P - 1);
+  const int nwords = (limit >> 6) + 1;
+  const int used_blocks = div_p(limit, a.pdiv) + 1;
+  const int32_t* g_table = a.block_table + (int64_t)(pad ? 0 : r) * a.max_blocks;
+  int32_t* l_table = (int32_t*)(bitmap + a.nwords_alloc);
+  // the first look-back window's entries (tokens i-1 .. i-kFThreads; never
+  // this token's own entry), in flight with the loads above
+  const int k_first = i - 1 - tid;
+  const int v_first = k_first >= 0 ? a.blk_indptr[k_first + 1] : -1;
+  if (kTableLds && !pad && own > 0) {
+    for (int b0 = 0; b0 < used_blocks; b0 += 2 * kFThreads) {
+      int pv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = b0 + tid + u * kFThreads;
+        pv[u] = b < used_blocks ? g_table[b] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = b0 + tid + u * kFThreads;
+        if (b < used_blocks) l_table[b] = pv[u];
+      }
+    }
   }
   __syncthreads();  // every thread has its `own` before thread 0 rewrites the entry
 
   // Look-back over tokens i-1, i-2, ...: raw counts until an inclusive prefix.
   int prefix = 0;
-  for (int hi = i; hi > 0; hi -= kThreads) {
+  for (int hi = i; hi > 0; hi -= kFThreads) {
     const int k = hi - 1 - tid;  // token index this thread reads
-    const int v = k >= 0 ? a.blk_indptr[k + 1] : -1;
+    const int v = hi == i ? v_first : (k >= 0 ? a.blk_indptr[k + 1] : -1);
     // the newest (largest k) inclusive prefix in this window, if any
     const int kp = (k >= 0 && v >= 0) ? k : -1;
     // (an LDS atomic max over the workgroup)
@@ -350,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
     int contrib = 0;
     if (k >= 0 && k > kstar) contrib = -v - 1;  // raw count after the newest prefix
     if (k >= 0 && k == kstar) contrib = v;      // the prefix itself
-    prefix += block_sum(contrib, s_red);
+    prefix += block_sum<kFWaves>(contrib, s_red);
     if (kstar >= 0) break;
   }
 
@@ -358,35 +415,31 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
     if (i == 0) a.blk_indptr[0] = 0;
     a.blk_indptr[i + 1] = prefix + own;
   }
-  if (own == 0 || r < 0 || r >= a.num_reqs || q < 0) return;
+  if (own == 0 || pad) return;
 
-  const int P = a.P;
-  const int limit = min(q, a.max_blocks * P - 1);
-  const int nwords = (limit >> 6) + 1;
-  const int used_blocks = div_p(limit, a.pdiv) + 1;
-  const int32_t* table = a.block_table + (int64_t)r * a.max_blocks;
-  for (int w = tid; w < nwords; w += kThreads) bitmap[w] = 0;
+  const int32_t* table = kTableLds ? l_table : g_table;
+  for (int w = tid; w < nwords; w += kFThreads) bitmap[w] = 0;
   __syncthreads();
-  auto set_bits = [&](const int (&v)[kDPerThread]) {
+  auto set_bits = [&](const int (&v)[kFDPer]) {
 #pragma unroll
-    for (int u = 0; u < kDPerThread; ++u)
+    for (int u = 0; u < kFDPer; ++u)
       if (v[u] >= 0) atomicOr((unsigned long long*)&bitmap[v[u] >> 6], 1ull << (v[u] & 63));
   };
   set_bits(tv);
-  for (int j0 = kDPerThread * kThreads; j0 < n; j0 += kDPerThread * kThreads) {
+  for (int j0 = kFDPer * kFThreads; j0 < n; j0 += kFDPer * kFThreads) {
 #pragma unroll
-    for (int u = 0; u < kDPerThread; ++u) {
-      const int j = j0 + tid + u * kThreads;
+    for (int u = 0; u < kFDPer; ++u) {
+      const int j = j0 + tid + u * kFThreads;
       tv[u] = j < n ? tok[j] : -1;
     }
     set_bits(tv);
   }
   __syncthreads();
 
-  // Blocks in chunks of 256, one per thread: in-page mask, page (its load in
-  // flight during the scan), position by a block-wide scan of the flags.
+  // Blocks in chunks of kFThreads, one per thread: in-page mask, page,
+  // position by a block-wide scan of the flags.
   int k0 = prefix;
-  for (int c0 = 0; c0 < used_blocks; c0 += kThreads) {
+  for (int c0 = 0; c0 < used_blocks; c0 += kFThreads) {
     const int b = c0 + tid;
     uint64_t m = 0;
     if (b < used_blocks) {
@@ -395,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void block_fill_kernel(FillArgs a) {
     }
     const int page = m ? table[b] : 0;
     int tot;
-    const int k = k0 + stp::block_exclusive_scan_256(m ? 1 : 0, s_scan, &tot);
+    const int k = k0 + block_excl_scan<kFWaves>(m ? 1 : 0, s_scan, &tot);
     if (m) {
       a.blk_logical[k] = b;
       a.blk_page[k] = page;
@@ -458,7 +511,9 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
         hipFuncSetAttribute((const void*)normalize_kernel<false, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
             hipSuccess ||
-        hipFuncSetAttribute((const void*)block_fill_kernel,
+        hipFuncSetAttribute((const void*)block_fill_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess ||
+        hipFuncSetAttribute((const void*)block_fill_kernel<false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess)
       return fail(STP_ERR_HIP, "normalize_indices: hipFuncSetAttribute failed");
     attr_set = true;
@@ -468,18 +523,21 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
               num_sinks, cap, nwords, pdiv, tok_out, slot_out, count_out,
               dropped_out, blk_indptr};
   if (table_in_lds && list_in_lds)
-    normalize_kernel<true, true><<<T, kThreads, lds, stream>>>(na);
+    normalize_kernel<true, true><<<T, kNThreads, lds, stream>>>(na);
   else if (table_in_lds)
-    normalize_kernel<true, false><<<T, kThreads, lds, stream>>>(na);
+    normalize_kernel<true, false><<<T, kNThreads, lds, stream>>>(na);
   else if (list_in_lds)
-    normalize_kernel<false, true><<<T, kThreads, lds, stream>>>(na);
+    normalize_kernel<false, true><<<T, kNThreads, lds, stream>>>(na);
   else
-    normalize_kernel<false, false><<<T, kThreads, lds, stream>>>(na);
+    normalize_kernel<false, false><<<T, kNThreads, lds, stream>>>(na);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
   if (blk_indptr) {
     FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,
-                cap, pdiv, blk_indptr, blk_logical, blk_page, blk_mask};
-    block_fill_kernel<<<T, kThreads, bitmap_bytes, stream>>>(fa);
+                cap, pdiv, nwords, blk_indptr, blk_logical, blk_page, blk_mask};
+    if (table_in_lds)
+      block_fill_kernel<true><<<T, kFThreads, bitmap_bytes + (size_t)max_blocks * 4, stream>>>(fa);
+    else
+      block_fill_kernel<false><<<T, kFThreads, bitmap_bytes, stream>>>(fa);
     if (int rc = stp::check_launch("block_fill_kernel")) return rc;
   }
   return STP_OK;
