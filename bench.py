@@ -61,6 +61,8 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the row-gather and device-copy ceiling measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy of known size, so that rocprofv3 "
                          "counter runs can scale FETCH_SIZE / WRITE_SIZE")
@@ -253,7 +255,8 @@ def main():
     dec_us = np.asarray([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e3
     merge_us = np.asarray([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e3
 
-    ceilings = measure_ceilings(stp, kv, norm, args.sets, S, (H + 63) // 64)
+    ceilings = None if args.no_ceilings else measure_ceilings(stp, kv, norm, args.sets, S,
+                                                              (H + 63) // 64)
 
     # algorithmic bytes / flops of one decode launch (average over the rotated sets)
     q_bytes = T * H * 576 * 2
@@ -305,7 +308,7 @@ def main():
         },
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
         "ceilings": ceilings,
-        "decode_vs_ceilings": {
+        "decode_vs_ceilings": None if ceilings is None else {
             "kv_gbs": round(kv_bytes / dec_avg_s / 1e9, 1),
             "frac_of_row_gather_decode_placement":
                 round(ceilings["row_gather_decode_placement"]["us"] / (dec_avg_s * 1e6), 4),

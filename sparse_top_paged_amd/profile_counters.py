@@ -4,6 +4,13 @@ benchmark (run by path, on any host; it reads CSV files only).
     python sparse_top_paged_amd/profile_counters.py stats <kernel_stats.csv> <out.txt> "<command>"
     python sparse_top_paged_amd/profile_counters.py traffic <fetch counter_collection.csv> \\
         <write counter_collection.csv> <kernel source> <out.json> "<command>"
+    python sparse_top_paged_amd/profile_counters.py counters <out.txt> "<command>" \\
+        <counter_collection.csv> [<counter_collection.csv> ...]
+
+`counters` averages every counter per dispatch for the decode kernel and the
+row-gather diagnostic (whose launches come in two runs of equal length: the
+decode's placement first, then each row read once) and derives the figures
+quoted beside the benchmark.
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
 counters read for the benchmark's calibration copy (a 256 MiB device-to-device
@@ -97,10 +104,56 @@ def traffic(fetch_csv, write_csv, kernel_src, out, command):
     open(out, "a").write("\n")
 
 
+def counters(out, command, *paths):
+    """Per-dispatch means of every collected counter, per kernel of interest."""
+    groups = defaultdict(lambda: defaultdict(dict))  # kernel -> dispatch -> counter -> value
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if DECODE_KERNEL in k:
+                k = "sparse_mla_decode_kernel"
+            elif "row_gather_kernel" not in k:
+                continue
+            d = groups[k][(path, int(r["Dispatch_Id"]))]
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    split = {}
+    for k, disp in groups.items():
+        if k == "row_gather_kernel":
+            for path in paths:
+                ids = sorted(i for (p, i) in disp if p == path)
+                half = len(ids) // 2
+                for n, sel in (("row_gather (decode placement)", ids[:half]),
+                               ("row_gather (each row once)", ids[half:])):
+                    split.setdefault(n, {}).update({(path, i): disp[(path, i)] for i in sel})
+        else:
+            split[k] = disp
+    lines = ["# rocprofv3 hardware counters, mean per dispatch", f"# command: {command}", "#"]
+    for k, disp in split.items():
+        names = sorted({c for d in disp.values() for c in d})
+        lines.append(f"{k}  ({len(disp)} dispatches across the passes)")
+        for c in names:
+            vals = [d[c] for d in disp.values() if c in d]
+            lines.append(f"  {c:<40} {sum(vals) / len(vals):>16.1f}")
+        m = {c: sum(d[c] for d in disp.values() if c in d) / max(1, sum(1 for d in disp.values() if c in d))
+             for c in names}
+        if "TCP_TCC_READ_REQ_sum" in m and m["TCP_TCC_READ_REQ_sum"]:
+            lines.append(f"  -> mean L2 round trip seen by the L1 (cycles)  "
+                         f"{m.get('TCP_TCC_READ_REQ_LATENCY_sum', 0) / m['TCP_TCC_READ_REQ_sum']:.0f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            lines.append(f"  -> bf16 MFMA work (GFLOP, 512 flop per MOP)     "
+                         f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f}")
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and (m["TCC_HIT_sum"] + m["TCC_MISS_sum"]):
+            lines.append(f"  -> L2 hit rate                                 "
+                         f"{m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(*sys.argv[2:5])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
+    elif sys.argv[1] == "counters":
+        counters(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
