@@ -61,6 +61,11 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["deepseek", "hot"], default="deepseek",
+                    help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
+                         "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
+                         "pinned host memory), reported on its own line")
+    ap.add_argument("--passes", type=int, default=6, help="hot workload: timed 16-step passes")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the row-gather and device-copy ceiling measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -169,12 +174,149 @@ def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     return out
 
 
+def bench_hot(args):
+    """The HiSparse hot-buffer decode: 64 requests, context 65536 + t, 16
+    steps whose top-k keeps 85% of the previous set, the whole latent pool
+    (4.8 GB) in pinned host memory, a 4096-row hot region per request.  One
+    step = the new KV row into its reserved hot row -> normalise -> lookup /
+    LRU / swap-in from host memory -> decode over the hot cache (split path)
+    -> back-up of the new rows.  Each pass starts cold (state reset), so step
+    0 swaps in every candidate row; steps 1-15 are the warm steps."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = workloads.hot_steps_case()
+    B, Hs, stride, P, heads = c.batch, c.hot_size, c.region_stride, c.page_size, c.heads
+    pool = workloads.pool_torch(c.host_rows, c.pool_seed, dev)
+    host = torch.empty((c.host_rows, ROW_BYTES), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pool.view(torch.uint8))
+    del pool
+    torch.cuda.empty_cache()
+    host_ptr = stp.host_device_pointer(host)
+    hot = torch.zeros((B * stride, ROW_BYTES), dtype=torch.uint8, device=dev)
+    kv = hot.view(torch.bfloat16).view(-1, 576)
+    dgi = torch.empty((B, Hs), dtype=torch.int32, device=dev)
+    lru = torch.empty((B, Hs), dtype=torch.int16, device=dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    table, req = t(c.block_table), t(np.arange(B, dtype=np.int32))
+    topk = [t(c.topk[s]) for s in range(c.steps)]
+    qpos = [t(c.q_pos(s)) for s in range(c.steps)]
+    newest = [t(np.asarray([c.block_table[r][c.q_pos(s)[r] // P] * P + c.q_pos(s)[r] % P
+                            for r in range(B)], np.int32)) for s in range(c.steps)]
+    q = [t(c.q_bits[s].view(np.int16)).view(torch.bfloat16) for s in range(c.steps)]
+    rng = np.random.default_rng(7)
+    new_rows = t(workloads.normal_bf16(rng, (c.steps, B, 576)).view(np.uint8)
+                 .reshape(c.steps, B, ROW_BYTES))
+    reserved = torch.arange(B, device=dev, dtype=torch.int64) * stride + Hs
+    src32 = reserved.to(torch.int32)
+    S = stp.decode_splits(B, heads, c.cap)
+    ws = torch.empty((max(1, stp.decode_workspace_bytes(B, heads, c.cap)),), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, heads), dtype=torch.float32, device=dev)
+    norm = stp.normalize_indices(topk[0], req, qpos[0], table, P, c.window, c.num_sinks, c.cap,
+                                 block_view=False)
+    rows = torch.empty((B, c.cap), dtype=torch.int32, device=dev)
+    miss = torch.empty((B, c.cap), dtype=torch.uint8, device=dev)
+    stats = torch.zeros((c.steps, 2), dtype=torch.int64, device=dev)
+
+    def run_pass(evs=None):
+        stp.hot_reset(dgi, lru)
+        stats.zero_()
+        for s in range(c.steps):
+            e = evs[s] if evs else None
+            if e:
+                e[0].record()
+            hot.index_copy_(0, reserved, new_rows[s])
+            stp.normalize_indices(topk[s], req, qpos[s], table, P, c.window, c.num_sinks, c.cap,
+                                  block_view=False, out=norm)
+            if e:
+                e[1].record()
+            stp.hot_lookup_swapin(host, hot, norm["slot"], newest[s], dgi, lru, stride,
+                                  hot_rows_out=rows, miss_mask=miss, stats=stats[s],
+                                  host_pool_ptr=host_ptr)
+            if e:
+                e[2].record()
+            stp.sparse_mla_decode(q[s], kv, rows, norm["count"], 576 ** -0.5, S, workspace=ws,
+                                  out=out, lse=lse)
+            if e:
+                e[3].record()
+            stp.backup_rows(hot, host, src32, newest[s], host_pool_ptr=host_ptr)
+            if e:
+                e[4].record()
+
+    run_pass()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    per_step = []  # (total, normalise, lookup+swap-in, decode, back-up) in us, per pass and step
+    st_all = []
+    for _ in range(args.passes):
+        evs = [[ev() for _ in range(5)] for _ in range(c.steps)]
+        run_pass(evs)
+        torch.cuda.synchronize()
+        per_step.append([[evs[s][0].elapsed_time(evs[s][4]) * 1e3] +
+                         [evs[s][k].elapsed_time(evs[s][k + 1]) * 1e3 for k in range(4)]
+                         for s in range(c.steps)])
+        st_all.append(stats.cpu().numpy().copy())
+    a = np.asarray(per_step)         # [passes, steps, 5]
+    st = np.asarray(st_all)          # [passes, steps, 2]
+    warm = a[:, 1:, :].reshape(-1, 5)
+    hits, misses = st[:, 1:, 0].sum(), st[:, 1:, 1].sum()
+    miss_per_step = misses / (args.passes * (c.steps - 1))
+    swap_us = float(np.median(warm[:, 2]))
+    cold_swap_us = float(np.median(a[:, 0, 2]))
+    cold_misses = float(st[:, 0, 1].mean())
+    # host link ceiling in the same run: pinned host -> device copies of 64 MiB
+    link = torch.empty((64 << 20,), dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+    h2d_us = median_us(lambda k: dst.copy_(link, non_blocking=True), 20, 1)
+    step_us = float(np.median(warm[:, 0]))
+    res = {
+        "metric": METRIC,
+        "value": round(B / (step_us * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": int(args.passes * (c.steps - 1)),
+        "warmup": int(c.steps + 1),
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hisparse hot-buffer decode, one layer, warm steps", "batch": B,
+                   "query_heads": heads, "context": c.ctx0, "steps_per_pass": c.steps,
+                   "top_k": c.top_k, "window": c.window, "sinks": c.num_sinks,
+                   "hot_rows_per_request": Hs, "host_pool_bytes": int(c.host_rows * ROW_BYTES),
+                   "splits": S},
+        "hot": {
+            "hit_rate_warm_steps": round(float(hits / (hits + misses)), 4),
+            "misses_per_warm_step": round(float(miss_per_step), 1),
+            "warm_step_us": {k: round(float(np.median(warm[:, i])), 2) for i, k in
+                             enumerate(["total", "normalise", "lookup_swapin", "decode_merge",
+                                        "backup"])},
+            "swapin_gbs_warm": round(miss_per_step * ROW_BYTES / swap_us / 1e3, 2),
+            "cold_step_us": round(float(np.median(a[:, 0, 0])), 1),
+            "cold_swapin_gbs": round(cold_misses * ROW_BYTES / cold_swap_us / 1e3, 2),
+            "pinned_h2d_copy_gbs": round((64 << 20) / h2d_us / 1e3, 2),
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU mode in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "hot":
+        bench_hot(args)
+        return
 
     import torch
 
