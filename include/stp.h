@@ -193,9 +193,11 @@ int stp_backup_rows(const void* hot_cache, int64_t hot_rows, void* host_pool, in
  * addressed by slot id, or the hot cache addressed by hot row); row_ids
  * [T, cap] int32; counts [T] int32 (nullable); out [T, H, 512] bf16; lse
  * [T, H] float (nullable).
- * num_splits: 0 = choose automatically, otherwise the number of contiguous
- * position ranges of ceil(n_t / num_splits) each (a performance hint: the
- * result does not depend on it beyond float rounding).  Splits > 1 need a
+ * num_splits: 0 = choose automatically (from T, H, cap and the current
+ * device's compute-unit count, so that the workgroups fill whole rounds of
+ * the device), otherwise the number of contiguous position ranges of
+ * ceil(n_t / num_splits) each (a performance hint: the result does not
+ * depend on it beyond float rounding).  Splits > 1 need a
  * workspace of stp_sparse_mla_decode_workspace() bytes (STP_ERR_WORKSPACE if
  * smaller); the workspace may be reused once the call's work has completed
  * on `stream`.
@@ -208,7 +210,9 @@ int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows
                           int32_t H, float scale, int32_t num_splits, void* workspace,
                           size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream);
 
-/* Splits stp_sparse_mla_decode uses for num_splits (0 = auto) at this shape. */
+/* Splits stp_sparse_mla_decode uses for num_splits (0 = auto) at this shape, on
+ * the current device (query it, and the workspace size, on the device the
+ * decode will run on). */
 int32_t stp_sparse_mla_decode_splits(int32_t T, int32_t H, int32_t cap, int32_t num_splits);
 
 /* Workspace bytes stp_sparse_mla_decode needs for this shape and num_splits. */

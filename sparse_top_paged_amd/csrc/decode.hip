@@ -738,18 +738,46 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   }
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Automatic split count: one workgroup per compute unit at a time, so the
+// launch takes ceil(workgroups / CUs) rounds of (fixed per-workgroup cost +
+// tiles of its split), and splitting adds the merge launch plus partial
+// states for it to read.  Costs in tile units: about four tiles of prologue
+// and epilogue per workgroup; the merge three tiles plus about 0.9 tile per
+// split per 32 query tokens.  A split's ids must fit the LDS list (kIdsMax).
+// The count depends on the current device's compute units.
 int32_t choose_splits(int32_t T, int32_t H, int32_t cap, int32_t requested) {
   const int G = (H + kHeadsPerWG - 1) / kHeadsPerWG;
-  int S;
-  if (requested > 0) {
-    S = requested;
-  } else {
-    const int64_t wgs = (int64_t)T * G;
-    S = wgs >= 256 ? 1 : (int)((256 + wgs - 1) / wgs);
-    S = min(S, max(1, cap / 128));  // keep at least four tiles per split
+  const int s_min = max(1, (cap + kIdsMax - 1) / kIdsMax);
+  if (requested > 0) return max(requested, s_min);
+  const int64_t cus = device_cus();
+  int best = s_min;
+  double best_cost = 1e300;
+  for (int S = s_min; S <= max(s_min, 16); ++S) {
+    const int64_t wgs = (int64_t)T * G * S;
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const int tiles = ((cap + S - 1) / S + kTileRows - 1) / kTileRows;
+    const double cost = (double)rounds * (4.0 + tiles) + (S > 1 ? 3.0 + 0.9 * S * T / 32.0 : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = S;
+    }
   }
-  S = max(S, (cap + kIdsMax - 1) / kIdsMax);  // a split's ids must fit the LDS list
-  return max(S, 1);
+  return best;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
