@@ -9,9 +9,11 @@
 // "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)",
 // Motivation: host-link bandwidth = bytes in flight / round trip.
 //
-// Design for wave64: one 256-thread workgroup per request row.  Phase 1
+// Design for wave64: one 1024-thread workgroup per request row.  Phase 1
 // builds an open-addressing hash (key = global id, value = entry index) in
-// LDS; phase 2 walks the LRU order in 256-slot chunks, and a block-wide scan
+// LDS and, when they fit, stages the request's LRU order and stored ids in
+// LDS with the same round trip; phase 2 walks the LRU order in 1024-slot
+// chunks (LDS reads only when staged), and a block-wide scan
 // keeps hits and evictables in walk order (hits from the front of an LDS
 // array, evictables from the back); phase 3 gives misses, in entry order,
 // the evictables from least recent on; phase 4 rewrites the order; phase 5
@@ -25,7 +27,9 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // reset and back-up kernels
+constexpr int kSwapThreads = 1024;  // swap-in kernel
+constexpr int kSwapWaves = kSwapThreads / 64;
 constexpr int kEmpty = -1;
 
 __device__ __forceinline__ uint32_t hash_of(int32_t g, int bits) {
@@ -34,22 +38,29 @@ __device__ __forceinline__ uint32_t hash_of(int32_t g, int bits) {
 
 struct HotLds {
   int32_t* keys;    // [HS]; after phase 2: global ids of the misses, in miss order
+  int32_t* dgi;     // [H] staged stored ids (when staged)
   int16_t* vals;    // [HS]
   int16_t* order;   // [H]: hits at the front, evictables reversed at the back
+  int16_t* lru;     // [H] staged LRU order (when staged)
   uint8_t* pend;    // [cap]
 };
 
-__device__ __forceinline__ HotLds carve(char* smem, int hash_bits, int H) {
+// LDS layout: keys, (dgi), vals, order, (lru), pend -- every array aligned to
+// its element size.
+__device__ __forceinline__ HotLds carve(char* smem, int hash_bits, int H, bool staged) {
   const int HS = 1 << hash_bits;
   HotLds s;
   s.keys = (int32_t*)smem;
-  s.vals = (int16_t*)(s.keys + HS);
+  s.dgi = s.keys + HS;
+  s.vals = (int16_t*)(s.dgi + (staged ? H : 0));
   s.order = s.vals + HS;
-  s.pend = (uint8_t*)(s.order + H);
+  s.lru = s.order + H;
+  s.pend = (uint8_t*)(s.lru + (staged ? H : 0));
   return s;
 }
 
-__global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
+template <bool kStaged>
+__global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
     const uint8_t* __restrict__ host_pool, int64_t host_rows, uint8_t* __restrict__ hot_cache,
     int64_t row_bytes, const int32_t* __restrict__ global_ids, int cap,
     const int32_t* __restrict__ newest_global, int32_t* __restrict__ dgi,
@@ -57,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
     int32_t* __restrict__ out, uint8_t* __restrict__ miss_mask,
     unsigned long long* __restrict__ stats, int hash_bits) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int s_scan[8];
+  __shared__ int s_scan[kSwapWaves];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* G = global_ids + (int64_t)r * cap;
@@ -65,14 +76,14 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
   uint8_t* row_miss = miss_mask ? miss_mask + (int64_t)r * cap : nullptr;
 
   if (r >= num_real_rows) {  // padding row: outputs -1, state untouched
-    for (int i = tid; i < cap; i += kThreads) {
+    for (int i = tid; i < cap; i += kSwapThreads) {
       row_out[i] = -1;
       if (row_miss) row_miss[i] = 0;
     }
     return;
   }
 
-  const HotLds s = carve(smem, hash_bits, H);
+  const HotLds s = carve(smem, hash_bits, H, kStaged);
   const int HS = 1 << hash_bits;
   const int hmask = HS - 1;
   const int64_t base = (int64_t)r * region_stride;
@@ -80,11 +91,18 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
   int32_t* row_dgi = dgi + (int64_t)r * H;
   int16_t* row_lru = lru + (int64_t)r * H;
 
-  for (int k = tid; k < HS; k += kThreads) s.keys[k] = kEmpty;
+  for (int k = tid; k < HS; k += kSwapThreads) s.keys[k] = kEmpty;
+  if (kStaged) {
+    // the LRU order and stored ids, all loads in flight with phase 1's
+    for (int p = tid; p < H; p += kSwapThreads) {
+      s.lru[p] = row_lru[p];
+      s.dgi[p] = row_dgi[p];
+    }
+  }
   __syncthreads();
 
   // Phase 1: classify entries; pending ones go into the hash.
-  for (int i = tid; i < cap; i += kThreads) {
+  for (int i = tid; i < cap; i += kSwapThreads) {
     const int32_t g = G[i];
     if (row_miss) row_miss[i] = 0;
     uint8_t p = 0;
@@ -110,11 +128,12 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
 
   // Phase 2: walk the LRU order, least recent first.
   int hits = 0, evicts = 0;
-  for (int p0 = 0; p0 < H; p0 += kThreads) {
+  for (int p0 = 0; p0 < H; p0 += kSwapThreads) {
     const int p = p0 + tid;
     const bool in_range = p < H;
-    const int slot = in_range ? row_lru[p] : -1;
-    const int32_t cached = (slot >= 0 && slot < H) ? row_dgi[slot] : -1;
+    const int slot = in_range ? (kStaged ? s.lru[p] : row_lru[p]) : -1;
+    const int32_t cached =
+        (slot >= 0 && slot < H) ? (kStaged ? s.dgi[slot] : row_dgi[slot]) : -1;
     int found = -1;
     if (cached >= 0) {
       uint32_t h = hash_of(cached, hash_bits);
@@ -135,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
       s.pend[found] = 0;
     }
     int total;
-    const int pre = stp::block_exclusive_scan_256((hit ? 1 << 16 : 0) | (evict ? 1 : 0), s_scan,
-                                                  &total);
+    const int pre = stp::block_exclusive_scan<kSwapWaves>((hit ? 1 << 16 : 0) | (evict ? 1 : 0),
+                                                           s_scan, &total);
     if (hit) s.order[hits + (pre >> 16)] = (int16_t)slot;
     if (evict) s.order[H - 1 - (evicts + (pre & 0xffff))] = (int16_t)slot;
     hits += total >> 16;
@@ -146,11 +165,11 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
 
   // Phase 3: misses, in entry order, take evictables from least recent on.
   int misses = 0;
-  for (int i0 = 0; i0 < cap; i0 += kThreads) {
+  for (int i0 = 0; i0 < cap; i0 += kSwapThreads) {
     const int i = i0 + tid;
     const bool miss = i < cap && s.pend[i];
     int total;
-    const int pre = stp::block_exclusive_scan_256(miss ? 1 : 0, s_scan, &total);
+    const int pre = stp::block_exclusive_scan<kSwapWaves>(miss ? 1 : 0, s_scan, &total);
     if (miss) {
       const int m = misses + pre;
       const int slot = s.order[H - 1 - m];
@@ -170,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
 
   // Phase 4: [evictables not taken] + [slots just loaded] + [hits].
   const int E = H - hits;
-  for (int p = tid; p < H; p += kThreads) {
+  for (int p = tid; p < H; p += kSwapThreads) {
     int slot;
     if (p < E - misses)
       slot = s.order[H - 1 - (p + misses)];
@@ -181,18 +200,19 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
     row_lru[p] = (int16_t)slot;
   }
 
-  // Phase 5: host -> hot row copies, 16-byte vectors, 4 in flight per thread.
+  // Phase 5: host -> hot row copies, 16-byte vectors, 4 in flight per thread
+  // (64 KiB per workgroup).
   const int64_t nvec = row_bytes >> 4;
   const int64_t total_vec = (int64_t)misses * nvec;
   const int4* host4 = (const int4*)host_pool;
   int4* hot4 = (int4*)hot_cache;
   const int4 zero = make_int4(0, 0, 0, 0);
-  for (int64_t k0 = tid; k0 < total_vec; k0 += 4 * kThreads) {
+  for (int64_t k0 = tid; k0 < total_vec; k0 += 4 * kSwapThreads) {
     int4 v[4];
     int64_t dst[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t k = k0 + (int64_t)u * kThreads;
+      const int64_t k = k0 + (int64_t)u * kSwapThreads;
       dst[u] = -1;
       if (k < total_vec) {
         const int m = (int)(k / nvec);
@@ -210,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void hot_swapin_kernel(
       if (dst[u] >= 0) hot4[dst[u]] = v[u];
   }
   __syncthreads();
-  for (int m = tid; m < misses; m += kThreads) {
+  for (int m = tid; m < misses; m += kSwapThreads) {
     const int slot = s.order[H - 1 - m];
     if (s.keys[m] >= host_rows && slot >= 0 && slot < H) row_dgi[slot] = -1;  // ownership revoked
   }
@@ -251,9 +271,10 @@ int hash_bits_for(int cap) {
   return bits;
 }
 
-size_t lds_bytes_for(int cap, int H) {
+size_t lds_bytes_for(int cap, int H, bool staged = false) {
   const int HS = 1 << hash_bits_for(cap);
-  return (size_t)HS * 4 + (size_t)HS * 2 + (size_t)H * 2 + (size_t)cap;
+  return (size_t)HS * 4 + (size_t)HS * 2 + (size_t)H * 2 + (size_t)cap +
+         (staged ? (size_t)H * 6 : 0);
 }
 
 constexpr size_t kLdsLimit = 160 * 1024 - 256;
@@ -299,16 +320,27 @@ extern "C" int stp_hot_lookup_swapin(const void* host_pool, int64_t host_rows, v
     return fail(STP_ERR_INVALID_ARG, "hot_lookup_swapin: null pointer");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)hot_swapin_kernel,
+    if (hipFuncSetAttribute((const void*)hot_swapin_kernel<true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) !=
-        hipSuccess)
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)hot_swapin_kernel<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) !=
+            hipSuccess)
       return fail(STP_ERR_HIP, "hot_lookup_swapin: hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hot_swapin_kernel<<<num_rows, kThreads, lds, stream>>>(
-      (const uint8_t*)host_pool, host_rows, (uint8_t*)hot_cache, row_bytes, global_ids, cap,
-      newest_global, dgi, lru, hot_size, region_stride, num_real_rows, hot_rows_out, miss_mask,
-      (unsigned long long*)stats, hash_bits_for(cap));
+  // stage the LRU order and stored ids in LDS when they fit beside the hash
+  const size_t staged_lds = lds_bytes_for(cap, hot_size, true);
+  if (staged_lds <= kLdsLimit)
+    hot_swapin_kernel<true><<<num_rows, kSwapThreads, staged_lds, stream>>>(
+        (const uint8_t*)host_pool, host_rows, (uint8_t*)hot_cache, row_bytes, global_ids, cap,
+        newest_global, dgi, lru, hot_size, region_stride, num_real_rows, hot_rows_out, miss_mask,
+        (unsigned long long*)stats, hash_bits_for(cap));
+  else
+    hot_swapin_kernel<false><<<num_rows, kSwapThreads, lds, stream>>>(
+        (const uint8_t*)host_pool, host_rows, (uint8_t*)hot_cache, row_bytes, global_ids, cap,
+        newest_global, dgi, lru, hot_size, region_stride, num_real_rows, hot_rows_out, miss_mask,
+        (unsigned long long*)stats, hash_bits_for(cap));
   return stp::check_launch("hot_swapin_kernel");
 }
 

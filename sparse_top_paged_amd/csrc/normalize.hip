@@ -318,26 +318,6 @@ struct FillArgs {
   uint64_t* blk_mask;
 };
 
-// Block-wide exclusive scan of one int per thread over kW waves; `scratch`
-// holds kW ints.  Returns the exclusive prefix and writes the total.
-template <int kW>
-__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int x = stp::wave_incl_sum(v);
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kW; ++w) {
-    const int sw = scratch[w];
-    off += w < wave ? sw : 0;
-    tot += sw;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + x - v;
-}
-
 // Per token: CSR offset by look-back, then the touched blocks from a bitmap
 // rebuilt out of the token's sorted S.  The request's page-table row is
 // staged in LDS (after the bitmap) while the look-back runs, when it fits.
@@ -448,7 +428,7 @@ __global__ __launch_bounds__(kFThreads) void block_fill_kernel(FillArgs a) {
     }
     const int page = m ? table[b] : 0;
     int tot;
-    const int k = k0 + block_excl_scan<kFWaves>(m ? 1 : 0, s_scan, &tot);
+    const int k = k0 + stp::block_exclusive_scan<kFWaves>(m ? 1 : 0, s_scan, &tot);
     if (m) {
       a.blk_logical[k] = b;
       a.blk_page[k] = page;

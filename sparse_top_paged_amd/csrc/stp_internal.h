@@ -37,25 +37,25 @@ __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_incl_sum(x), 63);
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x == 256).
-// `scratch` holds at least 8 ints of LDS.  Returns the exclusive prefix and
-// writes the block total to *total.
-__device__ __forceinline__ int block_exclusive_scan_256(int v, int* scratch, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+// Block-wide exclusive scan of one int per thread over a workgroup of kW
+// waves; `scratch` holds kW ints.  Returns the exclusive prefix and writes
+// the block total.
+template <int kW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int x = wave_incl_sum(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  int wave_off = 0, tot = 0;
+  int off = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    int s = scratch[w];
-    if (w < wave) wave_off += s;
-    tot += s;
+  for (int w = 0; w < kW; ++w) {
+    const int sw = scratch[w];
+    off += w < wave ? sw : 0;
+    tot += sw;
   }
   __syncthreads();
   *total = tot;
-  return wave_off + x - v;
+  return off + x - v;
 }
 
 // Two fp32 values -> a packed bf16 pair (a in the low half), round to

@@ -113,6 +113,17 @@ def test_multistep_full_width_rows():
     assert s[0] > 0
 
 
+def test_multistep_unstaged_state():
+    # hot_size 8192: the LRU order and stored ids no longer fit in LDS beside
+    # the hash, so the lookup reads them from global memory
+    import sparse_top_paged_amd as stp
+    H, cap = 8192, 4096 + 8 + 2
+    from sparse_top_paged_amd._lib import lib
+    assert stp.hot_lds_bytes(cap, H) > 0
+    s = _run_steps(batch=2, steps=3, top_k=4096, window=8, sinks=2, P=64, ctx0=20000)
+    assert s[0] > 0 and s[1] > 0
+
+
 def test_missing_host_rows_revoke():
     # the last pages of the pool are not in host memory: their slots are zeroed and revoked
     _run_steps(batch=3, steps=3, top_k=48, window=4, sinks=2, P=16, ctx0=900, trim_host=600)
