@@ -61,10 +61,16 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["deepseek", "hot"], default="deepseek",
+    ap.add_argument("--workload", choices=["deepseek", "hot", "locality"], default="deepseek",
                     help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
                          "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
-                         "pinned host memory), reported on its own line")
+                         "pinned host memory); locality: the long-context sweep (64 requests, "
+                         "context 131072, scattered against clustered top-k, 8 splits); the "
+                         "last two are reported on their own lines")
+    ap.add_argument("--locality-variant", choices=["both", "scattered", "clustered"],
+                    default="both", help="locality workload: which candidate layout to run")
+    ap.add_argument("--skip-auto", action="store_true",
+                    help="locality workload: time only the 8-split launches (counter runs)")
     ap.add_argument("--passes", type=int, default=6, help="hot workload: timed 16-step passes")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the row-gather and device-copy ceiling measurements")
@@ -131,6 +137,19 @@ def cpu_baseline(cases, kv, budget_s):
         "sample": f"{done} query-token decodes (the batch's {c.T} tokens cycled), each "
                   f"normalisation + fp64 attention over all {c.H} heads, {el:.1f} s on the host",
     }
+
+
+def copy_calibration():
+    """A plain device copy of known size (256 MiB read + 256 MiB written, three
+    launches), so that rocprofv3 counter runs can scale FETCH_SIZE and
+    WRITE_SIZE."""
+    import torch
+    src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def median_us(fn, n, sets):
@@ -308,14 +327,130 @@ def bench_hot(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_locality(args):
+    """The long-context locality sweep: 64 requests at context 131072 (page
+    64, a 9.66 GB pool in HBM), top-k 2048 only, either scattered uniformly or
+    clustered as 128 runs of 16 consecutive positions; decode with 8 splits,
+    then the merge.  Four candidate draws per layout rotate (the same tables
+    and queries).  Reports per layout the normalisation, decode and merge
+    times, the requested KV bytes and rate, and the page-granular efficiency
+    eta_blk = k / (u P) of loading whole touched pages instead of rows
+    ("5.1.1 · 从索引到 Kernel" §7.4 eq. (18))."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S = 8
+    nsets = 4
+    variants = ["scattered", "clustered"] if args.locality_variant == "both" else \
+        [args.locality_variant]
+    base = {v: workloads.locality_case(4001 if v == "scattered" else 4002, v == "clustered")
+            for v in variants}
+    c0 = base[variants[0]]
+    kv = workloads.pool_torch(c0.kv_rows, c0.pool_seed, dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    res_v = {}
+    for v in variants:
+        c = base[v]
+        T, H, cap, P = c.T, c.H, c.cap, c.page_size
+        ctx = int(c.q_pos[0]) + 1
+        draws = [c.topk]
+        for d in range(1, nsets):
+            rng = np.random.default_rng((4001 if v == "scattered" else 4002) * 100 + d)
+            if v == "clustered":
+                draws.append(np.stack([workloads.clustered_topk(rng, ctx, c.top_k)
+                                       for _ in range(T)]))
+            else:
+                draws.append(np.stack([rng.choice(ctx, size=c.top_k, replace=False)
+                                       .astype(np.int32) for _ in range(T)]))
+        q = t(c.q_bits.view(np.int16)).view(torch.bfloat16)
+        req, qpos, table = t(c.req_id), t(c.q_pos), t(c.block_table)
+        topk = [t(d) for d in draws]
+        norm = [stp.normalize_indices(tk, req, qpos, table, P, 0, 0, cap) for tk in topk]
+        torch.cuda.synchronize()
+        sel = np.asarray([int(n["count"].sum().item()) for n in norm], np.float64)
+        blocks = np.asarray([int(n["blk_indptr"][-1].item()) for n in norm], np.float64)
+        o_norm = torch.empty((T, S, H, 512), dtype=torch.bfloat16, device=dev)
+        m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+        l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        n_us = median_us(lambda k: stp.normalize_indices(topk[k], req, qpos, table, P, 0, 0, cap,
+                                                         out=norm[k]), 200, nsets)
+        d_us = median_us(lambda k: stp.sparse_mla_decode_partial_normalized(
+            q, kv, norm[k]["slot"], norm[k]["count"], c.scale, S, o_norm, m_part, l_part),
+            200, nsets)
+        m_us = median_us(lambda k: stp.splitkv_merge_normalized(o_norm, m_part, l_part, out, lse),
+                         200, nsets)
+        # the automatic split choice through the public entry point (decode + merge)
+        s_auto = stp.decode_splits(T, H, cap)
+        a_us = float("nan")
+        if not args.skip_auto:
+            ws = torch.empty((max(1, stp.decode_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
+                             device=dev)
+            a_us = median_us(lambda k: stp.sparse_mla_decode(
+                q, kv, norm[k]["slot"], norm[k]["count"], c.scale, 0, workspace=ws, out=out,
+                lse=lse), 200, nsets)
+        kv_bytes = float(sel.mean()) * ROW_BYTES
+        alg = kv_bytes + T * H * 576 * 2 + float(sel.mean()) * 4
+        part_bytes = T * S * H * (512 * 2 + 8)
+        res_v[v] = {
+            "normalise_us": round(n_us, 2),
+            "decode_us": round(d_us, 2),
+            "merge_us": round(m_us, 2),
+            "selected_rows_per_token": round(float(sel.mean()) / T, 1),
+            "touched_pages_per_token": round(float(blocks.mean()) / T, 1),
+            "eta_blk": round(float(sel.mean() / (blocks.mean() * P)), 4),
+            "requested_kv_bytes": int(kv_bytes),
+            "page_granular_kv_bytes": int(blocks.mean() * P * ROW_BYTES),
+            "decode_kv_gbs": round(kv_bytes / d_us / 1e3, 1),
+            "decode_alg_gbs": round(alg / d_us / 1e3, 1),
+            "decode_frac_of_hbm_peak": round(alg / d_us / 1e3 / HBM_PEAK_GBS, 4),
+            "partial_bytes_each_way": int(part_bytes),
+            "merge_gbs": round((part_bytes + T * H * (512 * 2 + 4)) / m_us / 1e3, 1),
+            "auto_splits": s_auto,
+            "auto_decode_and_merge_us": None if args.skip_auto else round(a_us, 2),
+        }
+    step_us = res_v[variants[0]]["normalise_us"] + res_v[variants[0]]["decode_us"] + \
+        res_v[variants[0]]["merge_us"]
+    res = {
+        "metric": METRIC,
+        "value": round(c0.T / (step_us * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": 200,
+        "warmup": 8,
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"long-context locality sweep ({variants[0]} rate as value)",
+                   "batch": c0.T, "query_heads": c0.H, "context": int(c0.q_pos[0]) + 1,
+                   "page_size": c0.page_size, "top_k": c0.top_k, "splits": S,
+                   "candidate_sets": nsets, "kv_pool_rows": c0.kv_rows},
+        "locality": res_v,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU mode in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
     if args.workload == "hot":
         bench_hot(args)
+        return
+    if args.workload == "locality":
+        bench_locality(args)
         return
 
     import torch
@@ -365,15 +500,6 @@ def main():
                 ev[1].record()
         if ev is not None:
             ev[2].record()
-
-    if args.copy_calibration:
-        # 256 MiB read + 256 MiB written per launch, three launches
-        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for i in range(args.warmup):
         step(i)
