@@ -53,6 +53,7 @@ struct NormArgs {
   const int32_t* block_table;
   int top_k, num_reqs, max_blocks, P, window, num_sinks, cap;
   int nwords_alloc;
+  int vec_out;    // cap % 4 == 0 and 16-byte aligned output rows: vector stores
   uint64_t pdiv;  // ceil(2^32 / P): t / P == (t * pdiv) >> 32 for t < 2^20
   int32_t* tok_out;
   int32_t* slot_out;
@@ -92,8 +93,9 @@ __device__ __forceinline__ int block_sum(int v, int* scratch) {
 template <bool kTableLds, bool kListLds>
 __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
   extern __shared__ uint64_t bitmap[];
-  __shared__ int s_red[kNWaves];
   __shared__ int s_wave_total[kNWaves];
+  __shared__ int s_wave_blocks[kNWaves];
+  __shared__ int s_wave_dropped[kNWaves];
 
   const int i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -195,9 +197,11 @@ __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
   const int na = min(a.num_sinks, q + 1);
   for (int t = tid; t < na; t += kNThreads)
     if (t <= limit && visible(t)) set_bit(t);
-  const int dropped = block_sum<kNWaves>(my_dropped, s_red);  // (its barriers publish the bitmap)
+  __syncthreads();  // bitmap complete
 
-  // Each wave owns a contiguous run of 64-word batches.
+  // One pass over the bitmap for the three totals, published together: the
+  // set's size (each wave owns a contiguous run of 64-word batches), the
+  // touched logical blocks (one block per thread) and the dropped entries.
   const int nbatch = (nwords + 63) >> 6;
   const int bpw = (nbatch + kNWaves - 1) / kNWaves;
   const int b0 = min(nbatch, wave * bpw), b1 = min(nbatch, b0 + bpw);
@@ -206,15 +210,30 @@ __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
     const int w = bb * 64 + lane;
     cnt += w < nwords ? __popcll(bitmap[w]) : 0;
   }
+  int my_blocks = 0;
+  if (a.blk_indptr) {
+    for (int b = tid; b < used_blocks; b += kNThreads) {
+      const int lo = b * P, hi = min(lo + P, limit + 1);
+      if (bits_in_range(bitmap, lo, hi)) ++my_blocks;
+    }
+  }
   cnt = stp::wave_sum(cnt);
-  if (lane == 0) s_wave_total[wave] = cnt;
+  my_blocks = stp::wave_sum(my_blocks);
+  my_dropped = stp::wave_sum(my_dropped);
+  if (lane == 0) {
+    s_wave_total[wave] = cnt;
+    s_wave_blocks[wave] = my_blocks;
+    s_wave_dropped[wave] = my_dropped;
+  }
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0, total = 0, nb = 0, dropped = 0;
 #pragma unroll
   for (int w = 0; w < kNWaves; ++w) {
     const int sw = s_wave_total[w];
     base += w < wave ? sw : 0;
     total += sw;
+    nb += s_wave_blocks[w];
+    dropped += s_wave_dropped[w];
   }
 
   // Ascending emission: into the LDS list (then written out below in one
@@ -255,7 +274,24 @@ __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
       if (mine) emit((bb * 64 + src) * 64 + lane, woff + (int)below);
     }
   }
-  if (kListLds) {
+  if (kListLds && a.vec_out) {
+    __syncthreads();  // list complete
+    // one coalesced pass, four consecutive entries per thread written as
+    // 16-byte vectors: tokens, slots and the -1 tail
+    for (int j0 = 4 * tid; j0 < a.cap; j0 += 4 * kNThreads) {
+      int tv[4], sl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) tv[u] = j0 + u < total ? l_list[j0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tv[u];
+        const int b = div_p(max(t, 0), a.pdiv);
+        sl[u] = t >= 0 ? table[b] * P + (t - b * P) : -1;
+      }
+      *(int4*)(tok_row + j0) = make_int4(tv[0], tv[1], tv[2], tv[3]);
+      *(int4*)(slot_row + j0) = make_int4(sl[0], sl[1], sl[2], sl[3]);
+    }
+  } else if (kListLds) {
     __syncthreads();  // list complete
     // one coalesced pass: tokens, slots and the -1 tail
     for (int j0 = 0; j0 < a.cap; j0 += 4 * kNThreads) {
@@ -287,15 +323,6 @@ __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
     }
   }
 
-  // Number of touched logical blocks (for the CSR block view).
-  int nb = 0;
-  if (a.blk_indptr) {
-    for (int b = tid; b < used_blocks; b += kNThreads) {
-      const int lo = b * P, hi = min(lo + P, limit + 1);
-      if (bits_in_range(bitmap, lo, hi)) ++nb;
-    }
-    nb = block_sum<kNWaves>(nb, s_red);
-  }
   if (tid == 0) {
     a.count_out[i] = total;
     if (a.dropped_out) a.dropped_out[i] = dropped;
@@ -499,8 +526,10 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
     attr_set = true;
   }
   const uint64_t pdiv = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+  const int vec_out = cap % 4 == 0 && (uintptr_t)tok_out % 16 == 0 &&
+                      (uintptr_t)slot_out % 16 == 0;
   NormArgs na{topk, req_id, q_pos, block_table, top_k, num_reqs, max_blocks, page_size, window,
-              num_sinks, cap, nwords, pdiv, tok_out, slot_out, count_out,
+              num_sinks, cap, nwords, vec_out, pdiv, tok_out, slot_out, count_out,
               dropped_out, blk_indptr};
   if (table_in_lds && list_in_lds)
     normalize_kernel<true, true><<<T, kNThreads, lds, stream>>>(na);
