@@ -18,12 +18,13 @@
 // on the same XCD (blockIdx % 8 picks the XCD) so the second reads the rows
 // from that XCD's L2.  Four wave64s per workgroup, one per SIMD, in two roles:
 //   score waves (0, 1): wave j owns heads 32 j .. 32 j + 31 of the group and
-//     keeps their Q^T for all 576 dims in 144 VGPRs.  Per 32-row tile it
+//     keeps their Q^T for all 576 dims in 144 AGPRs.  Per 32-row tile it
 //     forms S^T[32 rows x 32 heads] = K Q^T with 36 v_mfma_f32_32x32x16_bf16
 //     (A = K fragment read from LDS), runs the online softmax of its heads
 //     (a lane owns one head; base 2; the reference max moves only when a
 //     tile beats it by 2^8) and publishes P^T (bf16) and the per-head rescale
-//     factor of the tile in LDS.
+//     factor of the tile in LDS.  The softmax of tile i is interleaved with
+//     the QK products of tile i + 1, one MFMA per step.
 //   output waves (2, 3): wave j owns values 256 j .. 256 j + 255 of all 64
 //     heads, O^T[256 x 64] in 256 AGPRs.  One tile behind the score waves it
 //     rescales O^T when a factor is not 1 and adds V^T P^T with 32 MFMAs
@@ -34,11 +35,12 @@
 //   lane l of an output wave reads.  The QK and PV products (576 and 512 MACs
 //   per row and head) keep the four SIMDs equally busy, and the softmax of
 //   one tile overlaps the PV products of the previous one.
-// Rows are staged in a 3-deep LDS ring of 32-row tiles (36.5 KiB each) with
-// global_load_lds_dwordx4, so no VGPRs hold KV data in flight; one workgroup
-// barrier per tile hands over P^T, publishes the next tile and frees a ring
-// stage.  Invalid candidates load a zero row and are masked to -inf before
-// the exponent.
+// Rows are staged in a 4-stage LDS ring of 32-row tiles (36.5 KiB each) with
+// global_load_lds_dwordx4, so no VGPRs hold KV data in flight; only the
+// output waves issue tile loads, three tiles ahead, spread between their
+// MFMAs.  One LDS-only workgroup barrier per tile hands over P^T, publishes
+// the next tile and frees a ring stage.  Invalid candidates load a zero row
+// and are masked to -inf before the exponent.
 
 #include <type_traits>
 
