@@ -11,7 +11,8 @@ Sources (page titles as published):
   * "5.1.1 · 从索引到 Kernel" (PaperTrace) -- index normalisation, online
     softmax, split-KV merge (equations (1)-(21)).
   * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" -- decode
-    attention definition, partition combine, shifted causal mask.
+    attention definition, partition combine, shifted causal mask, paged
+    grouped-query decode and prefix-extend attention over a token pool.
 
 Pin status (what fixes each function other than itself) is listed in each
 module header.  Every function here is pinned; none is "parity unpinned".
@@ -29,6 +30,7 @@ from .attention import (
     split_ranges,
 )
 from .merge import merge, merge_normalized
+from .dense import decode_slots, extend_attention, extend_metadata, paged_gqa_decode
 
 __all__ = [
     "candidate_set", "normalize", "block_view",
@@ -36,4 +38,5 @@ __all__ = [
     "bf16_bits_to_f64", "attend_sparse", "attend_partial", "attend_dense_masked",
     "attend_fsum", "shifted_causal_mask", "split_ranges",
     "merge", "merge_normalized",
+    "decode_slots", "extend_attention", "extend_metadata", "paged_gqa_decode",
 ]
