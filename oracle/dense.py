@@ -25,7 +25,9 @@ What it states ("PagedAttention 与 RadixAttention：上游机制与海光实现
 Both are the dense masked softmax attention of attention.attend_dense_masked
 over the gathered rows -- the definition, with a numpy matrix product per
 step and no tiling.  A query row with nothing visible gives out = 0 and
-lse = -inf.
+lse = -inf.  Bad ids are data, as on the sparse path: a decode token whose
+page is unmapped (table entry < 0) or whose slot is outside the pool, and an
+extend key whose slot is outside the pool, take no part.
 
 Pins (tests/test_oracle_dense.py): the three-request ragged example of §3.3
 (its printed metadata arrays, tests/golden/extend_ragged_example.txt);
@@ -78,12 +80,15 @@ def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale)
         n = int(ctx_lens[b])
         if n <= 0:
             continue  # nothing to attend to: out = 0, lse = -inf
+        pages = np.asarray(block_table[b], dtype=np.int64)[np.arange(n) // page_size]
         slots = decode_slots(block_table[b], n, page_size)
+        ok = (pages >= 0) & (slots >= 0) & (slots < k_pool.shape[0])
+        slots = np.where(ok, slots, 0)
         for g in range(Hkv):
             K = _f64(k_pool[slots, g])
             V = _f64(v_pool[slots, g])
             heads = slice(g * group, (g + 1) * group)
-            mask = np.ones((group, n), dtype=bool)
+            mask = np.broadcast_to(ok, (group, n))
             out[b, heads], lse[b, heads] = attend_dense_masked(q[b, heads], K, V, mask, scale)
     return out, lse
 
@@ -102,7 +107,9 @@ def extend_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, scale)
         if q1 <= q0 or k1 <= k0:
             continue  # no queries, or no keys: out = 0, lse = -inf
         slots = np.asarray(kv_indices[k0:k1], dtype=np.int64)
-        mask = shifted_causal_mask(q1 - q0, k1 - k0)
+        ok = (slots >= 0) & (slots < k_pool.shape[0])
+        slots = np.where(ok, slots, 0)
+        mask = shifted_causal_mask(q1 - q0, k1 - k0) & ok[None, :]
         for h in range(Hq):
             g = h // group
             out[q0:q1, h], lse[q0:q1, h] = attend_dense_masked(
