@@ -26,8 +26,9 @@ Both are the dense masked softmax attention of attention.attend_dense_masked
 over the gathered rows -- the definition, with a numpy matrix product per
 step and no tiling.  A query row with nothing visible gives out = 0 and
 lse = -inf.  Bad ids are data, as on the sparse path: a decode token whose
-page is unmapped (table entry < 0) or whose slot is outside the pool, and an
-extend key whose slot is outside the pool, take no part.
+page is unmapped (table entry < 0, or a block past the end of the table) or
+whose slot is outside the pool, and an extend key whose slot is outside the
+pool, take no part.
 
 Pins (tests/test_oracle_dense.py): the three-request ragged example of §3.3
 (its printed metadata arrays, tests/golden/extend_ragged_example.txt);
@@ -80,8 +81,12 @@ def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale)
         n = int(ctx_lens[b])
         if n <= 0:
             continue  # nothing to attend to: out = 0, lse = -inf
-        pages = np.asarray(block_table[b], dtype=np.int64)[np.arange(n) // page_size]
-        slots = decode_slots(block_table[b], n, page_size)
+        row = np.asarray(block_table[b], dtype=np.int64).reshape(-1)
+        t = np.arange(n, dtype=np.int64)
+        inside = t // page_size < len(row)  # tokens past the table: unmapped
+        pages = np.where(inside, row[np.minimum(t // page_size, max(len(row) - 1, 0))]
+                         if len(row) else -1, -1)
+        slots = pages * page_size + t % page_size
         ok = (pages >= 0) & (slots >= 0) & (slots < k_pool.shape[0])
         slots = np.where(ok, slots, 0)
         for g in range(Hkv):

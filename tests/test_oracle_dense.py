@@ -125,3 +125,48 @@ def test_no_prefix_is_causal_prefill_and_one_query_is_decode():
     ext, else_ = oracle.extend_attention(q, k, v, md["qo_indptr"], md["kv_indptr"],
                                          np.concatenate(slots), 0.4)
     assert np.max(np.abs(dec - ext)) < 1e-14 and np.max(np.abs(dlse - else_)) < 1e-14
+
+
+def test_bad_ids_take_no_part():
+    """Unmapped pages (entry < 0), blocks past the end of the table, slots
+    outside the pool (decode) and kv_indices outside the pool (extend) drop
+    out: the result equals an fsum over the remaining rows only."""
+    rng = np.random.default_rng(9)
+    hq, hkv, d, P = 4, 2, 8, 4
+    slots_n = 40
+    k, v = _pool(rng, slots_n, hkv, d)
+    # request 0: page 1 unmapped, page 3 = 12 -> slots 48..51 outside the pool;
+    # request 1: ctx 14 with a 3-entry table -> tokens 12, 13 past the table
+    table = np.asarray([[2, -1, 5, 12], [0, 7, 3, 0]], np.int32)[:, :4]
+    table_short = table[:, :3]
+    ctx = np.asarray([16, 14], np.int32)
+    q = rng.standard_normal((2, hq, d)).astype(np.float16)
+    out, lse = oracle.paged_gqa_decode(q, k, v, table_short, ctx, P, 0.3)
+    out4, lse4 = oracle.paged_gqa_decode(q, k, v, table, ctx, P, 0.3)
+    for b, tab in ((0, table_short[0]), (1, table_short[1])):
+        live = []
+        for t in range(ctx[b]):
+            blk = t // P
+            if blk < len(tab) and tab[blk] >= 0 and tab[blk] * P + t % P < slots_n:
+                live.append(int(tab[blk]) * P + t % P)
+        for h in range(hq):
+            g = h // (hq // hkv)
+            o_ref, l_ref = _fsum_attend([q[b, h]], [k[s, g] for s in live],
+                                        [v[s, g] for s in live], 0.3)
+            assert np.max(np.abs(out[b, h] - o_ref[0])) < 1e-12
+            assert abs(lse[b, h] - l_ref[0]) < 1e-12
+    # request 0's fourth page maps outside the pool: the same result
+    assert np.max(np.abs(out4[0] - out[0])) < 1e-14
+    # extend: kv slots -1 and 45 drop out of request 0's keys
+    kvi = np.asarray([3, -1, 17, 45, 8, 9, 30], np.int32)
+    qo, kvp = np.asarray([0, 3]), np.asarray([0, 7])
+    qe = rng.standard_normal((3, hq, d)).astype(np.float16)
+    oe, le = oracle.extend_attention(qe, k, v, qo, kvp, kvi, 0.3)
+    for i in range(3):
+        live = [int(kvi[j]) for j in range(i + 4 + 1) if 0 <= kvi[j] < slots_n]
+        for h in range(hq):
+            g = h // (hq // hkv)
+            o_ref, l_ref = _fsum_attend([qe[i, h]], [k[s, g] for s in live],
+                                        [v[s, g] for s in live], 0.3)
+            assert np.max(np.abs(oe[i, h] - o_ref[0])) < 1e-12
+            assert abs(le[i, h] - l_ref[0]) < 1e-12
