@@ -10,6 +10,9 @@
  *   3. stp_sparse_mla_decode   attention over the selected latent rows with an
  *                              online softmax (optionally split);
  *   4. stp_splitkv_merge       merge of split partial states.
+ * Beside it, dense paged attention with grouped query heads over a token pool:
+ *      stp_paged_gqa_decode    decode over block tables;
+ *      stp_extend_attention    prefill of new tokens over a cached prefix.
  *
  * Sources: "HiSparse" hot-buffer walkthrough (devpress.csdn.net); "5.1.1 · 从
  * 索引到 Kernel" (PaperTrace); "PagedAttention 与 RadixAttention：上游机制与海光
@@ -295,6 +298,59 @@ int stp_row_gather(const void* rows, int64_t num_rows, int64_t row_bytes, const 
 
 /* Workgroups (= checksum words) of stp_row_gather; 0 for invalid sizes. */
 int32_t stp_row_gather_blocks(int32_t T, int32_t parts, int32_t replicas);
+
+/*
+ * ---- Dense paged attention with grouped query heads -------------------------
+ * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" §1.1 (decode
+ * attention), §1.2 (block table), §1.4 part 4 (grouped query heads: the grid
+ * runs over KV heads), §3.1-§3.4 (extend attention, the shifted causal mask,
+ * the ragged metadata arrays, the tile loop with early exit), §5 (the bshd
+ * token-pool layout).
+ *
+ * Token pool: k_pool, v_pool [num_slots, Hkv, head_dim] fp16 (uint16_t bit
+ * patterns), one row per slot and KV head.  Query head h reads KV head
+ * h / (Hq / Hkv).  Outputs are fp16 (round to nearest even) and the natural
+ * log-sum-exp of the scaled scores as float; a query with no visible key gets
+ * out = 0 and lse = -inf.  Keys whose slot is unmapped or outside the pool
+ * are data, not errors: they take no part.
+ * Requirements: head_dim == 128, Hq % Hkv == 0, 0 < scale < inf.
+ */
+
+/*
+ * Decode, one query token per request: for request b with n = ctx_lens[b]
+ * (values < 0 read as 0), token t < n lives in slot
+ * block_table[b, t / page_size] * page_size + t % page_size (a table entry
+ * < 0, or t / page_size >= max_blocks, is an unmapped page), and
+ *   out[b, h, :] = softmax_t(scale * <q[b, h], K[slot_t, h / group]>) V[slot_t, h / group]
+ * Layouts: q, out [B, Hq, 128]; block_table [B, max_blocks] int32; ctx_lens
+ * [B] int32; lse [B, Hq] (nullable).  Hq / Hkv <= 8.  One workgroup per
+ * (request, KV head) reads each K / V tile once for every query head of its
+ * group.
+ */
+int stp_paged_gqa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                         int64_t num_slots, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t head_dim, int32_t page_size, float scale, uint16_t* out,
+                         float* lse, hipStream_t stream);
+
+/*
+ * Extend (prefill over a cached prefix): request b has Lq = qo_indptr[b+1] -
+ * qo_indptr[b] new queries, rows qo_indptr[b] .. of the packed q, and Lk =
+ * kv_indptr[b+1] - kv_indptr[b] keys at slots kv_indices[kv_indptr[b] ..
+ * kv_indptr[b+1]) (the cached prefix first, then the new tokens).  Query i
+ * sees key j iff j <= i + (Lk - Lq):
+ *   out[qo_indptr[b] + i, h, :] = softmax_{j visible}(scale * <q, K_j>) V_j
+ * Layouts: q, out [N, Hq, 128] with N = qo_indptr[B]; qo_indptr, kv_indptr
+ * [B + 1] int32 ascending; kv_indices [kv_indptr[B]] int32; lse [N, Hq]
+ * (nullable).  max_extend_len >= every Lq (it sizes the grid: queries of a
+ * request beyond it are not computed).  Hq / Hkv <= 4.  Key tiles past the
+ * last one any query of a 64-query block can see are not read.
+ */
+int stp_extend_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                         int64_t num_slots, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t head_dim, int32_t max_extend_len, float scale, uint16_t* out,
+                         float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

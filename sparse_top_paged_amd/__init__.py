@@ -18,6 +18,7 @@ __all__ = [
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
+    "paged_gqa_decode", "extend_attention",
 ]
 
 
@@ -294,3 +295,63 @@ def row_gather(rows, row_ids, counts=None, parts=1, replicas=1, checksum=None):
         _opt(counts, "counts", torch.int32, dev), cap, T, parts, replicas,
         _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
     return checksum
+
+
+def _pool(k_pool, v_pool):
+    if k_pool.dim() != 3 or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must both be [slots, Hkv, head_dim]")
+    return k_pool.device, k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+
+
+def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale=None, out=None,
+                     lse=None):
+    """Dense paged decode with grouped query heads.  q [B, Hq, 128] fp16,
+    k_pool / v_pool [slots, Hkv, 128] fp16, block_table [B, max_blocks] int32,
+    ctx_lens [B] int32.  Returns (out [B, Hq, 128] fp16, lse [B, Hq] float32)."""
+    dev, slots, Hkv, D = _pool(k_pool, v_pool)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [B, Hq, head_dim]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and ctx_lens [B]")
+    scale = D ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    check(lib.stp_paged_gqa_decode(
+        _dev(q, "q", torch.float16, dev), _dev(k_pool, "k_pool", torch.float16, dev),
+        _dev(v_pool, "v_pool", torch.float16, dev), slots,
+        _dev(block_table, "block_table", torch.int32, dev), block_table.shape[1],
+        _dev(ctx_lens, "ctx_lens", torch.int32, dev), B, Hq, Hkv, D, page_size, float(scale),
+        _dev(out, "out", torch.float16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse
+
+
+def extend_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, max_extend_len,
+                     scale=None, out=None, lse=None):
+    """Prefix-extend attention with the shifted causal mask.  q [N, Hq, 128]
+    fp16 packed by qo_indptr [B + 1]; keys at kv_indices[kv_indptr[b] ..
+    kv_indptr[b + 1]) of the pools.  max_extend_len >= every request's query
+    count.  Returns (out [N, Hq, 128] fp16, lse [N, Hq] float32)."""
+    dev, slots, Hkv, D = _pool(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [N, Hq, head_dim]")
+    N, Hq = q.shape[0], q.shape[1]
+    B = qo_indptr.shape[0] - 1
+    if B < 0 or kv_indptr.shape[0] != B + 1:
+        raise ValueError("qo_indptr and kv_indptr must both be [B + 1]")
+    scale = D ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty((N, Hq, D), dtype=torch.float16, device=dev)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    kvi = kv_indices if kv_indices.numel() > 0 else torch.zeros(1, dtype=torch.int32, device=dev)
+    check(lib.stp_extend_attention(
+        _dev(q, "q", torch.float16, dev), _dev(k_pool, "k_pool", torch.float16, dev),
+        _dev(v_pool, "v_pool", torch.float16, dev), slots,
+        _dev(qo_indptr, "qo_indptr", torch.int32, dev), _dev(kv_indptr, "kv_indptr", torch.int32, dev),
+        _dev(kvi, "kv_indices", torch.int32, dev), B, Hq, Hkv, D, int(max_extend_len),
+        float(scale), _dev(out, "out", torch.float16, dev), _opt(lse, "lse", torch.float32, dev),
+        _stream(dev)))
+    return out, lse

@@ -58,6 +58,65 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   return off + x - v;
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS only (__syncthreads() would also wait
+// for every tile load in flight).  The signal fences stop the compiler from
+// moving memory accesses across it; the hardware wait is lgkmcnt(0) alone.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// max / sum of x over the lane pair (l, l ^ 32), identical in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): global address vaddr + offset, LDS address
+// m0 + offset + 16 * lane -- the immediate offset applies to both sides.
+// Issued from inline asm so that the compiler's wait-count pass does not
+// track these loads: the tile ring waits for them explicitly (wait_vmcnt),
+// and the compiler would otherwise drain the ring before every LDS access it
+// cannot prove disjoint from the loads in flight.
+template <int kOffset>
+__device__ __forceinline__ void load_lds_16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off offset:%1" ::"v"(gptr), "n"(kOffset),
+               "{m0}"(lds_addr));
+}
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// acc *= f for an MFMA accumulator kept in AGPRs.  Written as inline asm on
+// AGPR operands so that the compiler keeps the accumulators in AGPRs (a plain
+// VALU multiply makes it move all 256 of them through VGPRs).
+__device__ __forceinline__ void scale_acc(floatx16& acc, float f) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(acc[r]), "=&v"(t)
+        : "v"(f));
+  }
+}
+
 // Two fp32 values -> a packed bf16 pair (a in the low half), round to
 // nearest even, by the hardware conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

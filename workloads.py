@@ -251,3 +251,144 @@ def hot_steps_case(seed=3000, batch=64, ctx0=65536, steps=16, top_k=2048, window
         q_steps.append(normal_bf16(rng, (batch, heads, D_QK)))
     return HotSteps(batch, ctx0, steps, top_k, window, sinks, page_size, tables, topk_steps,
                     q_steps, pool_pages * page_size, seed + 1, heads)
+
+
+# ---- dense paged attention with grouped query heads -------------------------
+# Token pool [slots, Hkv, 128] fp16 for K and for V, values N(0, 1); page
+# size 16; each request owns a disjoint random set of pages of the pool.
+
+D_HEAD = 128
+
+
+def normal_fp16(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
+def dense_pool(slots, hkv, seed):
+    """K and V pools [slots, hkv, 128] fp16 on the host (numpy)."""
+    rng = np.random.default_rng(seed)
+    return normal_fp16(rng, (slots, hkv, D_HEAD)), normal_fp16(rng, (slots, hkv, D_HEAD))
+
+
+def dense_pool_torch(slots, hkv, seed, device, chunk_slots=1 << 16):
+    """K and V pools generated in device memory by torch's seeded generator
+    (N(0, 1) rounded to fp16 by torch's conversion)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    pools = []
+    for _ in range(2):
+        p = torch.empty((slots, hkv, D_HEAD), dtype=torch.float16, device=device)
+        for lo in range(0, slots, chunk_slots):
+            hi = min(slots, lo + chunk_slots)
+            p[lo:hi] = torch.randn((hi - lo, hkv, D_HEAD), generator=g, device=device,
+                                   dtype=torch.float32)
+        pools.append(p)
+    return pools[0], pools[1]
+
+
+@dataclass
+class GqaDecodeCase:
+    name: str
+    q: np.ndarray            # [B, Hq, 128] fp16
+    block_table: np.ndarray  # [B, max_blocks] int32, -1 = unmapped
+    ctx_lens: np.ndarray     # [B] int32
+    page_size: int
+    hkv: int
+    num_slots: int
+    pool_seed: int
+    scale: float = 1.0 / math.sqrt(D_HEAD)
+
+
+@dataclass
+class ExtendCase:
+    name: str
+    q: np.ndarray            # [N, Hq, 128] fp16, packed by qo_indptr
+    qo_indptr: np.ndarray    # [B + 1] int32
+    kv_indptr: np.ndarray    # [B + 1] int32
+    kv_indices: np.ndarray   # [kv_indptr[B]] int32 slot ids
+    max_extend_len: int
+    hkv: int
+    num_slots: int
+    pool_seed: int
+    scale: float = 1.0 / math.sqrt(D_HEAD)
+
+
+def _page_tables(rng, pages_per_req, spare=0):
+    """Disjoint random page sets of one pool; ragged rows padded with -1."""
+    total = int(np.sum(pages_per_req))
+    perm = rng.permutation(total + spare).astype(np.int32)
+    width = max(1, int(np.max(pages_per_req, initial=0)))
+    tables = np.full((len(pages_per_req), width), -1, np.int32)
+    off = 0
+    for b, n in enumerate(pages_per_req):
+        tables[b, :n] = perm[off:off + n]
+        off += n
+    return tables, total + spare
+
+
+def gqa_decode_case(seed=5000, batch=128, ctx_lo=1024, ctx_hi=4096, hq=32, hkv=8, page_size=16):
+    """Decode batch: context lengths uniform in [ctx_lo, ctx_hi], one query
+    token per request, random block tables."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(ctx_lo, ctx_hi + 1, size=batch).astype(np.int32)
+    tables, pages = _page_tables(rng, -(-ctx // page_size))
+    q = normal_fp16(rng, (batch, hq, D_HEAD))
+    return GqaDecodeCase(f"gqa_decode_b{batch}", q, tables, ctx, page_size, hkv,
+                         pages * page_size, pool_seed=seed + 1)
+
+
+def extend_case(seed=5100, batch=8, prefix=4096, extend=512, hq=32, hkv=8, page_size=16):
+    """Extend batch: every request has `prefix` cached tokens and `extend` new
+    ones; its keys are the slots of its pages in order (prefix first)."""
+    rng = np.random.default_rng(seed)
+    lk = np.full(batch, prefix + extend, np.int64)
+    lq = np.full(batch, extend, np.int64)
+    return _extend_from_lengths(rng, f"extend_b{batch}_p{prefix}_e{extend}", lq, lk, hq, hkv,
+                                page_size, seed + 1)
+
+
+def _extend_from_lengths(rng, name, lq, lk, hq, hkv, page_size, pool_seed, bad_frac=0.0):
+    pages_per_req = -(-np.asarray(lk) // page_size)
+    tables, pages = _page_tables(rng, pages_per_req, spare=1)
+    slots = []
+    for b in range(len(lk)):
+        t = np.arange(lk[b])
+        s = (tables[b][t // page_size].astype(np.int64) * page_size + t % page_size).astype(np.int32)
+        if bad_frac > 0:
+            bad = rng.random(len(s)) < bad_frac
+            s[bad] = rng.choice(np.asarray([-1, pages * page_size + 3, 1 << 30], np.int32),
+                                size=int(bad.sum()))
+        slots.append(s)
+    qo = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    kv = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = normal_fp16(rng, (int(qo[-1]), hq, D_HEAD))
+    kvi = np.concatenate(slots).astype(np.int32) if len(slots) else np.zeros(0, np.int32)
+    return ExtendCase(name, q, qo, kv, kvi, int(np.max(lq, initial=0)), hkv, pages * page_size,
+                      pool_seed)
+
+
+def random_extend_case(seed, lq, lk, hq=8, hkv=2, page_size=16, bad_frac=0.05):
+    """Small ragged extend batch with the given per-request query and key
+    counts (Lk < Lq allowed: the first Lq - Lk queries then see nothing) and
+    a fraction of bad slot ids (-1 or outside the pool)."""
+    rng = np.random.default_rng(seed)
+    return _extend_from_lengths(rng, f"extend_small_{seed}", np.asarray(lq, np.int64),
+                                np.asarray(lk, np.int64), hq, hkv, page_size, seed + 1, bad_frac)
+
+
+def random_gqa_decode_case(seed, ctx, hq=8, hkv=2, page_size=16, unmapped_frac=0.1,
+                           table_slack=1):
+    """Small ragged decode batch: context lengths as given, tables one block
+    wider than needed (-1), a fraction of unmapped pages, and one page
+    pointing outside the pool when the batch has room for it."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, np.int32)
+    tables, pages = _page_tables(rng, -(-np.maximum(ctx, 0) // page_size), spare=2)
+    tables = np.concatenate([tables, np.full((len(ctx), table_slack), -1, np.int32)], axis=1)
+    tables[(rng.random(tables.shape) < unmapped_frac) & (tables >= 0)] = -1
+    if len(ctx) > 1 and tables[1, 0] >= 0:
+        tables[1, 0] = pages + 5  # a page past the pool's end
+    q = normal_fp16(rng, (len(ctx), hq, D_HEAD))
+    return GqaDecodeCase(f"gqa_small_{seed}", q, tables, ctx, page_size, hkv, pages * page_size,
+                         pool_seed=seed + 1)
