@@ -323,7 +323,7 @@ int32_t stp_row_gather_blocks(int32_t T, int32_t parts, int32_t replicas);
  * < 0, or t / page_size >= max_blocks, is an unmapped page), and
  *   out[b, h, :] = softmax_t(scale * <q[b, h], K[slot_t, h / group]>) V[slot_t, h / group]
  * Layouts: q, out [B, Hq, 128]; block_table [B, max_blocks] int32; ctx_lens
- * [B] int32; lse [B, Hq] (nullable).  Hq / Hkv <= 8.  One workgroup per
+ * [B] int32; lse [B, Hq] (nullable).  Hq / Hkv <= 16.  One workgroup per
  * (request, KV head) reads each K / V tile once for every query head of its
  * group.
  */

@@ -82,7 +82,42 @@ using stp::pair_sum;
 using stp::scale_acc;
 using stp::wait_vmcnt;
 
+// the row a bad key loads: zeros keep P V finite where P = 0
+__device__ __attribute__((aligned(16))) uint8_t g_zero_head_row[kRowBytes] = {};
+
+constexpr int kStageBytes = 2 * kTile * kRowBytes;  // one tile: K then V, 32 KiB
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// Tile loads go straight to LDS, 1 KiB (4 keys) per wave instruction:
+// instruction u of wave w fills keys 16 w + 4 u + lane / 16 of the tile, LDS
+// chunk position lane % 16, so the lane fetches row chunk
+// (lane % 16) ^ (key % 16) -- the swizzled tile layout.  K and V of one key
+// share the slot.  slot < 0 loads the zero row.
+__device__ __forceinline__ void issue_kv_rows(const uint8_t* kpool, const uint8_t* vpool,
+                                              int64_t head_bytes, int g, const uint8_t* zero_row,
+                                              uint32_t stage_base, int wave, int lane,
+                                              const int64_t (&sl)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = 16 * wave + 4 * u + (lane >> 4);
+    const int c = (lane & 15) ^ (t & 15);
+    const int64_t off = sl[u] * head_bytes + g * kRowBytes + 16 * c;
+    const uint8_t* kp = sl[u] >= 0 ? kpool + off : zero_row + 16 * c;
+    const uint8_t* vp = sl[u] >= 0 ? vpool + off : zero_row + 16 * c;
+    const uint32_t row0 = __builtin_amdgcn_readfirstlane(stage_base + (16 * wave + 4 * u) * kRowBytes);
+    load_lds_16<0>(kp, row0);
+    load_lds_16<0>(vp, row0 + kTile * kRowBytes);
+  }
+}
+
 // ---------------------------------------------------------------- decode --
+
+constexpr int kDecStages = 4;      // tiles in the LDS ring (three in flight)
+constexpr int kTabChunk = 2048;    // block-table entries staged in LDS at a time
+constexpr int kDecMaxGroup = 16;   // query heads per KV head (the MFMA N width)
 
 struct DecArgs {
   const uint16_t* q;   // [B, Hq, 128]
@@ -98,141 +133,217 @@ struct DecArgs {
   float* lse;     // [B, Hq] (nullable)
 };
 
-__global__ __launch_bounds__(kThreads) void paged_gqa_decode_kernel(DecArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_k[kTile * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char s_v[kTile * kRowBytes];
-  __shared__ uint8_t s_ok[kTile];
+struct DecLds {
+  char tiles[kDecStages * kStageBytes];  // reused for the wave merge at the end
+  int32_t tab[kTabChunk];
+  uint8_t ok[kDecStages][kTile];
+};
+
+// One workgroup per (request, KV head), four waves.  Wave w takes keys
+// 16 w .. 16 w + 15 of every 64-key tile and keeps its own softmax state for
+// the group's heads; the four states are merged at the end.  Per tile and
+// wave:
+//   S^T[16 keys x 16 heads] = K Q^T with 4 v_mfma_f32_16x16x32_f16 (A = K
+//     rows from LDS, B = Q^T in registers, heads past the group are zero);
+//   lane l holds head l % 16, keys 4 (l / 16) .. + 3: the column max and sum
+//     over the 16 keys take two lane exchanges;
+//   O^T[128 x 16 heads] += V^T P^T with 8 v_mfma_f32_16x16x16_f16: A = V^T by
+//     ds_read_b64_tr_b16 (lane group gq reads keys 4 gq .. + 3, the keys the
+//     accumulator holds), B = P^T, the lane's own four softmax weights.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void paged_gqa_decode_kernel(DecArgs a) {
+  __shared__ __attribute__((aligned(1024))) DecLds L;
   const int b = blockIdx.x / a.Hkv, g = blockIdx.x - (blockIdx.x / a.Hkv) * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = a.Hq / a.Hkv;
   const int n = min(max(a.ctx[b], 0), a.max_blocks * a.P);
   const int ntiles = (n + kTile - 1) / kTile;
+  const int nb = (n + a.P - 1) / a.P;  // table entries in use
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  const int64_t head_stride = (int64_t)a.Hkv * kD;  // elements between slots
+  const int64_t head_bytes = (int64_t)a.Hkv * kRowBytes;
+  const uint8_t* zero_row = g_zero_head_row;
+  asm volatile("" : "+s"(zero_row));
+  const uint32_t tiles_base = (uint32_t)(uintptr_t)(lds_t*)L.tiles;
+  const int tab_tokens = kTabChunk * a.P;  // a multiple of the tile size
 
-  // loader role: chunk lc of tokens lt + 16 u (u = 0..3) of the tile, K and V
-  const int lc = tid & 15, lt = tid >> 4;
-  auto slot_of = [&](int t) -> int64_t {  // -1 for a token past n or a bad slot
-    if (t >= n) return -1;
-    const int blk = t / a.P;
-    const int page = trow[blk];
-    const int64_t s = (int64_t)page * a.P + (t - blk * a.P);
-    return (page >= 0 && s < a.slots) ? s : -1;
+  int chunk = -1;
+  auto load_chunk = [&](int c) {  // all threads; caller brackets with barriers
+    for (int i = tid; i < kTabChunk; i += kThreads) {
+      const int e = c * kTabChunk + i;
+      L.tab[i] = e < nb ? trow[e] : -1;
+    }
+    chunk = c;
   };
-  int64_t slot_next[4];
-  uintx4 kr[4], vr[4];
-  auto fetch = [&](const int64_t (&sl)[4]) {
+  // slots of this lane's four keys of tile j (-1: past n, unmapped, outside the pool)
+  auto slots_of = [&](int j, int64_t (&sl)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t e = sl[u] * head_stride + (int64_t)g * kD + lc * 8;
-      kr[u] = sl[u] >= 0 ? *(const uintx4*)(a.k + e) : uintx4{0u, 0u, 0u, 0u};
-      vr[u] = sl[u] >= 0 ? *(const uintx4*)(a.v + e) : uintx4{0u, 0u, 0u, 0u};
+      const int t = j * kTile + 16 * wave + 4 * u + (lane >> 4);
+      sl[u] = -1;
+      if (t < n) {
+        const int blk = t / a.P;
+        const int page = L.tab[blk - chunk * kTabChunk];
+        const int64_t s = (int64_t)page * a.P + (t - blk * a.P);
+        sl[u] = (page >= 0 && s < a.slots) ? s : -1;
+      }
     }
   };
-  auto stage = [&](const int64_t (&sl)[4]) {
+  auto issue = [&](int j) {
+    int64_t sl[4];
+    slots_of(j, sl);
+    const int st = j % kDecStages;
+    issue_kv_rows((const uint8_t*)a.k, (const uint8_t*)a.v, head_bytes, g, zero_row,
+                  tiles_base + st * kStageBytes, wave, lane, sl);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = lt + 16 * u;
-      *(__attribute__((address_space(3))) uintx4*)((lds_t*)s_k + tile_off(t, lc)) = kr[u];
-      *(__attribute__((address_space(3))) uintx4*)((lds_t*)s_v + tile_off(t, lc)) = vr[u];
-      if (lc == 0) s_ok[t] = sl[u] >= 0 ? 1 : 0;
-    }
+    for (int u = 0; u < 4; ++u)
+      if ((lane & 15) == 0) L.ok[st][16 * wave + 4 * u + (lane >> 4)] = sl[u] >= 0 ? 1 : 0;
   };
 
-  // query heads of this wave: g * group + wave + 4 k, k < 2 (group <= 8)
-  halfx2 qv[2][kD / 2];
-  bool has[2];
+  // Q^T fragments (B of S^T = K Q^T): head l % 16 of the group, values
+  // 32 ks + 8 (l / 16) .. + 7; zero past the group
+  halfx8 qf[kD / 32];
+  {
+    const int hl = lane & 15;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * group + min(hl, group - 1)) * kD;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int hl = wave + 4 * k;
-    has[k] = hl < group;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * group + (has[k] ? hl : 0)) * kD;
-#pragma unroll
-    for (int c = 0; c < kD / 8; ++c) {
-      const uintx4 w = *(const uintx4*)(qrow + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qv[k][c * 4 + e] = word_h2(w, e);
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      const uintx4 w = hl < group ? *(const uintx4*)(qrow + 32 * ks + 8 * (lane >> 4))
+                                  : uintx4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(halfx8, w);
     }
   }
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  float o0[2] = {0.f, 0.f}, o1[2] = {0.f, 0.f};
+  // K fragment (A of S^T): key 16 w + l % 16, chunk 4 ks + l / 16; the
+  // key's swizzle is l % 16, so ks steps are an XOR of ks << 6.
+  const uint32_t k_off = (16 * wave + (lane & 15)) * kRowBytes +
+                         ((((lane >> 4) ^ (lane & 15)) & 15) << 4);
+  // V^T fragment (A of O^T, transpose read): lane (gq, j16) points at key
+  // 16 w + 4 gq + j16 / 4, values 16 mb + 4 (j16 % 4) .. + 3, i.e. chunk
+  // 2 mb + (j16 % 4) / 2, byte 8 (j16 % 2); mb steps are an XOR of mb << 5.
+  const int vq = lane >> 4, vj = lane & 15;
+  const int v_tok = 4 * vq + (vj >> 2);
+  const uint32_t v_off = kTile * kRowBytes + (16 * wave + v_tok) * kRowBytes +
+                         (((((vj & 3) >> 1) ^ v_tok) & 15) << 4) + 8 * (vj & 1);
 
-  int64_t sl_cur[4];
-  if (ntiles > 0) {
+  floatx4 o[kD / 16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sl_cur[u] = slot_of(lt + 16 * u);
-    fetch(sl_cur);
-    stage(sl_cur);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) slot_next[u] = slot_of(kTile + lt + 16 * u);
-  }
+  for (int mb = 0; mb < kD / 16; ++mb) o[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, lsum = 0.f;  // head l % 16; lsum over this lane's keys
+
+  // prologue: table chunk 0, tiles 0 .. kDecStages - 2 in flight
+  if (ntiles > 0) load_chunk(0);
   __syncthreads();
-  for (int i = 0; i < ntiles; ++i) {
-    // next tile's rows in flight, the one after's page entries too
-    int64_t sl_after[4];
-    if (i + 1 < ntiles) fetch(slot_next);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sl_after[u] = slot_of((i + 2) * kTile + lt + 16 * u);
+  for (int j = 0; j < kDecStages - 1 && j < ntiles; ++j) issue(j);
 
-    const bool ok_t = s_ok[lane] != 0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (!has[k]) continue;  // wave-uniform
-      // score of this lane's token for head k
-      float z = 0.f;
-#pragma unroll
-      for (int c = 0; c < kD / 8; ++c) {
-        const uintx4 w = *(const __attribute__((address_space(3))) uintx4*)((lds_t*)s_k +
-                                                                             tile_off(lane, c));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          z = __builtin_amdgcn_fdot2(qv[k][c * 4 + e], word_h2(w, e), z, false);
+  for (int it = 0; it < ntiles; ++it) {
+    // tile it has landed once at most min(S - 2, ntiles - 1 - it) newer tiles
+    // are in flight (8 loads per wave each)
+    const int newer = min(kDecStages - 2, ntiles - 1 - it);
+    if (newer >= 2)
+      wait_vmcnt<16>();
+    else if (newer == 1)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // tile it visible; every wave is done with tile it - 1
+    const int jn = it + kDecStages - 1;
+    if (jn < ntiles) {
+      if (jn * kTile >= (chunk + 1) * tab_tokens) {
+        // next block-table chunk: every issue from the current one is done
+        load_chunk(jn * kTile / tab_tokens);
+        __syncthreads();
       }
-      z = ok_t ? z * a.scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m[k], wave_max(z));
-      if (m_new == -INFINITY) continue;  // nothing visible yet (wave-uniform)
-      const float alpha = __builtin_amdgcn_exp2f(m[k] - m_new);
-      const float p = __builtin_amdgcn_exp2f(z - m_new);
-      l[k] = l[k] * alpha + wave_sum(p);
-      m[k] = m_new;
-      float a0 = o0[k] * alpha, a1 = o1[k] * alpha;
-      // PV: lane owns values 2 lane, 2 lane + 1
-#pragma unroll 16
-      for (int t = 0; t < kTile; ++t) {
-        const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t));
-        const halfx2 vv = *(const __attribute__((address_space(3))) halfx2*)(
-            (lds_t*)s_v + tile_off(t, lane >> 2) + (lane & 3) * 4);
-        a0 = __builtin_fmaf(pt, (float)vv[0], a0);
-        a1 = __builtin_fmaf(pt, (float)vv[1], a1);
-      }
-      o0[k] = a0;
-      o1[k] = a1;
+      issue(jn);  // into the stage of tile it - 1
     }
-    __syncthreads();  // every wave is done with tile i
-    if (i + 1 < ntiles) stage(slot_next);
+    const int st = it % kDecStages;
+    const uint32_t sbase = tiles_base + st * kStageBytes;
+    // S^T for keys 16 w .. + 15
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) slot_next[u] = sl_after[u];
-    __syncthreads();  // tile i + 1 visible
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      const halfx8 kf = __builtin_bit_cast(
+          halfx8, *(const __attribute__((address_space(3))) uintx4*)(
+                      (lds_t*)(uintptr_t)((sbase + k_off) ^ (ks << 6))));
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s, 0, 0, 0);
+    }
+    // mask, column max over the 16 keys (lanes l, l ^ 16, l ^ 32, l ^ 48)
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = L.ok[st][16 * wave + 4 * (lane >> 4) + r] != 0;
+      s[r] = ok ? s[r] * a.scale_log2 : -INFINITY;
+      zmax = fmaxf(zmax, s[r]);
+    }
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
+    zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
+    // the reference maximum moves only when it is beaten by 2^8
+    if (zmax > m_ref + 8.0f) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - zmax);
+      m_ref = zmax;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < kD / 16; ++mb) o[mb] *= alpha;
+    }
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    halfx4 pf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] + neg_m);
+      lsum += p;
+      pf[r] = (_Float16)p;
+    }
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) {
+      const shortx4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_shortx4*)(uintptr_t)((sbase + v_off) ^ (mb << 5)));
+      o[mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(halfx4, vf), pf, o[mb], 0, 0,
+                                                    0);
+    }
   }
 
+  // merge the four waves' states: M = max m_w, out = sum 2^(m_w - M) O_w /
+  // sum 2^(m_w - M) l_w
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // the ring is free (every tile consumed)
+  float* sm = (float*)L.tiles;           // [4 waves][16 heads]
+  float* sl = sm + 4 * kDecMaxGroup;     // [4][16]
+  float* so = sl + 4 * kDecMaxGroup;     // [4][16 heads][128]
+  if (lane < 16) {
+    sm[wave * kDecMaxGroup + lane] = m_ref;
+    sl[wave * kDecMaxGroup + lane] = lsum;
+  }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    if (!has[k]) continue;
-    const int h = g * group + wave + 4 * k;
-    const float inv = l[k] > 0.f ? 1.f / l[k] : 0.f;
-    const halfx2 ov = {(_Float16)(o0[k] * inv), (_Float16)(o1[k] * inv)};
-    *(halfx2*)(a.out + ((int64_t)b * a.Hq + h) * kD + 2 * lane) = ov;
-    if (a.lse && lane == 0)
-      a.lse[(int64_t)b * a.Hq + h] = l[k] > 0.f ? (m[k] + log2f(l[k])) * kLn2 : -INFINITY;
+  for (int mb = 0; mb < kD / 16; ++mb)
+    *(floatx4*)&so[(wave * kDecMaxGroup + (lane & 15)) * kD + 16 * mb + 4 * (lane >> 4)] = o[mb];
+  __syncthreads();
+  for (int x = tid; x < group * (kD / 2); x += kThreads) {
+    const int hl = x / (kD / 2), d = 2 * (x % (kD / 2));
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = sm[w * kDecMaxGroup + hl];
+      M = fmaxf(M, mw[w]);
+    }
+    float lt = 0.f, o0 = 0.f, o1 = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+        lt += f * sl[w * kDecMaxGroup + hl];
+        o0 += f * so[(w * kDecMaxGroup + hl) * kD + d];
+        o1 += f * so[(w * kDecMaxGroup + hl) * kD + d + 1];
+      }
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t row = (int64_t)b * a.Hq + g * group + hl;
+    *(halfx2*)(a.out + row * kD + d) = halfx2{(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
+    if (a.lse && d == 0) a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
 // ---------------------------------------------------------------- extend --
 
 constexpr int kQBlock = 64;  // queries per workgroup and head
-
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 struct ExtArgs {
   const uint16_t* q;  // [N, Hq, 128]
@@ -247,11 +358,6 @@ struct ExtArgs {
   uint16_t* out;  // [N, Hq, 128]
   float* lse;     // [N, Hq] (nullable)
 };
-
-// the row a bad key loads: zeros keep P V finite where P = 0
-__device__ __attribute__((aligned(16))) uint8_t g_zero_head_row[kRowBytes] = {};
-
-constexpr int kStageBytes = 2 * kTile * kRowBytes;  // K then V, 32 KiB
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void extend_attention_kernel(ExtArgs a) {
@@ -507,7 +613,7 @@ extern "C" int stp_paged_gqa_decode(const uint16_t* q, const uint16_t* k_pool,
                                     uint16_t* out, float* lse, hipStream_t stream) {
   using stp::fail;
   if (int rc = check_dense("paged_gqa_decode", q, k_pool, v_pool, num_slots, B, Hq, Hkv, head_dim,
-                           scale, 8))
+                           scale, kDecMaxGroup))
     return rc;
   if (page_size < 1 || max_blocks < 0)
     return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: page_size %d / max_blocks %d", page_size,

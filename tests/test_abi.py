@@ -78,11 +78,11 @@ def test_host_side_validation():
     assert lib.stp_row_gather(fake, 10, 1152, fake, None, 8, 0, 1, 1, fake, None) == 0  # T = 0
     assert lib.stp_row_gather_blocks(32, 4, 2) == 256
     assert lib.stp_row_gather_blocks(33, 8, 1) == 320
-    # dense paged attention: head_dim 128 only, whole groups of at most 8 (decode)
+    # dense paged attention: head_dim 128 only, whole groups of at most 16 (decode)
     # or 4 (extend) query heads per KV head, positive finite scale, page size >= 1
     dec = lib.stp_paged_gqa_decode
     assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 64, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 36, 4, 128, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 68, 4, 128, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 30, 8, 128, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 0, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 16, 0.0, fake, None, None) == STP_ERR_INVALID_ARG

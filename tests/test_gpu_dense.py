@@ -27,7 +27,7 @@ def _pools(case):
     return k, v, to_dev(k), to_dev(v)
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 1), (32, 8), (8, 4), (4, 4), (6, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (32, 8), (8, 4), (4, 4), (6, 2), (16, 1)])
 def test_decode_small_ragged(hq, hkv):
     import sparse_top_paged_amd as stp
     case = workloads.random_gqa_decode_case(hq * 10 + hkv, [0, 1, 15, 64, 65, 300, 1000, -3],
@@ -54,6 +54,20 @@ def test_decode_tokens_past_table():
     o_ref, l_ref = oracle.paged_gqa_decode(case.q, k, v, table, case.ctx_lens, case.page_size,
                                            case.scale)
     assert_fp16_attention_close(out, lse, o_ref, l_ref, "past table")
+
+
+def test_decode_long_context_small_pages():
+    """Page size 1 and 5000 tokens: the block table is read in several chunks."""
+    import sparse_top_paged_amd as stp
+    case = workloads.random_gqa_decode_case(91, [5000, 4097, 2048, 2049], hq=8, hkv=2, page_size=1,
+                                            unmapped_frac=0.05)
+    k, v, kd, vd = _pools(case)
+    out, lse = stp.paged_gqa_decode(to_dev(case.q), kd, vd, to_dev(case.block_table),
+                                    to_dev(case.ctx_lens), case.page_size, case.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.paged_gqa_decode(case.q, k, v, case.block_table, case.ctx_lens,
+                                           case.page_size, case.scale)
+    assert_fp16_attention_close(out, lse, o_ref, l_ref, case.name)
 
 
 def test_decode_full_size_sampled():
