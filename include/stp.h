@@ -323,15 +323,30 @@ int32_t stp_row_gather_blocks(int32_t T, int32_t parts, int32_t replicas);
  * < 0, or t / page_size >= max_blocks, is an unmapped page), and
  *   out[b, h, :] = softmax_t(scale * <q[b, h], K[slot_t, h / group]>) V[slot_t, h / group]
  * Layouts: q, out [B, Hq, 128]; block_table [B, max_blocks] int32; ctx_lens
- * [B] int32; lse [B, Hq] (nullable).  Hq / Hkv <= 16.  One workgroup per
- * (request, KV head) reads each K / V tile once for every query head of its
- * group.
+ * [B] int32; lse [B, Hq] (nullable).  Hq / Hkv <= 16, page_size <= 2^20.
+ * One workgroup per (request, KV head, partition) reads each K / V tile once
+ * for every query head of its group.  num_splits: 0 = choose automatically
+ * (from B, Hkv, max_blocks * page_size and the current device's compute
+ * units), otherwise the number of equal token ranges (partitions, the
+ * vLLM v2 PARTITION_SIZE idea of §1.4) each request's table is cut into; a
+ * performance hint that changes the result only by float rounding.  More
+ * than one partition needs stp_paged_gqa_decode_workspace() bytes of
+ * workspace (STP_ERR_WORKSPACE if smaller), reusable once the call's work
+ * has completed on `stream`.
  */
 int stp_paged_gqa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                          int64_t num_slots, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                         int32_t head_dim, int32_t page_size, float scale, uint16_t* out,
-                         float* lse, hipStream_t stream);
+                         int32_t head_dim, int32_t page_size, float scale, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                         hipStream_t stream);
+
+/* Partitions stp_paged_gqa_decode uses for num_splits (0 = auto) at this
+ * shape on the current device, and the workspace bytes it then needs. */
+int32_t stp_paged_gqa_decode_splits(int32_t B, int32_t Hkv, int32_t max_blocks, int32_t page_size,
+                                    int32_t num_splits);
+size_t stp_paged_gqa_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_blocks,
+                                      int32_t page_size, int32_t num_splits);
 
 /*
  * Extend (prefill over a cached prefix): request b has Lq = qo_indptr[b+1] -

@@ -18,7 +18,8 @@ __all__ = [
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
-    "paged_gqa_decode", "extend_attention",
+    "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
+    "extend_attention",
 ]
 
 
@@ -303,8 +304,16 @@ def _pool(k_pool, v_pool):
     return k_pool.device, k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
 
 
-def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale=None, out=None,
-                     lse=None):
+def paged_gqa_decode_splits(B, Hkv, max_blocks, page_size, num_splits=0):
+    return lib.stp_paged_gqa_decode_splits(B, Hkv, max_blocks, page_size, num_splits)
+
+
+def paged_gqa_decode_workspace_bytes(B, Hq, Hkv, max_blocks, page_size, num_splits=0):
+    return lib.stp_paged_gqa_decode_workspace(B, Hq, Hkv, max_blocks, page_size, num_splits)
+
+
+def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale=None,
+                     num_splits=0, workspace=None, out=None, lse=None):
     """Dense paged decode with grouped query heads.  q [B, Hq, 128] fp16,
     k_pool / v_pool [slots, Hkv, 128] fp16, block_table [B, max_blocks] int32,
     ctx_lens [B] int32.  Returns (out [B, Hq, 128] fp16, lse [B, Hq] float32)."""
@@ -319,11 +328,18 @@ def paged_gqa_decode(q, k_pool, v_pool, block_table, ctx_lens, page_size, scale=
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = paged_gqa_decode_workspace_bytes(B, Hq, Hkv, block_table.shape[1], page_size,
+                                            num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", torch.uint8, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     check(lib.stp_paged_gqa_decode(
         _dev(q, "q", torch.float16, dev), _dev(k_pool, "k_pool", torch.float16, dev),
         _dev(v_pool, "v_pool", torch.float16, dev), slots,
         _dev(block_table, "block_table", torch.int32, dev), block_table.shape[1],
         _dev(ctx_lens, "ctx_lens", torch.int32, dev), B, Hq, Hkv, D, page_size, float(scale),
+        num_splits, ws_ptr, ws_bytes,
         _dev(out, "out", torch.float16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
     return out, lse
 

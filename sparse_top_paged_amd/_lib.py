@@ -45,7 +45,10 @@ SIGNATURES = {
     "stp_row_gather": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "stp_row_gather_blocks": (_i32, [_i32, _i32, _i32]),
     "stp_paged_gqa_decode": (ctypes.c_int, [
-        _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),
+        _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz,
+        _p, _p, _p]),
+    "stp_paged_gqa_decode_splits": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "stp_paged_gqa_decode_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "stp_extend_attention": (ctypes.c_int, [
         _p, _p, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),
 }

@@ -116,14 +116,7 @@ enum OutMode : int {
   kOutPartialBf16 = 2  // per split: o / l (bf16), m, l
 };
 
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
+using stp::static_for;
 
 using stp::lds_barrier;
 using stp::wait_vmcnt;
@@ -692,20 +685,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
   }
 }
 
-// Compute units of the current device (queried once per device).
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
+using stp::device_cus;
 
 // Automatic split count: one workgroup per compute unit at a time, so the
 // launch takes ceil(workgroups / CUs) rounds of (fixed per-workgroup cost +

@@ -11,16 +11,18 @@
 // (the bshd token-pool layout).
 //
 // Pool: keys and values as [slots, Hkv, 128] fp16, one 256-byte row per slot
-// and KV head.  Both kernels stage 64-key tiles in LDS through registers:
-// the loads of tile i + 1 are issued before tile i is computed and written
-// to LDS after it, so their latency hides behind the compute.  Bad slots
-// (unmapped page, outside the pool) load nothing and are masked.
+// and KV head.  Tiles of 64 keys (K and V, 32 KiB) are staged in LDS with a
+// 16-byte chunk swizzle; bad slots (unmapped page, outside the pool, past
+// the context) load a zero row and are masked before the exponent.
 //
-// decode: one 256-thread workgroup per (request, KV head).  Lane = token for
-// the scores (v_dot2_f32_f16 against the query heads held in registers, one
-// or two heads per wave), lane = two output values for the PV sum; online
-// softmax in base 2 per head.  At four query heads per KV head there is too
-// little width for the matrix cores, and the kernel is bound by the KV bytes.
+// decode: one 256-thread workgroup per (request, KV head, partition), two
+// workgroups per compute unit.  Tiles are prefetched two ahead into
+// registers and written to a double-buffered LDS tile; each wave takes 16
+// keys of a tile for all heads of the group at once: S^T = K Q^T and
+// O^T += V^T P^T on 16x16 MFMAs with the query heads as N (up to 16), P^T
+// taken from the S^T accumulator registers as they are.  The four waves'
+// softmax states are merged at the end; partitions of long contexts write
+// partial states merged by a second kernel.  Bound by the KV bytes.
 //
 // extend: one 256-thread workgroup per (request, KV head, 64-query block);
 // wave w computes query head g * group + w (group <= 4), every wave loads.
@@ -31,6 +33,8 @@
 // V^T P^T with 32 more MFMAs (A = V^T from a transposed LDS tile, B = P^T
 // built from the S^T accumulators in place).  Tiles wholly inside the prefix
 // rectangle skip the mask; the loop ends at the block's last visible key.
+
+#include <algorithm>
 
 #include "stp_internal.h"
 
@@ -80,6 +84,7 @@ using stp::load_lds_16;
 using stp::pair_max;
 using stp::pair_sum;
 using stp::scale_acc;
+using stp::static_for;
 using stp::wait_vmcnt;
 
 // the row a bad key loads: zeros keep P V finite where P = 0
@@ -115,8 +120,15 @@ __device__ __forceinline__ void issue_kv_rows(const uint8_t* kpool, const uint8_
 
 // ---------------------------------------------------------------- decode --
 
-constexpr int kDecStages = 4;      // tiles in the LDS ring (three in flight)
 constexpr int kTabChunk = 2048;    // block-table entries staged in LDS at a time
+#ifndef STP_DEC_RING
+#define STP_DEC_RING 2
+#endif
+#ifndef STP_DEC_WAVES
+#define STP_DEC_WAVES 2
+#endif
+constexpr int kDecRing = STP_DEC_RING;    // tiles prefetched into registers
+constexpr int kDecWaves = STP_DEC_WAVES;  // waves per SIMD (workgroups per CU)
 constexpr int kDecMaxGroup = 16;   // query heads per KV head (the MFMA N width)
 
 struct DecArgs {
@@ -128,21 +140,27 @@ struct DecArgs {
   int max_blocks;
   const int32_t* ctx;    // [B]
   int B, Hq, Hkv, P;
+  int S, part;  // KV partitions per request and their length in tokens (a multiple of 64)
   float scale_log2;
   uint16_t* out;  // [B, Hq, 128]
   float* lse;     // [B, Hq] (nullable)
+  float* o_part;  // S > 1: [B, S, Hq, 128] unnormalised, against m_part
+  float* m_part;  // [B, S, Hq], base-2 exponent units
+  float* l_part;  // [B, S, Hq]
 };
 
 struct DecLds {
-  char tiles[kDecStages * kStageBytes];  // reused for the wave merge at the end
+  char tiles[2 * kStageBytes];  // double buffer; reused for the wave merge at the end
   int32_t tab[kTabChunk];
-  uint8_t ok[kDecStages][kTile];
+  uint8_t ok[2][kTile];
 };
 
-// One workgroup per (request, KV head), four waves.  Wave w takes keys
-// 16 w .. 16 w + 15 of every 64-key tile and keeps its own softmax state for
-// the group's heads; the four states are merged at the end.  Per tile and
-// wave:
+// One workgroup per (request, KV head, partition), four waves.  Tiles of 64
+// keys (32 KiB of K and V) are prefetched kRing tiles ahead into registers
+// (thread: 16 B of each of 4 keys, K and V), written to a double-buffered
+// LDS tile when their turn comes, one barrier per tile.  Wave w takes keys
+// 16 w .. 16 w + 15 of every tile and keeps its own softmax state for the
+// group's heads; the four states are merged at the end.  Per tile and wave:
 //   S^T[16 keys x 16 heads] = K Q^T with 4 v_mfma_f32_16x16x32_f16 (A = K
 //     rows from LDS, B = Q^T in registers, heads past the group are zero);
 //   lane l holds head l % 16, keys 4 (l / 16) .. + 3: the column max and sum
@@ -150,17 +168,24 @@ struct DecLds {
 //   O^T[128 x 16 heads] += V^T P^T with 8 v_mfma_f32_16x16x16_f16: A = V^T by
 //     ds_read_b64_tr_b16 (lane group gq reads keys 4 gq .. + 3, the keys the
 //     accumulator holds), B = P^T, the lane's own four softmax weights.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int kRing, int kWaves>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves, kWaves)))
 void paged_gqa_decode_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(1024))) DecLds L;
-  const int b = blockIdx.x / a.Hkv, g = blockIdx.x - (blockIdx.x / a.Hkv) * a.Hkv;
+  const int bg = blockIdx.x / a.S, p = blockIdx.x - (blockIdx.x / a.S) * a.S;
+  const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = a.Hq / a.Hkv;
-  const int n = min(max(a.ctx[b], 0), a.max_blocks * a.P);
-  const int ntiles = (n + kTile - 1) / kTile;
+  const int n_all = min(max(a.ctx[b], 0), a.max_blocks * a.P);
+  // this partition's tokens [t0, n)
+  const int t0 = p * a.part;
+  const int n = min(n_all, t0 + a.part);
+  const int ntiles = n > t0 ? (n - t0 + kTile - 1) / kTile : 0;
   const int nb = (n + a.P - 1) / a.P;  // table entries in use
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   const int64_t head_bytes = (int64_t)a.Hkv * kRowBytes;
+  const uint8_t* kpool = (const uint8_t*)a.k + g * kRowBytes;
+  const uint8_t* vpool = (const uint8_t*)a.v + g * kRowBytes;
   const uint8_t* zero_row = g_zero_head_row;
   asm volatile("" : "+s"(zero_row));
   const uint32_t tiles_base = (uint32_t)(uintptr_t)(lds_t*)L.tiles;
@@ -174,29 +199,50 @@ void paged_gqa_decode_kernel(DecArgs a) {
     }
     chunk = c;
   };
-  // slots of this lane's four keys of tile j (-1: past n, unmapped, outside the pool)
-  auto slots_of = [&](int j, int64_t (&sl)[4]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = j * kTile + 16 * wave + 4 * u + (lane >> 4);
-      sl[u] = -1;
-      if (t < n) {
-        const int blk = t / a.P;
-        const int page = L.tab[blk - chunk * kTabChunk];
-        const int64_t s = (int64_t)page * a.P + (t - blk * a.P);
-        sl[u] = (page >= 0 && s < a.slots) ? s : -1;
-      }
+  // the chunk that holds tile j's table entries (a tile never straddles two);
+  // called by all threads before they fetch tile j
+  auto ensure_chunk = [&](int j) {
+    const int c = (t0 + j * kTile) / tab_tokens;
+    if (c != chunk) {
+      __syncthreads();  // every fetch from the current chunk is done
+      load_chunk(c);
+      __syncthreads();
     }
   };
-  auto issue = [&](int j) {
-    int64_t sl[4];
-    slots_of(j, sl);
-    const int st = j % kDecStages;
-    issue_kv_rows((const uint8_t*)a.k, (const uint8_t*)a.v, head_bytes, g, zero_row,
-                  tiles_base + st * kStageBytes, wave, lane, sl);
+  // loader role: chunk lc of keys lt + 16 u (u = 0..3) of a tile
+  const int lc = tid & 15, lt = tid >> 4;
+  uintx4 kr[kRing][4], vr[kRing][4];
+  uint32_t okb[kRing];
+  // loads of tile j into register set r; keys past n, unmapped or outside the
+  // pool load the zero row and are flagged
+  auto fetch = [&](int j, uintx4 (&kk)[4], uintx4 (&vv)[4], uint32_t& ok) {
+    ok = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if ((lane & 15) == 0) L.ok[st][16 * wave + 4 * u + (lane >> 4)] = sl[u] >= 0 ? 1 : 0;
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + j * kTile + lt + 16 * u;
+      int64_t s = -1;
+      if (t < n) {
+        const int blk = t / a.P;
+        const int e = blk - chunk * kTabChunk;
+        const int page = (e >= 0 && e < kTabChunk) ? L.tab[e] : -1;
+        s = (int64_t)page * a.P + (t - blk * a.P);
+        s = (page >= 0 && s < a.slots) ? s : -1;
+      }
+      const int64_t off = s * head_bytes + 16 * lc;
+      kk[u] = *(const uintx4*)(s >= 0 ? kpool + off : zero_row + 16 * lc);
+      vv[u] = *(const uintx4*)(s >= 0 ? vpool + off : zero_row + 16 * lc);
+      ok |= (s >= 0 ? 1u : 0u) << u;
+    }
+  };
+  auto stage_write = [&](int st, const uintx4 (&kk)[4], const uintx4 (&vv)[4], uint32_t ok) {
+    lds_t* kt = (lds_t*)L.tiles + st * kStageBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = lt + 16 * u;
+      *(__attribute__((address_space(3))) uintx4*)(kt + tile_off(t, lc)) = kk[u];
+      *(__attribute__((address_space(3))) uintx4*)(kt + kTile * kRowBytes + tile_off(t, lc)) = vv[u];
+      if (lc == 0) L.ok[st][t] = (ok >> u) & 1;
+    }
   };
 
   // Q^T fragments (B of S^T = K Q^T): head l % 16 of the group, values
@@ -229,32 +275,7 @@ void paged_gqa_decode_kernel(DecArgs a) {
   for (int mb = 0; mb < kD / 16; ++mb) o[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, lsum = 0.f;  // head l % 16; lsum over this lane's keys
 
-  // prologue: table chunk 0, tiles 0 .. kDecStages - 2 in flight
-  if (ntiles > 0) load_chunk(0);
-  __syncthreads();
-  for (int j = 0; j < kDecStages - 1 && j < ntiles; ++j) issue(j);
-
-  for (int it = 0; it < ntiles; ++it) {
-    // tile it has landed once at most min(S - 2, ntiles - 1 - it) newer tiles
-    // are in flight (8 loads per wave each)
-    const int newer = min(kDecStages - 2, ntiles - 1 - it);
-    if (newer >= 2)
-      wait_vmcnt<16>();
-    else if (newer == 1)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();  // tile it visible; every wave is done with tile it - 1
-    const int jn = it + kDecStages - 1;
-    if (jn < ntiles) {
-      if (jn * kTile >= (chunk + 1) * tab_tokens) {
-        // next block-table chunk: every issue from the current one is done
-        load_chunk(jn * kTile / tab_tokens);
-        __syncthreads();
-      }
-      issue(jn);  // into the stage of tile it - 1
-    }
-    const int st = it % kDecStages;
+  auto compute = [&](int st) {
     const uint32_t sbase = tiles_base + st * kStageBytes;
     // S^T for keys 16 w .. + 15
     floatx4 s = {0.f, 0.f, 0.f, 0.f};
@@ -287,9 +308,9 @@ void paged_gqa_decode_kernel(DecArgs a) {
     halfx4 pf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] + neg_m);
-      lsum += p;
-      pf[r] = (_Float16)p;
+      const float pe = __builtin_amdgcn_exp2f(s[r] + neg_m);
+      lsum += pe;
+      pf[r] = (_Float16)pe;
     }
 #pragma unroll
     for (int mb = 0; mb < kD / 16; ++mb) {
@@ -298,13 +319,41 @@ void paged_gqa_decode_kernel(DecArgs a) {
       o[mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(halfx4, vf), pf, o[mb], 0, 0,
                                                     0);
     }
+  };
+
+  // prologue: tiles 0 .. kRing - 1 in flight
+  static_for<kRing>([&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    if (r < ntiles) {
+      ensure_chunk(r);
+      fetch(r, kr[r], vr[r], okb[r]);
+    }
+  });
+  for (int base = 0; base < ntiles; base += kRing) {
+    static_for<kRing>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const int i = base + r;
+      if (i < ntiles) {
+        const int st = i & 1;
+        // every wave finished tile i - 2, the last user of this stage, before
+        // the barrier of tile i - 1
+        stage_write(st, kr[r], vr[r], okb[r]);
+        const int jn = i + kRing;
+        if (jn < ntiles) {
+          ensure_chunk(jn);
+          fetch(jn, kr[r], vr[r], okb[r]);
+        }
+        lds_barrier();  // tile i visible
+        compute(st);
+      }
+    });
   }
 
   // merge the four waves' states: M = max m_w, out = sum 2^(m_w - M) O_w /
   // sum 2^(m_w - M) l_w
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // the ring is free (every tile consumed)
+  __syncthreads();  // every wave is done with the tiles
   float* sm = (float*)L.tiles;           // [4 waves][16 heads]
   float* sl = sm + 4 * kDecMaxGroup;     // [4][16]
   float* so = sl + 4 * kDecMaxGroup;     // [4][16 heads][128]
@@ -334,11 +383,51 @@ void paged_gqa_decode_kernel(DecArgs a) {
         o1 += f * so[(w * kDecMaxGroup + hl) * kD + d + 1];
       }
     }
+    if (a.S > 1) {  // partial state of this partition
+      const int64_t row = ((int64_t)b * a.S + p) * a.Hq + g * group + hl;
+      *(float2*)(a.o_part + row * kD + d) = make_float2(o0, o1);
+      if (d == 0) {
+        a.m_part[row] = M;
+        a.l_part[row] = lt;
+      }
+      continue;
+    }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t row = (int64_t)b * a.Hq + g * group + hl;
     *(halfx2*)(a.out + row * kD + d) = halfx2{(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
     if (a.lse && d == 0) a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
   }
+}
+
+// Merge of the partitions' states, one 64-thread slice per (request, head):
+// M = max over partitions with l > 0 of m_p, out = sum 2^(m_p - M) o_p /
+// sum 2^(m_p - M) l_p ("PagedAttention 与 RadixAttention" §1.4 part 3).
+__global__ __launch_bounds__(kThreads) void paged_gqa_merge_kernel(DecArgs a) {
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= a.Hq) return;
+  const int b = blockIdx.x, d = 2 * (threadIdx.x & 63);
+  float M = -INFINITY;
+  for (int p = 0; p < a.S; ++p) {
+    const int64_t row = ((int64_t)b * a.S + p) * a.Hq + h;
+    if (a.l_part[row] > 0.f) M = fmaxf(M, a.m_part[row]);
+  }
+  float lt = 0.f, o0 = 0.f, o1 = 0.f;
+  if (M != -INFINITY) {
+    for (int p = 0; p < a.S; ++p) {
+      const int64_t row = ((int64_t)b * a.S + p) * a.Hq + h;
+      const float l = a.l_part[row];
+      if (!(l > 0.f)) continue;
+      const float f = __builtin_amdgcn_exp2f(a.m_part[row] - M);
+      const float2 o = *(const float2*)(a.o_part + row * kD + d);
+      lt += f * l;
+      o0 += f * o.x;
+      o1 += f * o.y;
+    }
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int64_t row = (int64_t)b * a.Hq + h;
+  *(halfx2*)(a.out + row * kD + d) = halfx2{(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
+  if (a.lse && d == 0) a.lse[row] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- extend --
@@ -399,20 +488,11 @@ void extend_attention_kernel(ExtArgs a) {
     return (s >= 0 && s < a.slots) ? s : -1;
   };
   auto issue = [&](const int64_t (&sl)[4], int stage) {
-    const uint32_t base = (uint32_t)(uintptr_t)(lds_t*)s_tiles + stage * kStageBytes;
+    issue_kv_rows((const uint8_t*)a.k, (const uint8_t*)a.v, head_bytes, g, zero_row,
+                  (uint32_t)(uintptr_t)(lds_t*)s_tiles + stage * kStageBytes, wave, lane, sl);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = my_key0 + 4 * u;
-      const int c = (lane & 15) ^ (t & 15);
-      const uint8_t* kp = sl[u] >= 0 ? (const uint8_t*)a.k + sl[u] * head_bytes + g * kRowBytes + 16 * c
-                                     : zero_row + 16 * c;
-      const uint8_t* vp = sl[u] >= 0 ? (const uint8_t*)a.v + sl[u] * head_bytes + g * kRowBytes + 16 * c
-                                     : zero_row + 16 * c;
-      const uint32_t row0 = __builtin_amdgcn_readfirstlane(base + (16 * wave + 4 * u) * kRowBytes);
-      load_lds_16<0>(kp, row0);
-      load_lds_16<0>(vp, row0 + kTile * kRowBytes);
-      if ((lane & 15) == 0) s_ok[stage][t] = sl[u] >= 0 ? 1 : 0;
-    }
+    for (int u = 0; u < 4; ++u)
+      if ((lane & 15) == 0) s_ok[stage][my_key0 + 4 * u] = sl[u] >= 0 ? 1 : 0;
   };
 
   // Q^T fragments (B operand of S^T = K Q^T), kept in AGPRs: query
@@ -603,31 +683,91 @@ int check_dense(const char* what, const void* q, const void* k, const void* v, i
   return STP_OK;
 }
 
+// Partitions of the decode: equal token ranges of every request's table.
+// Two workgroups share a compute unit (registers and LDS allow two), and a
+// workgroup's fixed cost (filling its prefetch ring, the wave merge) makes
+// extra partitions a loss once the (request, KV head) workgroups fill about
+// two rounds of the device; below that, partitions of at least 8 tiles make
+// up the difference.
+void dense_split_plan(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t requested, int* S,
+                      int* part) {
+  const int64_t tiles = std::max<int64_t>(1, (max_tokens + kTile - 1) / kTile);
+  int64_t s;
+  if (requested > 0) {
+    s = std::min<int64_t>(requested, tiles);
+  } else {
+    const int64_t target = 2 * kDecWaves * (int64_t)stp::device_cus();
+    const int64_t wgs = std::max<int64_t>(1, (int64_t)B * Hkv);
+    s = wgs >= target ? 1 : std::min((target + wgs - 1) / wgs, (tiles + 7) / 8);
+  }
+  s = std::max<int64_t>(1, std::min<int64_t>(s, 4096));
+  const int64_t p_tiles = (tiles + s - 1) / s;
+  *S = (int)((tiles + p_tiles - 1) / p_tiles);
+  *part = (int)(p_tiles * kTile);
+}
+
+size_t dense_workspace(int32_t B, int32_t Hq, int S) {
+  return S > 1 ? (size_t)B * S * Hq * (kD + 2) * sizeof(float) : 0;
+}
+
 }  // namespace
+
+extern "C" int32_t stp_paged_gqa_decode_splits(int32_t B, int32_t Hkv, int32_t max_blocks,
+                                               int32_t page_size, int32_t num_splits) {
+  if (B < 0 || Hkv < 1 || max_blocks < 0 || page_size < 1) return 0;
+  int S, part;
+  dense_split_plan(B, Hkv, (int64_t)max_blocks * page_size, num_splits, &S, &part);
+  return S;
+}
+
+extern "C" size_t stp_paged_gqa_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv,
+                                                 int32_t max_blocks, int32_t page_size,
+                                                 int32_t num_splits) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || max_blocks < 0 || page_size < 1) return 0;
+  int S, part;
+  dense_split_plan(B, Hkv, (int64_t)max_blocks * page_size, num_splits, &S, &part);
+  return dense_workspace(B, Hq, S);
+}
 
 extern "C" int stp_paged_gqa_decode(const uint16_t* q, const uint16_t* k_pool,
                                     const uint16_t* v_pool, int64_t num_slots,
                                     const int32_t* block_table, int32_t max_blocks,
                                     const int32_t* ctx_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                     int32_t head_dim, int32_t page_size, float scale,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
                                     uint16_t* out, float* lse, hipStream_t stream) {
   using stp::fail;
   if (int rc = check_dense("paged_gqa_decode", q, k_pool, v_pool, num_slots, B, Hq, Hkv, head_dim,
                            scale, kDecMaxGroup))
     return rc;
-  if (page_size < 1 || max_blocks < 0)
+  if (page_size < 1 || page_size > (1 << 20) || max_blocks < 0)
     return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: page_size %d / max_blocks %d", page_size,
                 max_blocks);
-  if ((int64_t)max_blocks * page_size > INT32_MAX)
+  if ((int64_t)max_blocks * page_size > INT32_MAX - kTabChunk * (int64_t)page_size)
     return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: max_blocks * page_size exceeds int32");
-  if ((int64_t)B * Hkv > INT32_MAX) return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: grid");
+  if (num_splits < 0) return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: num_splits < 0");
   if (B == 0) return STP_OK;
   if (!ctx_lens || !out || (max_blocks > 0 && !block_table))
     return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: null pointer");
+  int S, part;
+  dense_split_plan(B, Hkv, (int64_t)max_blocks * page_size, num_splits, &S, &part);
+  const size_t need = dense_workspace(B, Hq, S);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(STP_ERR_WORKSPACE, "paged_gqa_decode: workspace of %zu bytes needed", need);
+  if ((int64_t)B * Hkv * S > INT32_MAX) return fail(STP_ERR_INVALID_ARG, "paged_gqa_decode: grid");
+  float* ws = (float*)workspace;
+  const size_t rows = (size_t)B * S * Hq;
   DecArgs a{q, k_pool, v_pool, num_slots, block_table, max_blocks, ctx_lens, B, Hq, Hkv,
-            page_size, scale * kLog2e, out, lse};
-  paged_gqa_decode_kernel<<<B * Hkv, kThreads, 0, stream>>>(a);
-  return stp::check_launch("paged_gqa_decode_kernel");
+            page_size, S, part, scale * kLog2e, out, lse,
+            S > 1 ? ws : nullptr, S > 1 ? ws + rows * kD : nullptr,
+            S > 1 ? ws + rows * (kD + 1) : nullptr};
+  paged_gqa_decode_kernel<kDecRing, kDecWaves><<<B * Hkv * S, kThreads, 0, stream>>>(a);
+  if (int rc = stp::check_launch("paged_gqa_decode_kernel")) return rc;
+  if (S > 1) {
+    paged_gqa_merge_kernel<<<dim3(B, (Hq + 3) / 4), kThreads, 0, stream>>>(a);
+    return stp::check_launch("paged_gqa_merge_kernel");
+  }
+  return STP_OK;
 }
 
 extern "C" int stp_extend_attention(const uint16_t* q, const uint16_t* k_pool,

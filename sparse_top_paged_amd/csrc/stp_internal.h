@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "stp.h"
 
 namespace stp {
@@ -13,6 +15,10 @@ int fail(int status, const char* fmt, ...);
 
 // Checks the launch that was just enqueued.
 int check_launch(const char* what);
+
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+int device_cus();
 
 constexpr int kWave = 64;
 
@@ -56,6 +62,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   __syncthreads();
   *total = tot;
   return off + x - v;
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 template <int N>

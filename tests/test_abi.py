@@ -81,12 +81,20 @@ def test_host_side_validation():
     # dense paged attention: head_dim 128 only, whole groups of at most 16 (decode)
     # or 4 (extend) query heads per KV head, positive finite scale, page size >= 1
     dec = lib.stp_paged_gqa_decode
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 64, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 68, 4, 128, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 30, 8, 128, 16, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 0, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 16, 0.0, fake, None, None) == STP_ERR_INVALID_ARG
-    assert dec(fake, fake, fake, 64, fake, 4, fake, 0, 32, 8, 128, 16, 0.1, fake, None, None) == 0
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 64, 16, 0.1, 0, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 68, 4, 128, 16, 0.1, 0, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 30, 8, 128, 16, 0.1, 0, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 0, 0.1, 0, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 16, 0.0, 0, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 0, 32, 8, 128, 16, 0.1, 0, None, 0, fake, None, None) == 0
+    # more than one partition without workspace, negative split count
+    assert dec(fake, fake, fake, 64, fake, 64, fake, 2, 32, 8, 128, 16, 0.1, 4, None, 0, fake, None, None) == STP_ERR_WORKSPACE
+    assert dec(fake, fake, fake, 64, fake, 4, fake, 2, 32, 8, 128, 16, 0.1, -1, None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    assert lib.stp_paged_gqa_decode_splits(128, 8, 256, 16, 0) >= 1
+    assert lib.stp_paged_gqa_decode_splits(2, 8, 256, 16, 3) == 3
+    assert lib.stp_paged_gqa_decode_splits(2, 8, 1, 16, 5) == 1     # one tile: one partition
+    assert lib.stp_paged_gqa_decode_workspace(2, 32, 8, 256, 16, 1) == 0
+    assert lib.stp_paged_gqa_decode_workspace(2, 32, 8, 256, 16, 4) == 2 * 4 * 32 * 130 * 4
     ext = lib.stp_extend_attention
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 4, 128, 64, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 8, 96, 64, 0.1, fake, None, None) == STP_ERR_INVALID_ARG

@@ -70,15 +70,35 @@ def test_decode_long_context_small_pages():
     assert_fp16_attention_close(out, lse, o_ref, l_ref, case.name)
 
 
+@pytest.mark.parametrize("num_splits", [1, 2, 7, 40])
+def test_decode_partitions(num_splits):
+    """Partitions of the token range (some empty for the shorter requests,
+    some crossing a block-table chunk), merged; page size 1 and 5000 tokens."""
+    import sparse_top_paged_amd as stp
+    case = workloads.random_gqa_decode_case(93, [5000, 4097, 130, 0, 2049], hq=16, hkv=4,
+                                            page_size=1, unmapped_frac=0.05)
+    k, v, kd, vd = _pools(case)
+    assert stp.paged_gqa_decode_splits(5, 4, case.block_table.shape[1], 1, num_splits) == num_splits
+    out, lse = stp.paged_gqa_decode(to_dev(case.q), kd, vd, to_dev(case.block_table),
+                                    to_dev(case.ctx_lens), case.page_size, case.scale,
+                                    num_splits=num_splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.paged_gqa_decode(case.q, k, v, case.block_table, case.ctx_lens,
+                                           case.page_size, case.scale)
+    assert_fp16_attention_close(out, lse, o_ref, l_ref, f"{case.name} splits {num_splits}")
+
+
 def test_decode_full_size_sampled():
     import sparse_top_paged_amd as stp
     t0 = time.time()
     case = workloads.gqa_decode_case()
     kd, vd = workloads.dense_pool_torch(case.num_slots, case.hkv, case.pool_seed, dev())
+    S = stp.paged_gqa_decode_splits(len(case.ctx_lens), case.hkv, case.block_table.shape[1],
+                                    case.page_size)
     out, lse = stp.paged_gqa_decode(to_dev(case.q), kd, vd, to_dev(case.block_table),
                                     to_dev(case.ctx_lens), case.page_size, case.scale)
     torch.cuda.synchronize()
-    print(f"[dense decode full] ran at {time.time() - t0:.1f} s", flush=True)
+    print(f"[dense decode full] {S} partitions, ran at {time.time() - t0:.1f} s", flush=True)
     assert torch.isfinite(out.float()).all()
     order = np.argsort(case.ctx_lens)
     sample = sorted({0, 57, 127, int(order[0]), int(order[-1])})
