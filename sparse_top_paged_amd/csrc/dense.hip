@@ -56,10 +56,14 @@ typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_t;
 
-// K (and decode V) tile: 64 keys x 16 chunks of 16 B, chunk c of key t at
-// t * 256 + ((c ^ (t % 16)) * 16): a wave reading one chunk of 64 keys, or
-// 64 lanes reading 4 bytes each of one key, stays within few banks per pass.
-__device__ __forceinline__ int tile_off(int t, int c) { return t * kRowBytes + ((c ^ (t & 15)) << 4); }
+// K and V tiles: 64 keys x 16 chunks of 16 B, chunk c of key t at
+// t * 256 + ((c ^ swz(t)) * 16), swz(t) the two 2-bit halves of t % 16
+// swapped.  Rows are 256 B, one full turn of the banks, so the swizzle alone
+// spreads a read: 16 consecutive keys of one chunk (the K fragments) land on
+// 16 different chunk positions, and so do 4 consecutive keys x 4 consecutive
+// chunks (a half-wave of V^T transpose reads).
+__device__ __forceinline__ int key_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int t, int c) { return t * kRowBytes + ((c ^ key_swz(t)) << 4); }
 
 // Word e of a 16-byte vector as two halves.  The word is copied to a scalar
 // first: hipcc's __builtin_bit_cast applied to a vector component directly
@@ -99,7 +103,7 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // Tile loads go straight to LDS, 1 KiB (4 keys) per wave instruction:
 // instruction u of wave w fills keys 16 w + 4 u + lane / 16 of the tile, LDS
 // chunk position lane % 16, so the lane fetches row chunk
-// (lane % 16) ^ (key % 16) -- the swizzled tile layout.  K and V of one key
+// (lane % 16) ^ swz(key) -- the swizzled tile layout.  K and V of one key
 // share the slot.  slot < 0 loads the zero row.
 __device__ __forceinline__ void issue_kv_rows(const uint8_t* kpool, const uint8_t* vpool,
                                               int64_t head_bytes, int g, const uint8_t* zero_row,
@@ -108,7 +112,7 @@ __device__ __forceinline__ void issue_kv_rows(const uint8_t* kpool, const uint8_
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int t = 16 * wave + 4 * u + (lane >> 4);
-    const int c = (lane & 15) ^ (t & 15);
+    const int c = (lane & 15) ^ key_swz(t);
     const int64_t off = sl[u] * head_bytes + g * kRowBytes + 16 * c;
     const uint8_t* kp = sl[u] >= 0 ? kpool + off : zero_row + 16 * c;
     const uint8_t* vp = sl[u] >= 0 ? vpool + off : zero_row + 16 * c;
@@ -259,16 +263,16 @@ void paged_gqa_decode_kernel(DecArgs a) {
     }
   }
   // K fragment (A of S^T): key 16 w + l % 16, chunk 4 ks + l / 16; the
-  // key's swizzle is l % 16, so ks steps are an XOR of ks << 6.
+  // key's swizzle is swz(l % 16), so ks steps are an XOR of ks << 6.
   const uint32_t k_off = (16 * wave + (lane & 15)) * kRowBytes +
-                         ((((lane >> 4) ^ (lane & 15)) & 15) << 4);
+                         (((lane >> 4) ^ key_swz(lane & 15)) << 4);
   // V^T fragment (A of O^T, transpose read): lane (gq, j16) points at key
   // 16 w + 4 gq + j16 / 4, values 16 mb + 4 (j16 % 4) .. + 3, i.e. chunk
   // 2 mb + (j16 % 4) / 2, byte 8 (j16 % 2); mb steps are an XOR of mb << 5.
   const int vq = lane >> 4, vj = lane & 15;
   const int v_tok = 4 * vq + (vj >> 2);
   const uint32_t v_off = kTile * kRowBytes + (16 * wave + v_tok) * kRowBytes +
-                         (((((vj & 3) >> 1) ^ v_tok) & 15) << 4) + 8 * (vj & 1);
+                         ((((vj & 3) >> 1) ^ key_swz(v_tok)) << 4) + 8 * (vj & 1);
 
   floatx4 o[kD / 16];
 #pragma unroll
@@ -432,7 +436,15 @@ __global__ __launch_bounds__(kThreads) void paged_gqa_merge_kernel(DecArgs a) {
 
 // ---------------------------------------------------------------- extend --
 
-constexpr int kQBlock = 64;  // queries per workgroup and head
+constexpr int kQBlock = 32;      // queries per workgroup and head
+constexpr int kExtStages = 2;    // LDS tile double buffer
+constexpr int kIdxChunk = 2048;  // slot ids staged in LDS at a time
+
+struct ExtLds {
+  char tiles[kExtStages * kStageBytes];
+  int32_t idx[kIdxChunk];
+  uint8_t ok[kExtStages][kTile];
+};
 
 struct ExtArgs {
   const uint16_t* q;  // [N, Hq, 128]
@@ -448,10 +460,20 @@ struct ExtArgs {
   float* lse;     // [N, Hq] (nullable)
 };
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// One workgroup per (request, KV head, 32-query block), two per compute
+// unit; wave w computes query head g * group + w (group <= 4) for the 32
+// queries, every wave loads.  Per 64-key tile and wave:
+//   S^T[64 keys x 32 queries] = K Q^T with 16 v_mfma_f32_32x32x16_f16 (A = K
+//     rows from LDS, B = Q^T in registers); lane l owns query l % 32 and
+//     keys 8 (r / 4) + 4 (l / 32) + r % 4 of each 32-key half, so a
+//     query's max and sum need only the partner lane l ^ 32;
+//   O^T[128 x 32] += V^T P^T with 16 more: A = V^T by ds_read_b64_tr_b16,
+//     B = P^T made from the S^T registers in place.
+// Tiles wholly inside every query's visible range skip the mask; the loop
+// ends at the block's last visible key.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void extend_attention_kernel(ExtArgs a) {
-  __shared__ __attribute__((aligned(1024))) char s_tiles[2 * kStageBytes];
-  __shared__ uint8_t s_ok[2][kTile];
+  __shared__ __attribute__((aligned(1024))) ExtLds L;
   // all query blocks of one (request, KV head) on one XCD (block id mod 8),
   // so the later ones read the shared K / V tiles from that XCD's L2
   const int bid = blockIdx.x;
@@ -476,48 +498,62 @@ void extend_attention_kernel(ExtArgs a) {
   const int64_t head_bytes = (int64_t)a.Hkv * kRowBytes;  // between slots
   const uint8_t* zero_row = g_zero_head_row;
   asm volatile("" : "+s"(zero_row));
+  const uint32_t tiles_base = (uint32_t)(uintptr_t)(lds_t*)L.tiles;
 
-  // Tile loads go straight to LDS, 1 KiB (4 keys) per wave instruction:
-  // instruction u of wave w fills keys 16 w + 4 u + lane / 16, LDS chunk
-  // position lane % 16, so the lane fetches row chunk (lane % 16) ^ (key % 16)
-  // -- the swizzled tile layout.
-  const int my_key0 = 16 * wave + (lane >> 4);  // + 4 u
-  auto slot_of = [&](int j) -> int64_t {
-    if (j >= jmax) return -1;
-    const int64_t s = a.kvi[k_base + j];
-    return (s >= 0 && s < a.slots) ? s : -1;
+  // The request's slot list is staged in LDS a chunk at a time (plain loads
+  // of it interleaved with the tile loads would make every use wait for the
+  // tile loads in flight).
+  const int my_key0 = 16 * wave + (lane >> 4);  // + 4 u, the keys this lane loads
+  int chunk = -1;
+  auto ensure_chunk = [&](int j) {  // all threads, before tile j's issue
+    const int c = j * kTile / kIdxChunk;
+    if (c != chunk) {
+      __syncthreads();  // every issue from the current chunk is done
+      for (int i = tid; i < kIdxChunk; i += kThreads) {
+        const int e = c * kIdxChunk + i;
+        L.idx[i] = e < jmax ? a.kvi[k_base + e] : -1;
+      }
+      chunk = c;
+      __syncthreads();
+    }
   };
-  auto issue = [&](const int64_t (&sl)[4], int stage) {
+  auto issue = [&](int j) {
+    ensure_chunk(j);
+    const int stage = j % kExtStages;
+    int64_t sl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = j * kTile + my_key0 + 4 * u - chunk * kIdxChunk;
+      const int64_t sv = (e >= 0 && e < kIdxChunk) ? L.idx[e] : -1;
+      sl[u] = (sv >= 0 && sv < a.slots) ? sv : -1;
+    }
     issue_kv_rows((const uint8_t*)a.k, (const uint8_t*)a.v, head_bytes, g, zero_row,
-                  (uint32_t)(uintptr_t)(lds_t*)s_tiles + stage * kStageBytes, wave, lane, sl);
+                  tiles_base + stage * kStageBytes, wave, lane, sl);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if ((lane & 15) == 0) s_ok[stage][my_key0 + 4 * u] = sl[u] >= 0 ? 1 : 0;
+      if ((lane & 15) == 0) L.ok[stage][my_key0 + 4 * u] = sl[u] >= 0 ? 1 : 0;
   };
 
-  // Q^T fragments (B operand of S^T = K Q^T), kept in AGPRs: query
-  // 32 qb + lane % 32 of the block, values 16 ks + 8 (lane / 32) .. + 7
-  halfx8 qf[2][kD / 16];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = i0 + 32 * qb + (lane & 31);
+  // Q^T fragments (B operand of S^T = K Q^T): query i0 + lane % 32, values
+  // 16 ks + 8 (lane / 32) .. + 7
+  const int qi = i0 + (lane & 31);
+  halfx8 qf[kD / 16];
+  {
     const uint16_t* qrow = a.q + ((int64_t)(q_base + min(qi, Lq - 1)) * a.Hq + h) * kD;
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
       const uintx4 w = qi < Lq ? *(const uintx4*)(qrow + 16 * ks + 8 * (lane >> 5))
                                : uintx4{0u, 0u, 0u, 0u};
-      qf[qb][ks] = __builtin_bit_cast(halfx8, w);
-      asm volatile("" : "+a"(qf[qb][ks]));
+      qf[ks] = __builtin_bit_cast(halfx8, w);
     }
   }
   // LDS addresses.  In the swizzled tile, chunk c of key t sits at
-  // t * 256 + ((c ^ (t % 16)) << 4); the stage bases are 32 KiB aligned, so
+  // t * 256 + ((c ^ swz(t)) << 4); the stage bases are 32 KiB aligned, so
   // stepping c by a multiple of 2 (or 4) is an XOR on bits 5..7 (6..7) of the
   // address and stepping t by a multiple of 16 an immediate offset.
   //  K fragment (A of S^T): key 32 kb + lane % 32, chunk 2 ks + lane / 32.
-  const uint32_t tiles_base = (uint32_t)(uintptr_t)(lds_t*)s_tiles;
   const int kq = lane & 31;
-  const uint32_t k_off = kq * kRowBytes + ((((lane >> 5) ^ kq) & 15) << 4);
+  const uint32_t k_off = kq * kRowBytes + (((lane >> 5) ^ key_swz(kq)) << 4);
   //  V^T fragment (ds_read_b64_tr_b16): in each 16-lane group gq of the
   //  wave, lane j16 points at key 4 (gq / 2) + j16 / 4 (+ 8 for the second
   //  read) and values 16 (gq % 2) + 4 (j16 % 4) .. + 3 of a 32-value block;
@@ -528,145 +564,120 @@ void extend_attention_kernel(ExtArgs a) {
   const int vq = lane >> 4, vj = lane & 15;
   const int v_key = 4 * (vq >> 1) + (vj >> 2);  // < 8
   const int v_c0 = 2 * (vq & 1) + ((vj & 3) >> 1);
-  const uint32_t v_off = kTile * kRowBytes + v_key * kRowBytes + ((v_c0 ^ v_key) << 4) +
+  const uint32_t v_off = kTile * kRowBytes + v_key * kRowBytes + ((v_c0 ^ key_swz(v_key)) << 4) +
                          8 * (vj & 1);
-  // keys 8 further: chunk XOR 8 more, i.e. bit 7
-  const uint32_t v_off_hi = (v_off + 8 * kRowBytes) ^ 128u;
+  // keys 8 further: swz(t + 8) = swz(t) ^ 2 for t < 8, i.e. byte bit 5
+  const uint32_t v_off_hi = (v_off + 8 * kRowBytes) ^ 32u;
 
-  floatx16 o[4][2];  // O^T[32 mb + row][32 qb + lane % 32]
+  floatx16 o[kD / 32];  // O^T[32 mb + row][query lane % 32]
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[mb][qb] = floatx16{};
-  float m_ref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  for (int mb = 0; mb < kD / 32; ++mb) o[mb] = floatx16{};
+  float m_ref = -INFINITY, lsum = 0.f;  // query lane % 32 (lsum: this lane's keys)
 
-  int64_t sl_next[4];
-  if (ntiles > 0) {
-    int64_t sl0[4];
+  // one tile; `masked` is uniform, so tiles inside every query's visible
+  // range skip the mask arithmetic
+  auto tile = [&](int stage, int j0, uint64_t okm, bool masked) {
+    const uint32_t kbase = tiles_base + stage * kStageBytes + k_off;
+    const uint32_t vbase = tiles_base + stage * kStageBytes + v_off;
+    const uint32_t vbase_hi = tiles_base + stage * kStageBytes + v_off_hi;
+    // S^T[key 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4][query lane % 32]
+    floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sl0[u] = slot_of(my_key0 + 4 * u);
-    issue(sl0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sl_next[u] = slot_of(kTile + my_key0 + 4 * u);
-  }
-  wait_vmcnt<0>();
-  lds_barrier();  // tile 0 visible
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it & 1;
-    // the page entries of tile it + 2, then tile it + 1 into the other stage
-    int64_t sl_after[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sl_after[u] = slot_of((it + 2) * kTile + my_key0 + 4 * u);
-    if (it + 1 < ntiles) issue(sl_next, stage ^ 1);
-    const int j0 = it * kTile;
-    const uint64_t okm = __ballot(s_ok[stage][lane] != 0);
-    // no mask needed when every key is real and visible to every query
-    const bool full = okm == ~0ull && j0 + kTile - 1 <= i0 + prefix && i0 + kQBlock <= Lq;
-    if (active) {
-      uint32_t kbase = tiles_base + stage * kStageBytes + k_off;
-      uint32_t vbase = tiles_base + stage * kStageBytes + v_off;
-      uint32_t vbase_hi = tiles_base + stage * kStageBytes + v_off_hi;
-      // this lane's keys are 4 (lane / 32) + (8 (r / 4) + r % 4) of each half
-      const uint64_t okl = okm >> (4 * (lane >> 5));
+    for (int ks = 0; ks < kD / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T[key 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4][query 32 qb + lane % 32]
-        floatx16 s[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-          const halfx8 kf = __builtin_bit_cast(
-              halfx8, *(const __attribute__((address_space(3))) uintx4*)(
-                          (lds_t*)(uintptr_t)((kbase ^ (ks << 5)) + kb * 32 * kRowBytes)));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], s[qb], 0, 0, 0);
-        }
-        halfx8 pf[2][2];  // P^T [k-step of 16 keys][qb]
-        float alpha[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          // key j0 + 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 is visible to
-          // query qi iff it is real and 32 kb + 8 (r / 4) + r % 4 <= lim
-          const int qi = i0 + 32 * qb + (lane & 31);
-          const int lim = qi < Lq ? qi + prefix - j0 - 4 * (lane >> 5) : -1;
-          float zmax = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float z = s[qb][r];
-            if (!full) {
-              const int jl = 32 * kb + 8 * (r >> 2) + (r & 3);
-              const bool vis = ((okl >> jl) & 1) && jl <= lim;
-              z = vis ? z : -INFINITY;
-            }
-            s[qb][r] = z;
-            zmax = fmaxf(zmax, z);
-          }
-          const float tmax = pair_max(zmax) * a.scale_log2;
-          // the reference maximum moves only when it is beaten by 2^8
-          const bool move = tmax > m_ref[qb] + 8.0f;
-          alpha[qb] = move ? __builtin_amdgcn_exp2f(m_ref[qb] - tmax) : 1.f;
-          m_ref[qb] = move ? tmax : m_ref[qb];
-          const float neg_m = m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb];
-          float ps = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], a.scale_log2, neg_m));
-            ps += p;
-            pf[r >> 3][qb][r & 7] = (_Float16)p;
-          }
-          lsum[qb] = lsum[qb] * alpha[qb] + pair_sum(ps);
-        }
-        if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) scale_acc(o[mb][qb], alpha[qb]);
-        }
-        // O^T += V^T P^T over the 32 keys of this half, two k-steps of 16
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const uint32_t koff = (32 * kb + 16 * st) * kRowBytes;
-            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4*)(uintptr_t)((vbase ^ (mb << 6)) + koff));
-            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_shortx4*)(uintptr_t)((vbase_hi ^ (mb << 6)) + koff));
-            const halfx8 vf = __builtin_bit_cast(
-                halfx8, (shortx8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              o[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[st][qb], o[mb][qb], 0, 0, 0);
-          }
+        const halfx8 kf = __builtin_bit_cast(
+            halfx8, *(const __attribute__((address_space(3))) uintx4*)(
+                        (lds_t*)(uintptr_t)((kbase ^ (ks << 5)) + kb * 32 * kRowBytes)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[kb], 0, 0, 0);
       }
-    }
+    if (masked) {
+      // key j0 + 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 is visible to
+      // query qi iff it is real and 32 kb + 8 (r / 4) + r % 4 <= lim
+      const uint64_t okl = okm >> (4 * (lane >> 5));
+      const int lim = qi < Lq ? qi + prefix - j0 - 4 * (lane >> 5) : -1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sl_next[u] = sl_after[u];
-    wait_vmcnt<0>();  // this wave's loads of tile it + 1
-    lds_barrier();    // tile it + 1 visible, stage it & 1 free
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const bool vis = (jl <= lim) & (((okl >> jl) & 1) != 0);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        }
+    }
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) zmax = fmaxf(zmax, fmaxf(s[kb][r], s[kb][r + 1]));
+    const float tmax = pair_max(zmax) * a.scale_log2;
+    // the reference maximum moves only when it is beaten by 2^8
+    if (__ballot(tmax > m_ref + 8.0f)) {
+      const float alpha = tmax > m_ref + 8.0f ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;
+      m_ref = tmax > m_ref + 8.0f ? tmax : m_ref;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < kD / 32; ++mb) o[mb] *= alpha;
+    }
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    halfx8 pf[2][2];  // P^T [kb][k-step of 16 keys]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], a.scale_log2, neg_m));
+        lsum += p;
+        pf[kb][r >> 3][r & 7] = (_Float16)p;
+      }
+    // O^T += V^T P^T, four k-steps of 16 keys
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int mb = 0; mb < kD / 32; ++mb) {
+          const uint32_t koff = (32 * kb + 16 * st) * kRowBytes;
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_shortx4*)(uintptr_t)((vbase ^ (mb << 6)) + koff));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_shortx4*)(uintptr_t)((vbase_hi ^ (mb << 6)) + koff));
+          const halfx8 vf = __builtin_bit_cast(
+              halfx8, (shortx8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kb][st], o[mb], 0, 0, 0);
+        }
+  };
+
+  // prologue: tile 0 in flight
+  if (ntiles > 0) issue(0);
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmcnt<0>();  // this wave's loads of tile it
+    lds_barrier();    // tile it visible; every wave is done with tile it - 1
+    if (it + 1 < ntiles) issue(it + 1);  // into tile it - 1's stage
+    const int stage = it % kExtStages;
+    const int j0 = it * kTile;
+    const uint64_t okm = __ballot(L.ok[stage][lane] != 0);
+    // no mask needed when every key is real and visible to every query
+    const bool full = okm == ~0ull && j0 + kTile - 1 <= i0 + prefix && i0 + kQBlock <= Lq;
+    if (active) tile(stage, j0, okm, !full);
   }
 
-  if (!active) return;
+  if (!active || qi >= Lq) return;
+  // lane holds O^T[32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][query]
+  const float l_tot = pair_sum(lsum);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* orow = a.out + ((int64_t)(q_base + qi) * a.Hq + h) * kD;
+#pragma unroll
+  for (int mb = 0; mb < kD / 32; ++mb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const halfx4 w = {(_Float16)(o[mb][4 * rq] * inv), (_Float16)(o[mb][4 * rq + 1] * inv),
+                        (_Float16)(o[mb][4 * rq + 2] * inv), (_Float16)(o[mb][4 * rq + 3] * inv)};
+      *(halfx4*)(orow + 32 * mb + 8 * rq + 4 * (lane >> 5)) = w;
+    }
   // the exponents were taken against m_ref, so lse = (m_ref + log2 l) ln 2
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = i0 + 32 * qb + (lane & 31);
-    if (qi >= Lq) continue;
-    const float inv = lsum[qb] > 0.f ? 1.f / lsum[qb] : 0.f;
-    uint16_t* orow = a.out + ((int64_t)(q_base + qi) * a.Hq + h) * kD;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const halfx4 w = {(_Float16)(o[mb][qb][4 * rq] * inv), (_Float16)(o[mb][qb][4 * rq + 1] * inv),
-                          (_Float16)(o[mb][qb][4 * rq + 2] * inv),
-                          (_Float16)(o[mb][qb][4 * rq + 3] * inv)};
-        *(halfx4*)(orow + 32 * mb + 8 * rq + 4 * (lane >> 5)) = w;
-      }
-    if (a.lse && lane < 32)
-      a.lse[(int64_t)(q_base + qi) * a.Hq + h] =
-          lsum[qb] > 0.f ? (m_ref[qb] + log2f(lsum[qb])) * kLn2 : -INFINITY;
-  }
+  if (a.lse && lane < 32)
+    a.lse[(int64_t)(q_base + qi) * a.Hq + h] =
+        l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 int check_dense(const char* what, const void* q, const void* k, const void* v, int64_t slots,
