@@ -45,6 +45,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 1152
 METRIC = "decode query-tokens/sec and effective KV GB/s (% HBM/MFMA roofline), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+GQA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_decode_traffic.json")
+DENSE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "dense.hip")
 COPY_CAL_BYTES = 256 << 20
 DECODE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode.hip")
 
@@ -61,12 +63,15 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["deepseek", "hot", "locality"], default="deepseek",
+    ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa"],
+                    default="deepseek",
                     help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
                          "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
                          "pinned host memory); locality: the long-context sweep (64 requests, "
-                         "context 131072, scattered against clustered top-k, 8 splits); the "
-                         "last two are reported on their own lines")
+                         "context 131072, scattered against clustered top-k, 8 splits); gqa: "
+                         "dense paged decode (128 requests, 32 query / 8 KV heads) plus "
+                         "prefix-extend (8 x 4096 + 512); the last three are reported on their "
+                         "own lines")
     ap.add_argument("--locality-variant", choices=["both", "scattered", "clustered"],
                     default="both", help="locality workload: which candidate layout to run")
     ap.add_argument("--skip-auto", action="store_true",
@@ -85,15 +90,15 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(per_launch_alg_bytes):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    valid only while the kernel source is the one they were taken on."""
+def load_traffic(per_launch_alg_bytes, path=TRAFFIC_FILE, src=DECODE_SRC):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    runs, valid only while the kernel source is the one they were taken on."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha") != source_sha(DECODE_SRC):
+    if rec.get("kernel_source_sha") != source_sha(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -438,6 +443,147 @@ def bench_locality(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_gqa(args):
+    """Dense paged attention with grouped query heads: 32 query and 8 KV heads
+    of dimension 128, fp16, page size 16, random block tables.  Decode: 128
+    requests, contexts uniform in [1024, 4096] (1.35 GB of K and V read per
+    launch, beyond the 256 MB Infinity Cache); extend: 8 requests of a 4096-token
+    cached prefix + 512 new tokens under the shifted causal mask.  A step is
+    one decode launch and one extend launch; each kernel is timed alone with
+    HIP events (median over launches).  `value` is decode query tokens per
+    second; the decode roofline is HBM bytes (K, V, queries, outputs, the
+    block table) against 8 TB/s, the extend roofline fp16 MFMA flops of the
+    visible (query, key) pairs against 2.5 PFLOP/s.  The ceiling times the
+    plain gather of the decode's K and V rows (stp_row_gather, no
+    arithmetic)."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    n_launch = max(20, min(args.steps, 200))
+    # decode
+    c = workloads.gqa_decode_case()
+    B, Hq, Hkv = c.q.shape[0], c.q.shape[1], c.hkv
+    kd, vd = workloads.dense_pool_torch(c.num_slots, Hkv, c.pool_seed, dev)
+    q, tab, ctx = t(c.q), t(c.block_table), t(c.ctx_lens)
+    S = stp.paged_gqa_decode_splits(B, Hkv, tab.shape[1], c.page_size, args.splits)
+    ws = torch.empty((max(1, stp.paged_gqa_decode_workspace_bytes(B, Hq, Hkv, tab.shape[1],
+                                                                  c.page_size, S)),),
+                     dtype=torch.uint8, device=dev)
+    out, lse = stp.paged_gqa_decode(q, kd, vd, tab, ctx, c.page_size, c.scale, S, ws)
+    d_us = median_us(lambda k: stp.paged_gqa_decode(q, kd, vd, tab, ctx, c.page_size, c.scale, S,
+                                                    ws, out=out, lse=lse), n_launch, 1)
+    tokens = int(c.ctx_lens.astype(np.int64).sum())
+    kv_bytes = tokens * Hkv * 128 * 2 * 2
+    d_alg = kv_bytes + B * Hq * 128 * 2 * 2 + B * Hq * 4 + int(np.sum(-(-c.ctx_lens // c.page_size))) * 4
+    ceil_us = None
+    if not args.no_ceilings:
+        ids = np.full((B * Hkv, int(c.ctx_lens.max())), -1, np.int32)
+        for b in range(B):
+            n = int(c.ctx_lens[b])
+            t_ = np.arange(n)
+            sl = c.block_table[b][t_ // c.page_size].astype(np.int64) * c.page_size + t_ % c.page_size
+            for g in range(Hkv):
+                ids[b * Hkv + g, :n] = sl * Hkv + g
+        ids_d, cnt_d = t(ids), t(np.repeat(c.ctx_lens, Hkv).astype(np.int32))
+        krows, vrows = kd.view(torch.uint8).view(-1, 256), vd.view(torch.uint8).view(-1, 256)
+        ceil_us = median_us(lambda k: (stp.row_gather(krows, ids_d, cnt_d, parts=2),
+                                       stp.row_gather(vrows, ids_d, cnt_d, parts=2)), n_launch, 1)
+        del ids_d
+    traffic = load_traffic(d_alg, GQA_TRAFFIC_FILE, DENSE_SRC)
+    del kd, vd
+    torch.cuda.empty_cache()
+    # extend
+    e = workloads.extend_case()
+    ke, ve = workloads.dense_pool_torch(e.num_slots, e.hkv, e.pool_seed, dev)
+    qe, qo, kvp, kvi = t(e.q), t(e.qo_indptr), t(e.kv_indptr), t(e.kv_indices)
+    oe, le = stp.extend_attention(qe, ke, ve, qo, kvp, kvi, e.max_extend_len, e.scale)
+    e_us = median_us(lambda k: stp.extend_attention(qe, ke, ve, qo, kvp, kvi, e.max_extend_len,
+                                                    e.scale, out=oe, lse=le), n_launch, 1)
+    pairs = 0
+    for b in range(len(e.qo_indptr) - 1):
+        lq = int(e.qo_indptr[b + 1] - e.qo_indptr[b])
+        lk = int(e.kv_indptr[b + 1] - e.kv_indptr[b])
+        pairs += sum(max(0, min(lk, lk - lq + i + 1)) for i in range(lq))
+    e_flops = pairs * e.q.shape[1] * 128 * 4
+    step_us = d_us + e_us
+    res = {
+        "metric": METRIC,
+        "value": round(B / (d_us * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": n_launch,
+        "warmup": 8,
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "dense paged GQA decode (value) + prefix-extend",
+                   "query_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "page_size": c.page_size,
+                   "decode_batch": B, "decode_context": "uniform 1024..4096",
+                   "decode_partitions": S, "extend_batch": len(e.qo_indptr) - 1,
+                   "extend_prefix": 4096, "extend_new_tokens": 512},
+        "roofline": {"bound": "hbm", "achieved": round(d_alg / d_us / 1e3, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d_alg / d_us / 1e3 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "paged_gqa_decode_kernel",
+                     "bytes_per_launch": d_alg},
+        "roofline_extend": {"bound": "mfma", "achieved": round(e_flops / e_us / 1e6, 1),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(e_flops / e_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "kernel": "extend_attention_kernel", "flops_per_launch": e_flops},
+        "decode_us": round(d_us, 2),
+        "extend_us": round(e_us, 2),
+        "extend_tokens_per_s": round(int(e.qo_indptr[-1]) / (e_us * 1e-6), 1),
+        "ceilings": None if ceil_us is None else {
+            "kv_row_gather_us": round(ceil_us, 2),
+            "kv_row_gather_gbs": round(kv_bytes / ceil_us / 1e3, 1),
+            "decode_vs_gather": round(ceil_us / d_us, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = gqa_cpu_baseline(c, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def gqa_cpu_baseline(c, budget_s):
+    """The dense decode oracle on the host, one request at a time (its rows
+    from the same seeded pool, regenerated on the host for the pages the
+    request maps), cycling through the batch until the budget is spent."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import workloads
+
+    pool_k, pool_v = workloads.dense_pool(min(c.num_slots, 1 << 15), c.hkv, c.pool_seed)
+    done, t0 = 0, time.perf_counter()
+    B = c.q.shape[0]
+    while time.perf_counter() - t0 < budget_s:
+        b = done % B
+        n = int(c.ctx_lens[b])
+        # the request's tokens laid on consecutive slots of a host pool (the
+        # arithmetic is the same for any slot mapping)
+        tab = np.arange(-(-n // c.page_size), dtype=np.int32)[None, :]
+        oracle.paged_gqa_decode(c.q[b:b + 1], pool_k, pool_v, tab, np.asarray([n], np.int32),
+                                c.page_size, c.scale)
+        done += 1
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(done / el, 2),
+        "unit": "query-tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} request decodes (the batch's {B} requests cycled, contexts "
+                  f"1024..4096, all {c.q.shape[1]} heads, fp64), {el:.1f} s on the host",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -451,6 +597,9 @@ def main():
         return
     if args.workload == "locality":
         bench_locality(args)
+        return
+    if args.workload == "gqa":
+        bench_gqa(args)
         return
 
     import torch

@@ -3,7 +3,7 @@ benchmark (run by path, on any host; it reads CSV files only).
 
     python sparse_top_paged_amd/profile_counters.py stats <kernel_stats.csv> <out.txt> "<command>"
     python sparse_top_paged_amd/profile_counters.py traffic <fetch counter_collection.csv> \\
-        <write counter_collection.csv> <kernel source> <out.json> "<command>"
+        <write counter_collection.csv> <kernel source> <out.json> "<command>" [<kernel name>]
     python sparse_top_paged_amd/profile_counters.py counters <out.txt> "<command>" \\
         <counter_collection.csv> [<counter_collection.csv> ...]
 
@@ -14,7 +14,7 @@ quoted beside the benchmark.
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
 counters read for the benchmark's calibration copy (a 256 MiB device-to-device
-copy launched three times before warm-up), then reports the decode kernel's
+copy launched three times before warm-up), then reports a kernel's (by default the sparse decode kernel's)
 HBM bytes per launch together with a hash of the kernel source they were
 taken on, so that a later edit of the kernel invalidates them.
 """
@@ -69,17 +69,17 @@ def calibration(vals, expect_kib):
     return expect_kib / got, got
 
 
-def traffic(fetch_csv, write_csv, kernel_src, out, command):
+def traffic(fetch_csv, write_csv, kernel_src, out, command, kernel=DECODE_KERNEL):
     kib = COPY_BYTES / 1024
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_scale, f_copy = calibration(fetch, kib)
     w_scale, w_copy = calibration(write, kib)
-    dec_f = [v for k, vs in fetch.items() if DECODE_KERNEL in k for v in vs]
-    dec_w = [v for k, vs in write.items() if DECODE_KERNEL in k for v in vs]
+    dec_f = [v for k, vs in fetch.items() if kernel in k for v in vs]
+    dec_w = [v for k, vs in write.items() if kernel in k for v in vs]
     f_avg, w_avg = sum(dec_f) / len(dec_f), sum(dec_w) / len(dec_w)
     rec = {
         "command": command,
-        "kernel": DECODE_KERNEL,
+        "kernel": kernel,
         "kernel_source_sha": hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16],
         "dispatches": [len(dec_f), len(dec_w)],
         "fetch_kib_raw": round(f_avg, 3),
@@ -152,7 +152,7 @@ if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(*sys.argv[2:5])
     elif sys.argv[1] == "traffic":
-        traffic(*sys.argv[2:7])
+        traffic(*sys.argv[2:8])
     elif sys.argv[1] == "counters":
         counters(*sys.argv[2:])
     else:
