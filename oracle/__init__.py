@@ -13,6 +13,8 @@ Sources (page titles as published):
   * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" -- decode
     attention definition, partition combine, shifted causal mask, paged
     grouped-query decode and prefix-extend attention over a token pool.
+  * "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)" -- the
+    row copy between host and device pools.
 
 Pin status (what fixes each function other than itself) is listed in each
 module header.  Every function here is pinned; none is "parity unpinned".
@@ -31,12 +33,13 @@ from .attention import (
 )
 from .merge import merge, merge_normalized
 from .dense import decode_slots, extend_attention, extend_metadata, paged_gqa_decode
+from .transfer import kv_transfer
 
 __all__ = [
     "candidate_set", "normalize", "block_view",
     "HotState", "hot_lookup_swapin", "hot_reset", "backup_rows",
     "bf16_bits_to_f64", "attend_sparse", "attend_partial", "attend_dense_masked",
     "attend_fsum", "shifted_causal_mask", "split_ranges",
-    "merge", "merge_normalized",
+    "merge", "merge_normalized", "kv_transfer",
     "decode_slots", "extend_attention", "extend_metadata", "paged_gqa_decode",
 ]
