@@ -63,14 +63,15 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa"],
+    ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa", "transfer"],
                     default="deepseek",
                     help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
                          "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
                          "pinned host memory); locality: the long-context sweep (64 requests, "
                          "context 131072, scattered against clustered top-k, 8 splits); gqa: "
                          "dense paged decode (128 requests, 32 query / 8 KV heads) plus "
-                         "prefix-extend (8 x 4096 + 512); the last three are reported on their "
+                         "prefix-extend (8 x 4096 + 512); transfer: staged bulk host<->device "
+                         "transfer of cached prefix rows; the last four are reported on their "
                          "own lines")
     ap.add_argument("--locality-variant", choices=["both", "scattered", "clustered"],
                     default="both", help="locality workload: which candidate layout to run")
@@ -551,6 +552,77 @@ def bench_gqa(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_transfer(args):
+    """Staged bulk host <-> device transfer (HiCache-style layer-wise prefix
+    load): 8 layers x 16384 rows of 1152 B (bf16 MLA rows, page size 64;
+    151 MB per call) between a pinned host pool of 65536 rows per layer and a
+    device pool of 32768 rows per layer.  Rows are whole pages of a random
+    page table, or fully scattered rows.  Reported: host-to-device and
+    device-to-host GB/s for 1..16 workgroups, against hipMemcpyAsync of the
+    same bytes as one contiguous copy (the copy engines; the link's
+    ceiling)."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, hrows, drows, n, rb, page = 8, 65536, 32768, 16384, 1152, 64
+    rng = np.random.default_rng(6000)
+    host = torch.empty((L, hrows, rb), dtype=torch.uint8, pin_memory=True)
+    g = torch.Generator().manual_seed(6001)
+    for l in range(L):
+        host[l] = torch.randint(0, 256, (hrows, rb), dtype=torch.uint8, generator=g)
+    devp = torch.empty((L, drows, rb), dtype=torch.uint8, device=dev)
+    hb, db = [host[l] for l in range(L)], [devp[l] for l in range(L)]
+    pages = rng.permutation(hrows // page)[: n // page]
+    runs = (pages[:, None] * page + np.arange(page)[None, :]).reshape(-1).astype(np.int32)
+    scat = rng.choice(hrows, size=n, replace=False).astype(np.int32)
+    dpos = np.arange(n, dtype=np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    runs_d, scat_d, dpos_d = t(runs), t(scat), t(dpos)
+    nbytes = L * n * rb
+    n_launch = 20
+    res = {}
+    for blocks in [1, 2, 4, 8, 16]:
+        r = {}
+        us = median_us(lambda k: stp.kv_transfer(hb, db, runs_d, dpos_d, num_blocks=blocks),
+                       n_launch, 1)
+        r["h2d_pages_gbs"] = round(nbytes / us / 1e3, 2)
+        us = median_us(lambda k: stp.kv_transfer(hb, db, scat_d, dpos_d, num_blocks=blocks),
+                       n_launch, 1)
+        r["h2d_scattered_gbs"] = round(nbytes / us / 1e3, 2)
+        us = median_us(lambda k: stp.kv_transfer(db, hb, dpos_d, runs_d, num_blocks=blocks),
+                       n_launch, 1)
+        r["d2h_pages_gbs"] = round(nbytes / us / 1e3, 2)
+        res[str(blocks)] = r
+    src_h = host.view(-1)[:nbytes]
+    dst_d = devp.view(-1)[:nbytes]
+    h2d_us = median_us(lambda k: dst_d.copy_(src_h, non_blocking=True), n_launch, 1)
+    d2h_us = median_us(lambda k: src_h.copy_(dst_d, non_blocking=True), n_launch, 1)
+    out = {
+        "metric": "staged host<->device KV transfer GB/s, 1 MI355X",
+        "value": res["4"]["h2d_pages_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_launch,
+        "warmup": 8,
+        "ms_per_step": round(nbytes / res["4"]["h2d_pages_gbs"] / 1e6, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "layer-wise prefix load host->device, page runs, 4 workgroups "
+                               "(value)", "layers": L, "rows_per_layer": n, "row_bytes": rb,
+                   "page_size": page, "bytes_per_call": nbytes},
+        "by_workgroups": res,
+        "copy_engine": {"h2d_gbs": round(nbytes / h2d_us / 1e3, 2),
+                        "d2h_gbs": round(nbytes / d2h_us / 1e3, 2)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def gqa_cpu_baseline(c, budget_s):
     """The dense decode oracle on the host, one request at a time (its rows
     from the same seeded pool, regenerated on the host for the pages the
@@ -600,6 +672,9 @@ def main():
         return
     if args.workload == "gqa":
         bench_gqa(args)
+        return
+    if args.workload == "transfer":
+        bench_transfer(args)
         return
 
     import torch

@@ -12,7 +12,9 @@
  *   4. stp_splitkv_merge       merge of split partial states.
  * Beside it, dense paged attention with grouped query heads over a token pool:
  *      stp_paged_gqa_decode    decode over block tables;
- *      stp_extend_attention    prefill of new tokens over a cached prefix.
+ *      stp_extend_attention    prefill of new tokens over a cached prefix;
+ * and the staged bulk transfer of KV rows between host and device pools:
+ *      stp_kv_transfer.
  *
  * Sources: "HiSparse" hot-buffer walkthrough (devpress.csdn.net); "5.1.1 · 从
  * 索引到 Kernel" (PaperTrace); "PagedAttention 与 RadixAttention：上游机制与海光
@@ -366,6 +368,35 @@ int stp_extend_attention(const uint16_t* q, const uint16_t* k_pool, const uint16
                          const int32_t* kv_indices, int32_t B, int32_t Hq, int32_t Hkv,
                          int32_t head_dim, int32_t max_extend_len, float scale, uint16_t* out,
                          float* lse, hipStream_t stream);
+
+/*
+ * ---- Staged bulk host <-> device KV transfer --------------------------------
+ * "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)",
+ * Motivation and Modifications (cached prefixes brought back from the pinned
+ * host pool layer by layer on a side stream; any row size that is a multiple
+ * of 16 B; layer-first and page-first host views).
+ *
+ * For every buffer b < num_bufs and list position i < n:
+ *   dst_bufs[b] + dst_idx[i] * dst_stride  <-  src_bufs[b] + src_idx[i] * src_stride
+ * row_bytes bytes each.  A position whose src_idx is outside [0, src_rows) or
+ * whose dst_idx is outside [0, dst_rows) is skipped (data, not an error).
+ * Two positions with the same destination race.
+ * src_bufs / dst_bufs: host arrays of num_bufs device-visible addresses
+ * (device memory, or pinned host memory through stp_host_device_pointer);
+ * one call per direction, H2D or D2H or device to device.  A page-first host
+ * view (rows of all layers interleaved) is a per-layer base with stride
+ * layers * row_bytes.  src_idx, dst_idx: device arrays [n] int32.
+ * num_blocks: workgroups (256 threads, 128 KiB of LDS each) the transfer may
+ * occupy; each keeps 64 KiB of loads in flight (about 12.8 GB/s of host
+ * reads per workgroup on MI355X; five saturate a PCIe 5.0 x16 link).
+ * Requirements: 1 <= num_bufs <= 32; row_bytes a multiple of 16 in
+ * [16, 65536]; strides multiples of 16 and >= row_bytes; n >= 0;
+ * num_blocks >= 1.
+ */
+int stp_kv_transfer(const void* const* src_bufs, void* const* dst_bufs, int32_t num_bufs,
+                    int64_t row_bytes, int64_t src_stride, int64_t src_rows, int64_t dst_stride,
+                    int64_t dst_rows, const int32_t* src_idx, const int32_t* dst_idx, int32_t n,
+                    int32_t num_blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

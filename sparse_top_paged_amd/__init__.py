@@ -19,7 +19,7 @@ __all__ = [
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
-    "extend_attention",
+    "extend_attention", "kv_transfer",
 ]
 
 
@@ -371,3 +371,49 @@ def extend_attention(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, max_ex
         float(scale), _dev(out, "out", torch.float16, dev), _opt(lse, "lse", torch.float32, dev),
         _stream(dev)))
     return out, lse
+
+
+def _visible_ptr(t):
+    """Device-visible address of a device tensor or of a pinned host tensor
+    (a view into pinned memory too: the allocation's base is mapped and the
+    view's offset added)."""
+    import ctypes
+    if t.is_cuda:
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise ValueError("host buffers must be pinned (pin_memory=True)")
+    base = t.untyped_storage().data_ptr()
+    out = ctypes.c_void_p()
+    check(lib.stp_host_device_pointer(ctypes.c_void_p(base), ctypes.byref(out)))
+    return out.value + (t.data_ptr() - base)
+
+
+def kv_transfer(src_bufs, dst_bufs, src_idx, dst_idx, row_bytes=None, src_stride=None,
+                dst_stride=None, src_rows=None, dst_rows=None, num_blocks=4):
+    """Staged bulk copy of rows: for every buffer pair and position i,
+    dst[dst_idx[i]] <- src[src_idx[i]] (row_bytes each).  Buffers are device
+    tensors or pinned host tensors, all of one side alike in shape; by default
+    a buffer is [rows, row_bytes] bytes (strides = row_bytes, rows = its row
+    count).  src_idx / dst_idx: device int32 [n]."""
+    import ctypes
+    if not src_bufs or len(src_bufs) != len(dst_bufs):
+        raise ValueError("src_bufs and dst_bufs must be equally long, non-empty lists")
+    dev = src_idx.device
+    s0, d0 = src_bufs[0], dst_bufs[0]
+    row_bytes = row_bytes or s0.shape[-1] * s0.element_size()
+    src_stride = src_stride or row_bytes
+    dst_stride = dst_stride or row_bytes
+    if src_rows is None:
+        src_rows = s0.numel() * s0.element_size() // src_stride
+    if dst_rows is None:
+        dst_rows = d0.numel() * d0.element_size() // dst_stride
+    n = src_idx.numel()
+    if dst_idx.numel() != n:
+        raise ValueError("src_idx and dst_idx must have the same length")
+    nb = len(src_bufs)
+    sp = (ctypes.c_void_p * nb)(*[_visible_ptr(t) for t in src_bufs])
+    dp = (ctypes.c_void_p * nb)(*[_visible_ptr(t) for t in dst_bufs])
+    check(lib.stp_kv_transfer(sp, dp, nb, row_bytes, src_stride, src_rows, dst_stride, dst_rows,
+                              _dev(src_idx, "src_idx", torch.int32, dev),
+                              _dev(dst_idx, "dst_idx", torch.int32, dev), n, num_blocks,
+                              _stream(dev)))

@@ -49,6 +49,8 @@ SIGNATURES = {
         _p, _p, _p]),
     "stp_paged_gqa_decode_splits": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "stp_paged_gqa_decode_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "stp_kv_transfer": (ctypes.c_int, [
+        _p, _p, _i32, _i64, _i64, _i64, _i64, _i64, _p, _p, _i32, _i32, _p]),
     "stp_extend_attention": (ctypes.c_int, [
         _p, _p, _p, _i64, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),
 }

@@ -95,6 +95,16 @@ def test_host_side_validation():
     assert lib.stp_paged_gqa_decode_splits(2, 8, 1, 16, 5) == 1     # one tile: one partition
     assert lib.stp_paged_gqa_decode_workspace(2, 32, 8, 256, 16, 1) == 0
     assert lib.stp_paged_gqa_decode_workspace(2, 32, 8, 256, 16, 4) == 2 * 4 * 32 * 130 * 4
+    # staged transfer: row size a multiple of 16 in [16, 65536], strides >= row size,
+    # 1..32 buffers, at least one workgroup; n = 0 launches nothing
+    bufs = (ctypes.c_void_p * 1)(fake)
+    tr = lib.stp_kv_transfer
+    assert tr(bufs, bufs, 1, 1000, 1008, 10, 1008, 10, fake, fake, 4, 1, None) == STP_ERR_INVALID_ARG
+    assert tr(bufs, bufs, 1, 1152, 1136, 10, 1152, 10, fake, fake, 4, 1, None) == STP_ERR_INVALID_ARG
+    assert tr(bufs, bufs, 0, 1152, 1152, 10, 1152, 10, fake, fake, 4, 1, None) == STP_ERR_INVALID_ARG
+    assert tr(bufs, bufs, 33, 1152, 1152, 10, 1152, 10, fake, fake, 4, 1, None) == STP_ERR_INVALID_ARG
+    assert tr(bufs, bufs, 1, 1152, 1152, 10, 1152, 10, fake, fake, 4, 0, None) == STP_ERR_INVALID_ARG
+    assert tr(bufs, bufs, 1, 1152, 1152, 10, 1152, 10, fake, fake, 0, 1, None) == 0
     ext = lib.stp_extend_attention
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 4, 128, 64, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 8, 96, 64, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
