@@ -15,6 +15,8 @@ Sources (page titles as published):
     grouped-query decode and prefix-extend attention over a token pool.
   * "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)" -- the
     row copy between host and device pools.
+  * "HiSparse" walkthrough and "5.1.1 · 从索引到 Kernel" §7.2 -- the 656-byte
+    fp8_ds_mla latent rows and their dequantisation.
 
 Pin status (what fixes each function other than itself) is listed in each
 module header.  Every function here is pinned; none is "parity unpinned".
@@ -34,6 +36,7 @@ from .attention import (
 from .merge import merge, merge_normalized
 from .dense import decode_slots, extend_attention, extend_metadata, paged_gqa_decode
 from .transfer import kv_transfer
+from .fp8 import attend_sparse_fp8, dequant_rows, e4m3_to_f64
 
 __all__ = [
     "candidate_set", "normalize", "block_view",
@@ -41,5 +44,6 @@ __all__ = [
     "bf16_bits_to_f64", "attend_sparse", "attend_partial", "attend_dense_masked",
     "attend_fsum", "shifted_causal_mask", "split_ranges",
     "merge", "merge_normalized", "kv_transfer",
+    "attend_sparse_fp8", "dequant_rows", "e4m3_to_f64",
     "decode_slots", "extend_attention", "extend_metadata", "paged_gqa_decode",
 ]

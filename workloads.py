@@ -392,3 +392,54 @@ def random_gqa_decode_case(seed, ctx, hq=8, hkv=2, page_size=16, unmapped_frac=0
     q = normal_fp16(rng, (len(ctx), hq, D_HEAD))
     return GqaDecodeCase(f"gqa_small_{seed}", q, tables, ctx, page_size, hkv, pages * page_size,
                          pool_seed=seed + 1)
+
+
+# ---- fp8_ds_mla rows ----------------------------------------------------------
+# 656 bytes: 512 E4M3 codes of the latent values, 4 float32 scales (one per
+# 128 values: amax / 448, the format's largest finite value), 64 bf16 RoPE
+# values.  Latent and RoPE values are N(0, 1).  The rounding to E4M3 is
+# torch's float8_e4m3fn conversion.
+
+FP8_ROW_BYTES = 656
+
+
+def _fp8_pack(latent, rope_bits, pow2_scales):
+    """latent float32 [n, 512] (torch), rope bf16 bits [n, 64] (torch int16)
+    -> [n, 656] uint8 rows (torch, same device)."""
+    import torch
+    n = latent.shape[0]
+    g = latent.view(n, 4, 128)
+    amax = g.abs().amax(dim=2).clamp_min(1e-12)
+    scale = amax / 448.0
+    if pow2_scales:
+        scale = torch.exp2(torch.ceil(torch.log2(scale)))
+    codes = (g / scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).view(n, 512)
+    rows = torch.empty((n, FP8_ROW_BYTES), dtype=torch.uint8, device=latent.device)
+    rows[:, :512] = codes
+    rows[:, 512:528] = scale.to(torch.float32).contiguous().view(torch.uint8).view(n, 16)
+    rows[:, 528:] = rope_bits.contiguous().view(torch.uint8).view(n, 128)
+    return rows
+
+
+def fp8_rows(rng, n, pow2_scales=False):
+    """n fp8_ds_mla rows on the host (numpy uint8 [n, 656])."""
+    import torch
+    latent = torch.from_numpy(rng.standard_normal((n, 512), dtype=np.float32))
+    rope = torch.from_numpy(normal_bf16(rng, (n, 64)).view(np.int16))
+    return _fp8_pack(latent, rope, pow2_scales).numpy()
+
+
+def fp8_pool_torch(rows, seed, device, chunk_rows=1 << 18):
+    """fp8_ds_mla pool [rows, 656] uint8 generated in device memory by torch's
+    seeded generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    pool = torch.empty((rows, FP8_ROW_BYTES), dtype=torch.uint8, device=device)
+    for lo in range(0, rows, chunk_rows):
+        hi = min(rows, lo + chunk_rows)
+        latent = torch.randn((hi - lo, 512), generator=g, device=device, dtype=torch.float32)
+        rope = torch.randn((hi - lo, 64), generator=g, device=device,
+                           dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        pool[lo:hi] = _fp8_pack(latent, rope, False)
+    return pool
