@@ -9,6 +9,7 @@
  *      stp_backup_rows         and the back-up of each step's new rows;
  *   3. stp_sparse_mla_decode   attention over the selected latent rows with an
  *                              online softmax (optionally split);
+ *      stp_sparse_mla_decode_fp8   the same over 656-byte fp8_ds_mla rows;
  *   4. stp_splitkv_merge       merge of split partial states.
  * Beside it, dense paged attention with grouped query heads over a token pool:
  *      stp_paged_gqa_decode    decode over block tables;
@@ -214,6 +215,28 @@ int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows
                           const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T,
                           int32_t H, float scale, int32_t num_splits, void* workspace,
                           size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * Stage 3 over fp8_ds_mla rows ("HiSparse" walkthrough: the 656-byte
+ * FP8_DS_MLA row, 512 B quantised latent + 16 B scales + 128 B RoPE;
+ * "5.1.1 · 从索引到 Kernel" §7.2: dequantise at tile load).  As
+ * stp_sparse_mla_decode, with kv [kv_rows, 656] uint8 rows: latent value i =
+ * e4m3(byte i) * scale[i / 128] (OCP FP8 E4M3; scale = float32 at bytes
+ * 512 + 4 (i / 128)), RoPE values bf16 at bytes 528..655; the key is the 576
+ * values, the value vector the first 512.  The scales are applied in fp32,
+ * the codes converted exactly.  num_splits 0 = automatic; more than one
+ * split needs stp_sparse_mla_decode_fp8_workspace() bytes.  At most 1024
+ * candidate ids per split (raised automatically).
+ * Requirements: T >= 0, H >= 1, cap >= 0, kv_rows > 0, 0 < scale < inf.
+ */
+int stp_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_rows,
+                              const int32_t* row_ids, const int32_t* counts, int32_t cap,
+                              int32_t T, int32_t H, float scale, int32_t num_splits,
+                              void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                              hipStream_t stream);
+int32_t stp_sparse_mla_decode_fp8_splits(int32_t T, int32_t H, int32_t cap, int32_t num_splits);
+size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
+                                           int32_t num_splits);
 
 /* Splits stp_sparse_mla_decode uses for num_splits (0 = auto) at this shape, on
  * the current device (query it, and the workspace size, on the device the

@@ -19,7 +19,8 @@ __all__ = [
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
-    "extend_attention", "kv_transfer",
+    "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
+    "decode_fp8_workspace_bytes",
 ]
 
 
@@ -417,3 +418,45 @@ def kv_transfer(src_bufs, dst_bufs, src_idx, dst_idx, row_bytes=None, src_stride
                               _dev(src_idx, "src_idx", torch.int32, dev),
                               _dev(dst_idx, "dst_idx", torch.int32, dev), n, num_blocks,
                               _stream(dev)))
+
+
+FP8_ROW_BYTES = 656
+
+
+def decode_fp8_splits(T, H, cap, num_splits=0):
+    return lib.stp_sparse_mla_decode_fp8_splits(T, H, cap, num_splits)
+
+
+def decode_fp8_workspace_bytes(T, H, cap, num_splits=0):
+    return lib.stp_sparse_mla_decode_fp8_workspace(T, H, cap, num_splits)
+
+
+def sparse_mla_decode_fp8(q, kv, row_ids, counts=None, scale=D_QK ** -0.5, num_splits=0,
+                          workspace=None, out=None, lse=None):
+    """Stage 3 over fp8_ds_mla rows: q [T, H, 576] bf16, kv [rows, 656] uint8,
+    row_ids [T, cap] int32, counts [T] int32.  Returns (out [T, H, 512] bf16,
+    lse [T, H] float32)."""
+    dev = q.device
+    if q.dim() != 3 or q.shape[2] != D_QK:
+        raise ValueError("q must be [T, H, 576]")
+    if kv.dim() != 2 or kv.shape[1] != FP8_ROW_BYTES or kv.dtype != torch.uint8:
+        raise ValueError("kv must be uint8 [rows, 656]")
+    T, H = q.shape[0], q.shape[1]
+    if row_ids.dim() != 2 or row_ids.shape[0] != T:
+        raise ValueError("row_ids must be [T, cap]")
+    cap = row_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = decode_fp8_workspace_bytes(T, H, cap, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", torch.uint8, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(lib.stp_sparse_mla_decode_fp8(
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.uint8, dev), kv.shape[0],
+        _dev(row_ids, "row_ids", torch.int32, dev), _opt(counts, "counts", torch.int32, dev), cap,
+        T, H, float(scale), num_splits, ws_ptr, ws_bytes,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse
