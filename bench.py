@@ -63,7 +63,8 @@ def parse():
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa", "transfer"],
+    ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa", "transfer",
+                                           "fp8"],
                     default="deepseek",
                     help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
                          "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
@@ -71,8 +72,8 @@ def parse():
                          "context 131072, scattered against clustered top-k, 8 splits); gqa: "
                          "dense paged decode (128 requests, 32 query / 8 KV heads) plus "
                          "prefix-extend (8 x 4096 + 512); transfer: staged bulk host<->device "
-                         "transfer of cached prefix rows; the last four are reported on their "
-                         "own lines")
+                         "transfer of cached prefix rows; fp8: the deepseek step over 656-byte "
+                         "fp8_ds_mla rows; the last five are reported on their own lines")
     ap.add_argument("--locality-variant", choices=["both", "scattered", "clustered"],
                     default="both", help="locality workload: which candidate layout to run")
     ap.add_argument("--skip-auto", action="store_true",
@@ -623,6 +624,88 @@ def bench_transfer(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_fp8(args):
+    """The DeepSeek-shaped step over fp8_ds_mla rows: the same 32 tokens, 128
+    heads, context 32768, top-k 2048 + 128 + 4, page 64, with a 1,048,576-row
+    pool of 656-byte rows (688 MB) instead of 1152-byte bf16 rows (1.21 GB).
+    Eight candidate sets rotate.  Timed (median of HIP event pairs): the
+    normalisation, and each decode entry point with its automatic splits
+    (decode + merge): fp8 rows and, for comparison, bf16 rows of the same
+    shape.  KV bytes per call: selected rows x 656 (fp8) or x 1152 (bf16)."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsets = args.sets
+    cases = [workloads.deepseek_case(variant=v) for v in range(nsets)]
+    c0 = cases[0]
+    T, H, cap = c0.T, c0.H, c0.cap
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q = t(c0.q_bits.view(np.int16)).view(torch.bfloat16)
+    req, qpos, table = t(c0.req_id), t(c0.q_pos), t(c0.block_table)
+    norm = [stp.normalize_indices(t(c.topk), req, qpos, table, c0.page_size, c0.window,
+                                  c0.num_sinks, cap) for c in cases]
+    torch.cuda.synchronize()
+    sel = float(np.mean([int(n["count"].sum().item()) for n in norm]))
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    n_launch = max(50, min(args.steps, 400))
+    kv8 = workloads.fp8_pool_torch(c0.kv_rows, c0.pool_seed, dev)
+    s8 = stp.decode_fp8_splits(T, H, cap)
+    ws8 = torch.empty((max(1, stp.decode_fp8_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
+                      device=dev)
+    f_us = median_us(lambda k: stp.sparse_mla_decode_fp8(q, kv8, norm[k]["slot"],
+                                                         norm[k]["count"], c0.scale, 0, ws8,
+                                                         out, lse), n_launch, nsets)
+    del kv8
+    torch.cuda.empty_cache()
+    kvb = workloads.pool_torch(c0.kv_rows, c0.pool_seed, dev)
+    sb = stp.decode_splits(T, H, cap)
+    wsb = torch.empty((max(1, stp.decode_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
+                      device=dev)
+    b_us = median_us(lambda k: stp.sparse_mla_decode(q, kvb, norm[k]["slot"], norm[k]["count"],
+                                                     c0.scale, 0, wsb, out, lse), n_launch, nsets)
+    topks = [t(c.topk) for c in cases]
+    n_us = median_us(lambda k: stp.normalize_indices(topks[k], req, qpos, table, c0.page_size,
+                                                     c0.window, c0.num_sinks, cap, out=norm[k]),
+                     n_launch, nsets)
+    q_bytes = T * H * 576 * 2
+    alg8 = sel * 656 + q_bytes + sel * 4
+    step_us = n_us + f_us
+    res = {
+        "metric": METRIC,
+        "value": round(T / (step_us * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": n_launch,
+        "warmup": 8,
+        "ms_per_step": round(step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "deepseek-v3.2-shaped sparse MLA decode over fp8_ds_mla rows",
+                   "batch": T, "query_heads": H, "context": 32768, "page_size": c0.page_size,
+                   "top_k": c0.top_k, "row_bytes": 656, "kv_pool_rows": c0.kv_rows,
+                   "splits": s8, "candidate_sets": nsets,
+                   "mean_selected_rows_per_token": round(sel / T, 2)},
+        "normalise_us": round(n_us, 2),
+        "fp8_decode_and_merge_us": round(f_us, 2),
+        "bf16_decode_and_merge_us": round(b_us, 2),
+        "bf16_splits": sb,
+        "kv_bytes_fp8": int(sel * 656),
+        "kv_bytes_bf16": int(sel * ROW_BYTES),
+        "byte_ratio": round(656 / ROW_BYTES, 4),
+        "time_ratio": round(f_us / b_us, 4),
+        "fp8_alg_gbs": round(alg8 / f_us / 1e3, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def gqa_cpu_baseline(c, budget_s):
     """The dense decode oracle on the host, one request at a time (its rows
     from the same seeded pool, regenerated on the host for the pages the
@@ -675,6 +758,9 @@ def main():
         return
     if args.workload == "transfer":
         bench_transfer(args)
+        return
+    if args.workload == "fp8":
+        bench_fp8(args)
         return
 
     import torch
