@@ -17,6 +17,8 @@ Sources (page titles as published):
     row copy between host and device pools.
   * "HiSparse" walkthrough and "5.1.1 · 从索引到 Kernel" §7.2 -- the 656-byte
     fp8_ds_mla latent rows and their dequantisation.
+  * "5.1.1 · 从索引到 Kernel" §5.1 and §7.4 -- task tables of a ragged batch
+    (plan / run) with stable row identity.
 
 Pin status (what fixes each function other than itself) is listed in each
 module header.  Every function here is pinned; none is "parity unpinned".
@@ -37,6 +39,7 @@ from .merge import merge, merge_normalized
 from .dense import decode_slots, extend_attention, extend_metadata, paged_gqa_decode
 from .transfer import kv_transfer
 from .fp8 import attend_sparse_fp8, dequant_rows, e4m3_to_f64
+from .plan import plan_tasks, run_tasks
 
 __all__ = [
     "candidate_set", "normalize", "block_view",
@@ -46,4 +49,5 @@ __all__ = [
     "merge", "merge_normalized", "kv_transfer",
     "attend_sparse_fp8", "dequant_rows", "e4m3_to_f64",
     "decode_slots", "extend_attention", "extend_metadata", "paged_gqa_decode",
+    "plan_tasks", "run_tasks",
 ]
