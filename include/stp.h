@@ -10,6 +10,8 @@
  *   3. stp_sparse_mla_decode   attention over the selected latent rows with an
  *                              online softmax (optionally split);
  *      stp_sparse_mla_decode_fp8   the same over 656-byte fp8_ds_mla rows;
+ *      stp_decode_plan / stp_decode_run   the same as a plan (task table of a
+ *                              capacity tier) and a graph-stable run over it;
  *   4. stp_splitkv_merge       merge of split partial states.
  * Beside it, dense paged attention with grouped query heads over a token pool:
  *      stp_paged_gqa_decode    decode over block tables;
@@ -237,6 +239,56 @@ int stp_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_r
 int32_t stp_sparse_mla_decode_fp8_splits(int32_t T, int32_t H, int32_t cap, int32_t num_splits);
 size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
                                            int32_t num_splits);
+
+/*
+ * Plan / run ("5.1.1 · 从索引到 Kernel" §5.1: plan once from the row lengths,
+ * run per layer, caller-provided workspace sized for a capacity tier; §7.1:
+ * for graph capture every address and grid shape is fixed by the tier and
+ * the kernels read the valid task count; §7.4: a row of n candidates becomes
+ * ceil(n / R) tasks (row, start, end, split) numbered by a prefix sum, and
+ * each task's partial goes to the slot of its (row, split)).
+ *
+ * A tier is (T, cap, rows_per_task = R): T rows (pad a smaller batch with
+ * rows whose count is 0: they get no task, out = 0 and lse = -inf), at most
+ * cap candidates per row, at most R (1 <= R <= 1024) candidate positions per
+ * task.  max_tasks = T * ceil(cap / R).
+ *
+ * stp_decode_plan reads counts [T] (nullable: every row has cap candidates;
+ * each count is clamped to [0, cap]) on the device and writes the plan
+ * buffer (int32, stp_decode_plan_bytes() bytes, caller-owned device memory):
+ *   [0] number of tasks, [1] T, [2] R, [3] max_tasks, [4..11] queue heads
+ *   (set to 0), [16 .. 16 + T] row_first (row_first[r] = tasks before row r),
+ *   then, from int32 index ceil((17 + T) / 4) * 4, the tasks as 4 int32
+ *   (row, start, end, split), row by row in split order.
+ * stp_decode_run computes, for every row t, the attention of
+ * stp_sparse_mla_decode over row_ids[t, 0 : count_t] (the counts the plan
+ * was made from): a persistent grid pops (task, head group) work items from
+ * eight queues (one per XCD), writes each task's normalised partial to slot
+ * row_first[row] + split of the workspace (stp_decode_run_workspace() bytes:
+ * bf16 o/l [max_tasks][H][512], then fp32 m and l [max_tasks][H], each
+ * 256-byte aligned), and a merge writes out [T, H, 512] bf16 and lse [T, H]
+ * (nullable).  The order of the tasks in the table does not change the
+ * result: a caller may reorder them.  The run leaves the queue heads at 0, so
+ * one plan serves any number of runs; runs over one plan buffer must not
+ * overlap in time (they share the queue heads).  Grids depend only on the
+ * tier and the device, so plan + run (or run alone) can be captured in a HIP
+ * graph and replayed after the counts and candidates change in place.
+ * Errors: STP_ERR_INVALID_ARG for bad sizes, R outside [1, 1024] or null
+ * pointers; STP_ERR_WORKSPACE when the plan buffer or workspace is smaller
+ * than the tier needs.
+ */
+int stp_decode_plan(const int32_t* counts, int32_t T, int32_t cap, int32_t rows_per_task,
+                    int32_t* plan, size_t plan_bytes, hipStream_t stream);
+int stp_decode_run(const uint16_t* q, const uint16_t* kv, int64_t kv_rows, const int32_t* row_ids,
+                   int32_t cap, int32_t T, int32_t H, float scale, int32_t rows_per_task,
+                   int32_t* plan, size_t plan_bytes, void* workspace, size_t workspace_bytes,
+                   uint16_t* out, float* lse, hipStream_t stream);
+/* Bytes of the plan buffer and of the run workspace of a tier (0 for bad
+ * sizes), and a task size R for (T, H, cap): the static split's range
+ * rounded up to whole 32-row tiles, at most 1024. */
+size_t stp_decode_plan_bytes(int32_t T, int32_t cap, int32_t rows_per_task);
+size_t stp_decode_run_workspace(int32_t T, int32_t H, int32_t cap, int32_t rows_per_task);
+int32_t stp_decode_plan_rows_per_task(int32_t T, int32_t H, int32_t cap);
 
 /* Splits stp_sparse_mla_decode uses for num_splits (0 = auto) at this shape, on
  * the current device (query it, and the workspace size, on the device the

@@ -20,7 +20,8 @@ __all__ = [
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
     "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
-    "decode_fp8_workspace_bytes",
+    "decode_fp8_workspace_bytes", "decode_plan", "decode_run", "decode_plan_bytes",
+    "decode_run_workspace_bytes", "decode_plan_rows_per_task", "plan_view",
 ]
 
 
@@ -458,5 +459,70 @@ def sparse_mla_decode_fp8(q, kv, row_ids, counts=None, scale=D_QK ** -0.5, num_s
         _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.uint8, dev), kv.shape[0],
         _dev(row_ids, "row_ids", torch.int32, dev), _opt(counts, "counts", torch.int32, dev), cap,
         T, H, float(scale), num_splits, ws_ptr, ws_bytes,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse
+
+
+def decode_plan_rows_per_task(T, H, cap):
+    return lib.stp_decode_plan_rows_per_task(T, H, cap)
+
+
+def decode_plan_bytes(T, cap, rows_per_task):
+    return lib.stp_decode_plan_bytes(T, cap, rows_per_task)
+
+
+def decode_run_workspace_bytes(T, H, cap, rows_per_task):
+    return lib.stp_decode_run_workspace(T, H, cap, rows_per_task)
+
+
+def decode_plan(counts, T, cap, rows_per_task, plan=None, device=None):
+    """Plan of a capacity tier (T rows, cap candidates, rows_per_task per
+    task) from counts [T] int32 on the device (None: every row has cap).
+    Returns the plan buffer (int32 device tensor), allocated when not given."""
+    dev = counts.device if counts is not None else (device or torch.device("cuda"))
+    need = decode_plan_bytes(T, cap, rows_per_task)
+    if plan is None:
+        plan = torch.empty((max(need, 4) // 4,), dtype=torch.int32, device=dev)
+    check(lib.stp_decode_plan(_opt(counts, "counts", torch.int32, dev), T, cap, rows_per_task,
+                              _dev(plan, "plan", torch.int32, dev), plan.numel() * 4,
+                              _stream(dev)))
+    return plan
+
+
+def plan_view(plan, T):
+    """(number of tasks, row_first [T + 1], tasks [n, 4]) views of a plan
+    buffer, in the layout stp_decode_plan writes."""
+    n = int(plan[0].item())
+    off = (17 + T + 3) // 4 * 4
+    return n, plan[16:17 + T], plan[off:off + 4 * n].view(n, 4)
+
+
+def decode_run(q, kv, row_ids, plan, rows_per_task, scale=D_QK ** -0.5, workspace=None,
+               out=None, lse=None):
+    """Run over a plan: q [T, H, 576] bf16, kv [rows, 576] bf16, row_ids
+    [T, cap] int32, plan from decode_plan with the same T, cap and
+    rows_per_task.  Returns (out [T, H, 512] bf16, lse [T, H] float32)."""
+    dev = q.device
+    if q.dim() != 3 or q.shape[2] != D_QK:
+        raise ValueError("q must be [T, H, 576]")
+    if kv.dim() != 2 or kv.shape[1] != D_QK:
+        raise ValueError("kv must be [rows, 576]")
+    T, H = q.shape[0], q.shape[1]
+    if row_ids.dim() != 2 or row_ids.shape[0] != T:
+        raise ValueError("row_ids must be [T, cap]")
+    cap = row_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = decode_run_workspace_bytes(T, H, cap, rows_per_task)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", torch.uint8, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    check(lib.stp_decode_run(
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0],
+        _dev(row_ids, "row_ids", torch.int32, dev), cap, T, H, float(scale), rows_per_task,
+        _dev(plan, "plan", torch.int32, dev), plan.numel() * 4, ws_ptr, ws_bytes,
         _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
     return out, lse

@@ -38,6 +38,12 @@ SIGNATURES = {
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p, _p, _p]),
     "stp_sparse_mla_decode_fp8_splits": (_i32, [_i32, _i32, _i32, _i32]),
     "stp_sparse_mla_decode_fp8_workspace": (_sz, [_i32, _i32, _i32, _i32]),
+    "stp_decode_plan": (ctypes.c_int, [_p, _i32, _i32, _i32, _p, _sz, _p]),
+    "stp_decode_run": (ctypes.c_int, [
+        _p, _p, _i64, _p, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p, _sz, _p, _p, _p]),
+    "stp_decode_plan_bytes": (_sz, [_i32, _i32, _i32]),
+    "stp_decode_run_workspace": (_sz, [_i32, _i32, _i32, _i32]),
+    "stp_decode_plan_rows_per_task": (_i32, [_i32, _i32, _i32]),
     "stp_sparse_mla_decode_splits": (_i32, [_i32, _i32, _i32, _i32]),
     "stp_sparse_mla_decode_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "stp_sparse_mla_decode_partial": (ctypes.c_int, [

@@ -107,6 +107,12 @@ struct DecodeArgs {
   float* l_part;
   uint16_t* out;   // final mode: [T, H, 512] bf16
   float* lse;
+  // task-queue launch: the plan's task count, (row, start, end, split)
+  // entries, first partial slot of each row and the eight queue heads
+  const int32_t* num_tasks;
+  const int32_t* tasks;
+  const int32_t* row_first;
+  int32_t* queue;
 };
 
 // Output modes of the decode kernel.
@@ -291,7 +297,7 @@ constexpr int kHeadStride = kDV * 2 + 16;
 // store instruction: the final output, or the split's normalised partial.
 template <int kMode>
 __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeLds& L, int t,
-                                              int s, int hg, int tid) {
+                                              int64_t part, int hg, int tid) {
 #pragma unroll 4
   for (int it = 0; it < 64 * 64 / kThreads; ++it) {
     const int idx = it * kThreads + tid;    // 64 lanes per head row of 1 KiB
@@ -302,51 +308,22 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
         *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
     uint16_t* orow = kMode == kOutFinal
                          ? a.out + ((int64_t)t * a.H + head) * kDV
-                         : (uint16_t*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+                         : (uint16_t*)a.o_part + (part * a.H + head) * kDV;
     *(uintx4*)(orow + c * 8) = v;
   }
 }
 
+// One work item: token t, candidate positions lo .. lo + len - 1 of its list,
+// head group hg; split partials go to slot `part` ([part][H][512]).
 template <int kMode>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void sparse_mla_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
-  __shared__ __attribute__((aligned(16))) char s_pbuf[2 * 2 * 2 * 1024];
-  __shared__ __attribute__((aligned(16))) float s_alpha[2 * 64];
-  __shared__ __attribute__((aligned(16))) float s_stat[3 * 64];
-  __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
-  __shared__ int s_bad[2];
-  const DecodeLds L{(lds_t*)s_tiles, (lds_t*)s_pbuf, s_alpha, s_stat, s_ids};
-
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
+                                            const uint8_t* zero_row, int t, int lo, int len,
+                                            int hg, int64_t part) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const bool score = wave < 2;
   const int j = wave & 1;
-  // the zero row's address, fetched once: inside the loops its GOT load (a
-  // scalar load, which only a full lgkmcnt(0) wait covers) would drain the
-  // LDS reads in flight
-  const uint8_t* zero_row = g_zero_row;
-  asm volatile("" : "+s"(zero_row));
-
-  // XCD-aware task map: every workgroup of one token (all splits, all head
-  // groups) gets a block id of the same residue mod 8, i.e. runs on the same
-  // XCD, so the token's query rows and the KV rows its head groups share are
-  // fetched into one L2.
-  const int bid = blockIdx.x;
-  const int xk = bid >> 3;
-  const int per_token = a.S * a.G;
-  const int t = (xk / per_token) * 8 + (bid & 7);
-  const int rem = xk % per_token;
-  const int s = rem / a.G;
-  const int hg = rem - s * a.G;
-  if (t >= a.T) return;
-
-  int n = a.counts ? a.counts[t] : a.cap;
-  n = min(max(n, 0), a.cap);
-  const int chunk = (n + a.S - 1) / a.S;
-  const int lo = min(n, s * chunk);
-  const int len = min(n, lo + chunk) - lo;
   const int ntiles = (len + kTileRows - 1) / kTileRows;
 
   // Row loads go straight to LDS (global_load_lds), one 8-row group per wave
@@ -500,7 +477,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     lds_barrier();  // statistics published
     if (kMode == kOutPartialF32) return;
     lds_barrier();  // output rows staged by the output waves
-    copy_out_rows<kMode>(a, L, t, s, hg, tid);
+    copy_out_rows<kMode>(a, L, t, part, hg, tid);
     return;
   }
 
@@ -628,7 +605,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       const float m_ref = L.stat[hl], m_true = L.stat[64 + hl], l_tot = L.stat[128 + hl];
       const bool live = m_true != -INFINITY;
       const float f = live ? fast_exp2(m_ref - m_true) : 0.f;  // rebase to the true maximum
-      float* orow = (float*)a.o_part + (((int64_t)t * a.S + s) * a.H + head) * kDV;
+      float* orow = (float*)a.o_part + (part * a.H + head) * kDV;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -637,7 +614,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
               make_float4(o[hb][mb][4 * rq] * f, o[hb][mb][4 * rq + 1] * f,
                           o[hb][mb][4 * rq + 2] * f, o[hb][mb][4 * rq + 3] * f);
       if (j == 0 && lane < 32) {
-        const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
+        const int64_t k = part * a.H + head;
         a.m_part[k] = live ? m_true * kLn2 : -INFINITY;
         a.l_part[k] = l_tot * f;
       }
@@ -664,7 +641,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       }
   }
   lds_barrier();  // output rows staged
-  copy_out_rows<kMode>(a, L, t, s, hg, tid);
+  copy_out_rows<kMode>(a, L, t, part, hg, tid);
   if (lane < 32) {
     // lse / (m, l): output wave j covers heads 32 j .. 32 j + 31, one lane each
     const int hl = 32 * j + (lane & 31);
@@ -677,10 +654,84 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
           a.lse[(int64_t)t * a.H + head] = live ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       } else {
         // m = the split's max logit, l = sum of exp(z - m)
-        const int64_t k = ((int64_t)t * a.S + s) * a.H + head;
+        const int64_t k = part * a.H + head;
         a.m_part[k] = live ? m_true * kLn2 : -INFINITY;
         a.l_part[k] = live ? l_tot * fast_exp2(m_ref - m_true) : 0.f;
       }
+    }
+  }
+}
+
+// Kernel.  Static launch: one workgroup per (token, split, head group) in an
+// XCD-aware order; every workgroup of one token (all splits, all head groups)
+// gets a block id of the same residue mod 8, i.e. runs on the same XCD, so
+// the token's query rows and the KV rows its head groups share are fetched
+// into one L2.  Queue launch (kQueue): a persistent grid pops work items
+// (task, head group) from eight queues, one per XCD: queue x holds the tasks
+// x, x + 8, ... of the plan's table, both head groups of a task next to each
+// other, so the pair runs on one XCD; an exhausted queue sends the workgroup
+// on to the next one, and a workgroup ends when all eight are exhausted
+// (every queue is finite, so every workgroup exits).
+template <int kMode, bool kQueue>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) char s_pbuf[2 * 2 * 2 * 1024];
+  __shared__ __attribute__((aligned(16))) float s_alpha[2 * 64];
+  __shared__ __attribute__((aligned(16))) float s_stat[3 * 64];
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
+  __shared__ int s_bad[2];
+  const DecodeLds L{(lds_t*)s_tiles, (lds_t*)s_pbuf, s_alpha, s_stat, s_ids};
+  // the zero row's address, fetched once: inside the loops its GOT load (a
+  // scalar load, which only a full lgkmcnt(0) wait covers) would drain the
+  // LDS reads in flight
+  const uint8_t* zero_row = g_zero_row;
+  asm volatile("" : "+s"(zero_row));
+
+  if constexpr (!kQueue) {
+    const int bid = blockIdx.x;
+    const int xk = bid >> 3;
+    const int per_token = a.S * a.G;
+    const int t = (xk / per_token) * 8 + (bid & 7);
+    const int rem = xk % per_token;
+    const int s = rem / a.G;
+    const int hg = rem - s * a.G;
+    if (t >= a.T) return;
+    int n = a.counts ? a.counts[t] : a.cap;
+    n = min(max(n, 0), a.cap);
+    const int chunk = (n + a.S - 1) / a.S;
+    const int lo = min(n, s * chunk);
+    const int len = min(n, lo + chunk) - lo;
+    decode_item<kMode>(a, L, s_bad, zero_row, t, lo, len, hg, (int64_t)t * a.S + s);
+  } else {
+    __shared__ int s_item[2];
+    const int ntasks = *a.num_tasks;
+    const int x = blockIdx.x & 7;
+    int qi = 0;  // queues x, x + 1, ... (mod 8) before qi are exhausted
+    for (;;) {
+      __syncthreads();  // the previous item is done with LDS and s_item
+      if (threadIdx.x == 0) {
+        int task = -1, hg = 0;
+        for (; qi < 8; ++qi) {
+          const int qx = (x + qi) & 7;
+          const int k = atomicAdd(a.queue + qx, 1);
+          const int tk = qx + 8 * (k / a.G);
+          if (tk < ntasks) {
+            task = tk;
+            hg = k - (k / a.G) * a.G;
+            break;
+          }
+        }
+        s_item[0] = task;
+        s_item[1] = hg;
+      }
+      __syncthreads();
+      const int task = s_item[0];
+      if (task < 0) break;
+      const int32_t* e = a.tasks + 4 * (int64_t)task;  // row, start, end, split
+      const int row = e[0], lo = e[1], len = e[2] - e[1];
+      decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, s_item[1],
+                         (int64_t)a.row_first[row] + e[3]);
     }
   }
 }
@@ -720,7 +771,7 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
                   const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T, int32_t H,
                   float scale, int32_t S, float* o_part, float* m_part, float* l_part,
                   uint16_t* out, float* lse, hipStream_t stream) {
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = q;
   a.kv = kv;
   a.kv_rows = kv_rows;
@@ -740,11 +791,11 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
   const int64_t blocks = (int64_t)8 * ((T + 7) / 8) * S * a.G;
   if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: grid too large");
   if (mode == kOutPartialF32)
-    sparse_mla_decode_kernel<kOutPartialF32><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+    sparse_mla_decode_kernel<kOutPartialF32, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   else if (mode == kOutPartialBf16)
-    sparse_mla_decode_kernel<kOutPartialBf16><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+    sparse_mla_decode_kernel<kOutPartialBf16, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   else
-    sparse_mla_decode_kernel<kOutFinal><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+    sparse_mla_decode_kernel<kOutFinal, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   return stp::check_launch("sparse_mla_decode_kernel");
 }
 
@@ -844,3 +895,40 @@ extern "C" int stp_sparse_mla_decode_partial_normalized(
   return launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale,
                        num_splits, (float*)o_norm, m_part, l_part, nullptr, nullptr, stream);
 }
+
+namespace stp {
+
+int decode_ids_max() { return kIdsMax; }
+
+int decode_head_groups(int32_t H) { return (H + kHeadsPerWG - 1) / kHeadsPerWG; }
+
+int decode_choose_splits(int32_t T, int32_t H, int32_t cap) { return choose_splits(T, H, cap, 0); }
+
+int launch_decode_tasks(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+                        const int32_t* row_ids, int32_t cap, int32_t T, int32_t H, float scale,
+                        const int32_t* num_tasks, const int32_t* tasks, const int32_t* row_first,
+                        int32_t* queue, int32_t grid, uint16_t* o_norm, float* m_part,
+                        float* l_part, hipStream_t stream) {
+  DecodeArgs a{};
+  a.q = q;
+  a.kv = kv;
+  a.kv_rows = kv_rows;
+  a.row_ids = row_ids;
+  a.cap = cap;
+  a.T = T;
+  a.H = H;
+  a.scale_log2 = scale * kLog2e;
+  a.S = 1;
+  a.G = decode_head_groups(H);
+  a.o_part = o_norm;
+  a.m_part = m_part;
+  a.l_part = l_part;
+  a.num_tasks = num_tasks;
+  a.tasks = tasks;
+  a.row_first = row_first;
+  a.queue = queue;
+  sparse_mla_decode_kernel<kOutPartialBf16, true><<<(unsigned)grid, kThreads, 0, stream>>>(a);
+  return check_launch("sparse_mla_decode_kernel (task queue)");
+}
+
+}  // namespace stp

@@ -137,6 +137,32 @@ def deepseek_case(seed=2000, batch=32, ctx=32768, heads=128, top_k=2048, window=
                       extra={"variant": variant})
 
 
+def ragged_case(seed=2100, batch=128, n_long=8, short_ctx=96, long_ctx=32768, heads=128,
+                top_k=2048, window=128, sinks=4, page_size=64, variant=0):
+    """A ragged decode batch in the DeepSeek shape: most requests are short
+    (context short_ctx: every position is a candidate, |S| = short_ctx), a
+    few long (context long_ctx: top-k + window + sinks, |S| ~ 2180), at
+    seeded positions in the batch -- the "most rows a few blocks, a few rows
+    hundreds" mix of a ragged batch.  Short requests draw min(top_k, ctx)
+    ids and pad with -1.  Page tables cover long_ctx for every request."""
+    rng = np.random.default_rng(seed)
+    pages_per_req = -(-long_ctx // page_size)
+    pool_pages = batch * pages_per_req
+    tables = rng.permutation(pool_pages).astype(np.int32).reshape(batch, pages_per_req)
+    q = normal_bf16(rng, (batch, heads, D_QK))
+    ctxs = np.full(batch, short_ctx, np.int64)
+    ctxs[rng.choice(batch, size=n_long, replace=False)] = long_ctx
+    rng_k = np.random.default_rng([seed, 7919, variant])
+    topk = np.full((batch, top_k), -1, np.int32)
+    for b in range(batch):
+        k = min(top_k, int(ctxs[b]))
+        topk[b, :k] = _uniform_without_replacement(rng_k, int(ctxs[b]), k)
+    return DecodeCase(f"ragged_b{batch}", q, topk, np.arange(batch, dtype=np.int32),
+                      (ctxs - 1).astype(np.int32), tables, page_size, window, sinks,
+                      top_k + window + sinks, pool_pages * page_size, pool_seed=seed + 1,
+                      extra={"contexts": ctxs, "variant": variant})
+
+
 def clustered_topk(rng, ctx, top_k, run=16):
     """top_k ids as top_k/run non-overlapping runs of `run` consecutive tokens."""
     nruns = top_k // run
