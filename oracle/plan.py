@@ -8,8 +8,8 @@ What it states ("5.1.1 · 从索引到 Kernel"):
   * §5.1 (plan / run) and §7.4 (turning a ragged batch into a task table).
     The plan reads each row's length -- here the row's candidate count,
     clamped to [0, cap] as everywhere on this path -- and cuts the row into
-    ceil(n_r / R) tasks of at most R consecutive candidate positions, R
-    being the target task size; a task is (row, start, end, split).  A
+    k_r = ceil(n_r / R) tasks of consecutive candidate positions, R being
+    the target task size; a task is (row, start, end, split).  A
     prefix sum of the per-row task counts gives the global task ids:
     row_first[r] = sum over r' < r of ceil(n_r' / R), and the tasks of row r
     are row_first[r] .. row_first[r + 1] - 1 in split order.
@@ -21,9 +21,12 @@ What it states ("5.1.1 · 从索引到 Kernel"):
     of S equals the single pass).
 
 Readings: a row with n_r = 0 gets no task and its output is the empty-set
-output (out = 0, lse = -inf); the tasks of a row are its first R positions,
-the next R, and so on (the plainest cut that §7.4's count ceil(k_i / R)
-describes).
+output (out = 0, lse = -inf); §7.4 fixes the number of tasks of a row
+(about R candidates each, ceil(k_i / R) of them) but not where the cuts
+fall: here task i of a row covers positions floor(i n / k) .. floor((i + 1)
+n / k) - 1, so a row's tasks differ in size by at most one (none exceeds R,
+none is empty) and no task is a short remainder that leaves the others
+longer than they need to be.
 
 Pins (tests/test_oracle_plan.py): a hand-worked table
 (tests/golden/plan_example.txt); brute force over positions on random small
@@ -56,8 +59,9 @@ def plan_tasks(counts, T, cap, rows_per_task):
     row_first[1:] = np.cumsum(per_row)
     tasks = []
     for r, n in enumerate(n_rows):
-        for k in range(per_row[r]):
-            tasks.append((r, k * R, min(n, (k + 1) * R), k))
+        k = per_row[r]
+        for i in range(k):
+            tasks.append((r, i * n // k, (i + 1) * n // k, i))
     return np.asarray(tasks, dtype=np.int64).reshape(-1, 4), row_first
 
 

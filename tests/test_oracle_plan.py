@@ -54,6 +54,11 @@ def test_positions_covered_once(seed):
     tasks, row_first = plan_tasks(counts, T, cap, R)
     n = np.clip(counts, 0, cap)
     assert len(tasks) == int(sum(-(-int(k) // R) for k in n))
+    sizes = {}
+    for r, a, b, _ in tasks:
+        sizes.setdefault(int(r), []).append(int(b - a))
+    for v in sizes.values():
+        assert max(v) - min(v) <= 1  # a row's tasks differ by at most one
     assert row_first[0] == 0 and row_first[-1] == len(tasks)
     hits = [np.zeros(int(k), dtype=np.int64) for k in n]
     for i, (r, a, b, s) in enumerate(tasks):
@@ -68,7 +73,7 @@ def test_positions_covered_once(seed):
 def test_counts_none_means_cap():
     tasks, row_first = plan_tasks(None, 3, 20, 8)
     assert row_first.tolist() == [0, 3, 6, 9]
-    assert tasks[:3].tolist() == [[0, 0, 8, 0], [0, 8, 16, 1], [0, 16, 20, 2]]
+    assert tasks[:3].tolist() == [[0, 0, 6, 0], [0, 6, 13, 1], [0, 13, 20, 2]]
 
 
 def _small_problem(seed):
