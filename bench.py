@@ -64,7 +64,7 @@ def parse():
                          "(coprime with --sets, so every candidate set is sampled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa", "transfer",
-                                           "fp8"],
+                                           "fp8", "plan"],
                     default="deepseek",
                     help="deepseek: the headline DeepSeek-shaped step (HBM-resident pool); "
                          "hot: the HiSparse hot-buffer decode (64 requests, 16 steps, pool in "
@@ -73,7 +73,8 @@ def parse():
                          "dense paged decode (128 requests, 32 query / 8 KV heads) plus "
                          "prefix-extend (8 x 4096 + 512); transfer: staged bulk host<->device "
                          "transfer of cached prefix rows; fp8: the deepseek step over 656-byte "
-                         "fp8_ds_mla rows; the last five are reported on their own lines")
+                         "fp8_ds_mla rows; plan: the deepseek step through plan/run and HIP graphs, "
+                         "plus a ragged batch; the last six are reported on their own lines")
     ap.add_argument("--locality-variant", choices=["both", "scattered", "clustered"],
                     default="both", help="locality workload: which candidate layout to run")
     ap.add_argument("--skip-auto", action="store_true",
@@ -172,6 +173,23 @@ def median_us(fn, n, sets):
         evs[k][1].record()
     torch.cuda.synchronize()
     return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+
+def throughput_us(fn, n, sets):
+    """Mean time per call of fn(k) over n calls enqueued back to back between
+    two HIP events (host launch cost hidden wherever the device is the slower
+    side)."""
+    import torch
+    for k in range(8):
+        fn(k % sets)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(n):
+        fn(k % sets)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
 
 
 def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
@@ -706,6 +724,168 @@ def bench_fp8(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_plan(args):
+    """Plan / run against the static split decode.
+
+    DeepSeek-shaped step (32 tokens, 128 heads, |S| ~ 2172, eight candidate
+    sets rotating): normalise (no block view) then either the static decode
+    with automatic splits, or plan + run with the task size
+    decode_plan_rows_per_task picks; eager, and the whole step replayed from
+    HIP graphs (one per candidate set, each bound to its own top-k buffer).
+    Ragged batch (128 tokens: 120 with |S| = 96, 8 with |S| ~ 2180, four
+    candidate sets): the static decode with automatic splits against plan +
+    run at several task sizes.  Mean time per call over calls enqueued back to
+    back between two HIP events."""
+    import torch
+
+    import sparse_top_paged_amd as stp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    n_launch = max(50, min(args.steps, 400))
+
+    def setup(cases):
+        c0 = cases[0]
+        q = t(c0.q_bits.view(np.int16)).view(torch.bfloat16)
+        req, qpos, table = t(c0.req_id), t(c0.q_pos), t(c0.block_table)
+        topk = [t(c.topk) for c in cases]
+        norm = [stp.normalize_indices(tk, req, qpos, table, c0.page_size, c0.window,
+                                      c0.num_sinks, c0.cap, block_view=False) for tk in topk]
+        return c0, q, req, qpos, table, topk, norm
+
+    def normalise(c0, req, qpos, table, topk, norm, k):
+        stp.normalize_indices(topk[k], req, qpos, table, c0.page_size, c0.window, c0.num_sinks,
+                              c0.cap, block_view=False, out=norm[k])
+
+    res_extra = {}
+    # ---- DeepSeek-shaped step ----
+    nsets = args.sets
+    cases = [workloads.deepseek_case(variant=v) for v in range(nsets)]
+    c0, q, req, qpos, table, topk, norm = setup(cases)
+    T, H, cap = c0.T, c0.H, c0.cap
+    kv = workloads.pool_torch(c0.kv_rows, c0.pool_seed, dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_s = torch.empty((max(1, stp.decode_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
+                       device=dev)
+    R = stp.decode_plan_rows_per_task(T, H, cap)
+    plan = torch.empty((stp.decode_plan_bytes(T, cap, R) // 4,), dtype=torch.int32, device=dev)
+    ws_r = torch.empty((max(1, stp.decode_run_workspace_bytes(T, H, cap, R)),), dtype=torch.uint8,
+                       device=dev)
+
+    def static_step(k):
+        normalise(c0, req, qpos, table, topk, norm, k)
+        stp.sparse_mla_decode(q, kv, norm[k]["slot"], norm[k]["count"], c0.scale, 0, ws_s, out,
+                              lse)
+
+    def plan_step(k):
+        normalise(c0, req, qpos, table, topk, norm, k)
+        stp.decode_plan(norm[k]["count"], T, cap, R, plan=plan)
+        stp.decode_run(q, kv, norm[k]["slot"], plan, R, c0.scale, ws_r, out, lse)
+
+    def graphs(step):
+        gs = []
+        s = torch.cuda.Stream()
+        for k in range(nsets):
+            step(k)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    step(k)
+            torch.cuda.current_stream().wait_stream(s)
+            gs.append(g)
+        torch.cuda.synchronize()
+        return gs
+
+    static_us = throughput_us(static_step, n_launch, nsets)
+    plan_us = throughput_us(plan_step, n_launch, nsets)
+    g_plan = graphs(plan_step)
+    graph_us = throughput_us(lambda k: g_plan[k].replay(), n_launch, nsets)
+    g_static = graphs(static_step)
+    static_graph_us = throughput_us(lambda k: g_static[k].replay(), n_launch, nsets)
+
+    def run_only(k):
+        stp.decode_plan(norm[k]["count"], T, cap, R, plan=plan)
+        stp.decode_run(q, kv, norm[k]["slot"], plan, R, c0.scale, ws_r, out, lse)
+
+    plan_run_us = throughput_us(run_only, n_launch, nsets)
+    static_dec_us = throughput_us(lambda k: stp.sparse_mla_decode(q, kv, norm[k]["slot"],
+                                                                  norm[k]["count"], c0.scale, 0,
+                                                                  ws_s, out, lse),
+                                  n_launch, nsets)
+    del g_plan, g_static, kv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ---- ragged batch ----
+    rsets = 4
+    rcases = [workloads.ragged_case(variant=v) for v in range(rsets)]
+    r0, rq, rreq, rqpos, rtable, rtopk, rnorm = setup(rcases)
+    for k in range(rsets):
+        normalise(r0, rreq, rqpos, rtable, rtopk, rnorm, k)
+    torch.cuda.synchronize()
+    rT, rcap = r0.T, r0.cap
+    rkv = workloads.pool_torch(r0.kv_rows, r0.pool_seed, dev)
+    rout = torch.empty((rT, H, 512), dtype=torch.bfloat16, device=dev)
+    rlse = torch.empty((rT, H), dtype=torch.float32, device=dev)
+    rws = torch.empty((max(1, stp.decode_workspace_bytes(rT, H, rcap)),), dtype=torch.uint8,
+                      device=dev)
+    r_static = throughput_us(lambda k: stp.sparse_mla_decode(rq, rkv, rnorm[k]["slot"],
+                                                         rnorm[k]["count"], r0.scale, 0, rws,
+                                                         rout, rlse), n_launch, rsets)
+    r_sel = float(np.mean([int(nb["count"].sum().item()) for nb in rnorm]))
+    r_runs = {}
+    for rr in (128, 256, 512, 1024):
+        rplan = torch.empty((stp.decode_plan_bytes(rT, rcap, rr) // 4,), dtype=torch.int32,
+                            device=dev)
+        rwr = torch.empty((max(1, stp.decode_run_workspace_bytes(rT, H, rcap, rr)),),
+                          dtype=torch.uint8, device=dev)
+
+        def rstep(k, rr=rr, rplan=rplan, rwr=rwr):
+            stp.decode_plan(rnorm[k]["count"], rT, rcap, rr, plan=rplan)
+            stp.decode_run(rq, rkv, rnorm[k]["slot"], rplan, rr, r0.scale, rwr, rout, rlse)
+
+        r_runs[str(rr)] = round(throughput_us(rstep, n_launch, rsets), 2)
+        del rplan, rwr
+    best_r = min(r_runs, key=lambda x: r_runs[x])
+    res_extra.update({
+        "ragged_batch": rT, "ragged_mean_selected_rows": round(r_sel / rT, 2),
+        "ragged_static_decode_us": round(r_static, 2),
+        "ragged_plan_run_us_by_rows_per_task": r_runs,
+        "ragged_best_speedup": round(r_static / r_runs[best_r], 3),
+    })
+    res = {
+        "metric": METRIC,
+        "value": round(T / (graph_us * 1e-6), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": n_launch,
+        "warmup": 8,
+        "ms_per_step": round(graph_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "deepseek-v3.2-shaped step (normalise + plan + run) replayed "
+                               "from HIP graphs",
+                   "batch": T, "query_heads": H, "context": 32768, "page_size": c0.page_size,
+                   "top_k": c0.top_k, "rows_per_task": R, "candidate_sets": nsets},
+        "static_step_us": round(static_us, 2),
+        "plan_step_us": round(plan_us, 2),
+        "graph_step_us": round(graph_us, 2),
+        "static_graph_step_us": round(static_graph_us, 2),
+        "plan_and_run_us": round(plan_run_us, 2),
+        "static_decode_and_merge_us": round(static_dec_us, 2),
+    }
+    res.update(res_extra)
+    print(json.dumps(res), flush=True)
+
+
 def gqa_cpu_baseline(c, budget_s):
     """The dense decode oracle on the host, one request at a time (its rows
     from the same seeded pool, regenerated on the host for the pages the
@@ -761,6 +941,9 @@ def main():
         return
     if args.workload == "fp8":
         bench_fp8(args)
+        return
+    if args.workload == "plan":
+        bench_plan(args)
         return
 
     import torch

@@ -257,18 +257,27 @@ size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
  * each count is clamped to [0, cap]) on the device and writes the plan
  * buffer (int32, stp_decode_plan_bytes() bytes, caller-owned device memory):
  *   [0] number of tasks, [1] T, [2] R, [3] max_tasks, [4..11] queue heads
- *   (set to 0), [16 .. 16 + T] row_first (row_first[r] = tasks before row r),
- *   then, from int32 index ceil((17 + T) / 4) * 4, the tasks as 4 int32
- *   (row, start, end, split), row by row in split order.
+ *   (set to 0), [12..19] qcount, [20] qcap = ceil(T / 8) * ceil(cap / R),
+ *   [32 .. 32 + T] row_first (row_first[r] = tasks before row r), then, from
+ *   int32 index ceil((33 + T) / 4) * 4, the tasks as 4 int32 (row, start,
+ *   end, split), row by row in split order (task i of a row of n candidates
+ *   and k tasks covers floor(i n / k) .. floor((i + 1) n / k) - 1), then
+ *   eight queue segments of qcap entries of 4 int32 (row, start,
+ *   end - start, slot = row_first[row] + split, or -1 for a row's only task,
+ *   whose output the run writes directly): queue x (run on XCD x) is
+ *   the first qcount[x] entries of segment x, the tasks of rows x, x + 8,
+ *   x + 16, ... in order.
  * stp_decode_run computes, for every row t, the attention of
  * stp_sparse_mla_decode over row_ids[t, 0 : count_t] (the counts the plan
  * was made from): a persistent grid pops (task, head group) work items from
- * eight queues (one per XCD), writes each task's normalised partial to slot
+ * the eight queues (each workgroup's first item by its block id, later ones
+ * claimed with the queue heads), writes each task's normalised partial to slot
  * row_first[row] + split of the workspace (stp_decode_run_workspace() bytes:
  * bf16 o/l [max_tasks][H][512], then fp32 m and l [max_tasks][H], each
  * 256-byte aligned), and a merge writes out [T, H, 512] bf16 and lse [T, H]
- * (nullable).  The order of the tasks in the table does not change the
- * result: a caller may reorder them.  The run leaves the queue heads at 0, so
+ * (nullable).  The run reads only the queue entries; their order, within a
+ * queue or across queues, does not change the result (each entry carries its
+ * row and slot), so a caller may reorder them.  The run leaves the queue heads at 0, so
  * one plan serves any number of runs; runs over one plan buffer must not
  * overlap in time (they share the queue heads).  Grids depend only on the
  * tier and the device, so plan + run (or run alone) can be captured in a HIP

@@ -21,7 +21,7 @@ __all__ = [
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
     "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
     "decode_fp8_workspace_bytes", "decode_plan", "decode_run", "decode_plan_bytes",
-    "decode_run_workspace_bytes", "decode_plan_rows_per_task", "plan_view",
+    "decode_run_workspace_bytes", "decode_plan_rows_per_task", "plan_view", "plan_queues",
 ]
 
 
@@ -493,8 +493,17 @@ def plan_view(plan, T):
     """(number of tasks, row_first [T + 1], tasks [n, 4]) views of a plan
     buffer, in the layout stp_decode_plan writes."""
     n = int(plan[0].item())
-    off = (17 + T + 3) // 4 * 4
-    return n, plan[16:17 + T], plan[off:off + 4 * n].view(n, 4)
+    off = (33 + T + 3) // 4 * 4
+    return n, plan[32:33 + T], plan[off:off + 4 * n].view(n, 4)
+
+
+def plan_queues(plan, T):
+    """(qcount [8], segments [8, qcap, 4]) views of a plan buffer: the run's
+    eight queues; queue x is segments[x, :qcount[x]], entries (row, start,
+    length, slot)."""
+    max_tasks, qcap = int(plan[3].item()), int(plan[20].item())
+    off = (33 + T + 3) // 4 * 4 + 4 * max_tasks
+    return plan[12:20], plan[off:off + 32 * qcap].view(8, qcap, 4)
 
 
 def decode_run(q, kv, row_ids, plan, rows_per_task, scale=D_QK ** -0.5, workspace=None,

@@ -107,11 +107,12 @@ struct DecodeArgs {
   float* l_part;
   uint16_t* out;   // final mode: [T, H, 512] bf16
   float* lse;
-  // task-queue launch: the plan's task count, (row, start, end, split)
-  // entries, first partial slot of each row and the eight queue heads
-  const int32_t* num_tasks;
-  const int32_t* tasks;
-  const int32_t* row_first;
+  // task-queue launch: queue x's entries are the first qcount[x] of segment
+  // x (qcap entries from qent + 4 qcap x) of (row, start, length, partial
+  // slot); queue heads for claiming them
+  const int32_t* qcount;
+  const int32_t* qent;
+  int qcap;
   int32_t* queue;
 };
 
@@ -319,7 +320,11 @@ template <int kMode>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
                                             int hg, int64_t part) {
-  const int tid = threadIdx.x;
+  // opaque per call, so that nothing derived from the thread index is hoisted
+  // out of the queue launch's item loop (it would stay live across the whole
+  // item and push the registers into spills)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const bool score = wave < 2;
@@ -666,12 +671,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
 // XCD-aware order; every workgroup of one token (all splits, all head groups)
 // gets a block id of the same residue mod 8, i.e. runs on the same XCD, so
 // the token's query rows and the KV rows its head groups share are fetched
-// into one L2.  Queue launch (kQueue): a persistent grid pops work items
+// into one L2.  Queue launch (kQueue): a persistent grid takes work items
 // (task, head group) from eight queues, one per XCD: queue x holds the tasks
-// x, x + 8, ... of the plan's table, both head groups of a task next to each
-// other, so the pair runs on one XCD; an exhausted queue sends the workgroup
-// on to the next one, and a workgroup ends when all eight are exhausted
-// (every queue is finite, so every workgroup exits).
+// of rows x, x + 8, ... (the plan's queue entries), so all splits of a row run
+// on one XCD and share its query rows there, and both head groups of a task
+// sit next to each other, so the pair shares the KV rows in that L2.  Each workgroup's first item is
+// assigned by its block id; later items are claimed with the queue heads,
+// the workgroup's own XCD queue first, then the others.  A task that covers
+// its whole row writes the row's final output and lse itself (its entry's
+// slot is -1); the others write partial states for the merge.  A workgroup ends
+// when no queue has an unclaimed item (every queue is finite and its head
+// only grows, so every workgroup exits).
 template <int kMode, bool kQueue>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
@@ -704,34 +714,96 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const int len = min(n, lo + chunk) - lo;
     decode_item<kMode>(a, L, s_bad, zero_row, t, lo, len, hg, (int64_t)t * a.S + s);
   } else {
-    __shared__ int s_item[2];
-    const int ntasks = *a.num_tasks;
+    const int grid = gridDim.x;
     const int x = blockIdx.x & 7;
+    // queue q: items i = 0 .. items(q) - 1 over its entries (item i is entry
+    // i / G of segment q, head group i % G); the first pre(q) of them are
+    // pre-assigned, one to each workgroup of block id = q (mod 8) (no atomic
+    // for a workgroup's first item), the rest are claimed with the queue head
+    // (an atomic counter from 0) as item pre(q) + head
+    int qc[8];
+#pragma unroll
+    for (int y = 0; y < 8; ++y) qc[y] = a.qcount[y];
+    const int idx = blockIdx.x >> 3;  // the pre-assigned item in queue x
+    int4 e0 = make_int4(-1, 0, 0, 0);
+    if (threadIdx.x == 0 && idx / a.G < a.qcap)  // read together with the counts
+      e0 = *(const int4*)(a.qent + 4 * ((int64_t)x * a.qcap + idx / a.G));
+    auto qsel = [&](int q) {  // qc[q] without dynamic register indexing
+      int v = qc[0];
+#pragma unroll
+      for (int y = 1; y < 8; ++y) v = y == q ? qc[y] : v;
+      return v;
+    };
+    auto items = [&](int q) { return a.G * qsel(q); };
+    auto pre = [&](int q) { return (grid - q + 7) >> 3; };
+    bool dynamic = false;  // does any queue hold items beyond the pre-assigned ones?
+#pragma unroll
+    for (int y = 0; y < 8; ++y) dynamic |= a.G * qc[y] > ((grid - y + 7) >> 3);
     int qi = 0;  // queues x, x + 1, ... (mod 8) before qi are exhausted
+    bool first = true;
+    __shared__ int s_ent[5];
     for (;;) {
-      __syncthreads();  // the previous item is done with LDS and s_item
+      __syncthreads();  // the previous item is done with LDS and s_ent
       if (threadIdx.x == 0) {
-        int task = -1, hg = 0;
-        for (; qi < 8; ++qi) {
-          const int qx = (x + qi) & 7;
-          const int k = atomicAdd(a.queue + qx, 1);
-          const int tk = qx + 8 * (k / a.G);
-          if (tk < ntasks) {
-            task = tk;
-            hg = k - (k / a.G) * a.G;
-            break;
+        int q = x, i = -1;
+        int4 e = e0;
+        if (first && idx < items(x)) {
+          i = idx;
+        } else if (dynamic) {
+          // own queue first, then the others: their heads read in one go, an
+          // atomic only where items remain (so leaving costs at most one
+          // atomic and one read when every queue is drained)
+          if (qi == 0) {
+            if (pre(x) < items(x)) {
+              const int k = pre(x) + atomicAdd(a.queue + x, 1);
+              if (k < items(x)) i = k;
+            }
+            if (i < 0) qi = 1;
           }
+          if (i < 0 && qi < 8) {
+            int head[8];
+#pragma unroll
+            for (int y = 0; y < 8; ++y)
+              head[y] = __hip_atomic_load(a.queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (; qi < 8; ++qi) {
+              q = (x + qi) & 7;
+              int hq = head[0];
+#pragma unroll
+              for (int y = 1; y < 8; ++y) hq = y == q ? head[y] : hq;
+              if (pre(q) + hq >= items(q)) continue;
+              const int k = pre(q) + atomicAdd(a.queue + q, 1);
+              if (k < items(q)) {
+                i = k;
+                break;
+              }
+            }
+          }
+          if (i >= 0) e = *(const int4*)(a.qent + 4 * ((int64_t)q * a.qcap + i / a.G));
         }
-        s_item[0] = task;
-        s_item[1] = hg;
+        first = false;
+        if (i >= 0) {
+          s_ent[0] = e.x;  // row
+          s_ent[1] = e.y;  // start
+          s_ent[2] = e.z;  // length
+          s_ent[3] = e.w;  // partial slot
+          s_ent[4] = i - (i / a.G) * a.G;
+        } else {
+          s_ent[0] = -1;
+        }
       }
       __syncthreads();
-      const int task = s_item[0];
-      if (task < 0) break;
-      const int32_t* e = a.tasks + 4 * (int64_t)task;  // row, start, end, split
-      const int row = e[0], lo = e[1], len = e[2] - e[1];
-      decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, s_item[1],
-                         (int64_t)a.row_first[row] + e[3]);
+      // the item is the same for the whole workgroup: keep it (and all that
+      // derives from it) in scalar registers, as the static launch does
+      const int row = __builtin_amdgcn_readfirstlane(s_ent[0]);
+      if (row < 0) break;
+      const int lo = __builtin_amdgcn_readfirstlane(s_ent[1]);
+      const int len = __builtin_amdgcn_readfirstlane(s_ent[2]);
+      const int part = __builtin_amdgcn_readfirstlane(s_ent[3]);
+      const int hg = __builtin_amdgcn_readfirstlane(s_ent[4]);
+      if (part < 0)  // the row's only task: its output is final
+        decode_item<kOutFinal>(a, L, s_bad, zero_row, row, lo, len, hg, 0);
+      else
+        decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, hg, (int64_t)part);
     }
   }
 }
@@ -906,9 +978,9 @@ int decode_choose_splits(int32_t T, int32_t H, int32_t cap) { return choose_spli
 
 int launch_decode_tasks(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                         const int32_t* row_ids, int32_t cap, int32_t T, int32_t H, float scale,
-                        const int32_t* num_tasks, const int32_t* tasks, const int32_t* row_first,
-                        int32_t* queue, int32_t grid, uint16_t* o_norm, float* m_part,
-                        float* l_part, hipStream_t stream) {
+                        const int32_t* qcount, const int32_t* qent, int32_t qcap, int32_t* queue,
+                        int32_t grid, uint16_t* o_norm, float* m_part, float* l_part,
+                        uint16_t* out, float* lse, hipStream_t stream) {
   DecodeArgs a{};
   a.q = q;
   a.kv = kv;
@@ -923,9 +995,11 @@ int launch_decode_tasks(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
   a.o_part = o_norm;
   a.m_part = m_part;
   a.l_part = l_part;
-  a.num_tasks = num_tasks;
-  a.tasks = tasks;
-  a.row_first = row_first;
+  a.out = out;
+  a.lse = lse;
+  a.qcount = qcount;
+  a.qent = qent;
+  a.qcap = qcap;
   a.queue = queue;
   sparse_mla_decode_kernel<kOutPartialBf16, true><<<(unsigned)grid, kThreads, 0, stream>>>(a);
   return check_launch("sparse_mla_decode_kernel (task queue)");

@@ -148,14 +148,17 @@ int launch_merge(const float* o_part, const float* m_part, const float* l_part, 
 int launch_merge_normalized(const uint16_t* o_norm, const float* m_part, const float* l_part, int T,
                             int S, int H, int dv, uint16_t* out, float* lse, hipStream_t stream);
 
-// Sparse MLA decode over a plan's task table (decode.hip): a persistent grid
-// of `grid` workgroups pops (task, head group) items from the eight queue
-// heads and writes normalised bf16 partials to slot row_first[row] + split.
+// Sparse MLA decode over a plan's queues (decode.hip): a persistent grid of
+// `grid` workgroups takes (entry, head group) items from eight queues (the
+// first qcount[x] entries of segment x, qcap entries from qent + 4 qcap x,
+// each (row, start, length, slot), claimed with the queue heads) and writes
+// normalised bf16 partials to their slots, or, for slot -1 (a task that
+// covers its whole row), the row's final out and lse.
 int launch_decode_tasks(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                         const int32_t* row_ids, int32_t cap, int32_t T, int32_t H, float scale,
-                        const int32_t* num_tasks, const int32_t* tasks, const int32_t* row_first,
-                        int32_t* queue, int32_t grid, uint16_t* o_norm, float* m_part,
-                        float* l_part, hipStream_t stream);
+                        const int32_t* qcount, const int32_t* qent, int32_t qcap, int32_t* queue,
+                        int32_t grid, uint16_t* o_norm, float* m_part, float* l_part,
+                        uint16_t* out, float* lse, hipStream_t stream);
 int decode_ids_max();                 // candidate positions one work item may hold
 int decode_head_groups(int32_t H);    // work items per task
 int decode_choose_splits(int32_t T, int32_t H, int32_t cap);

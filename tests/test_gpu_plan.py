@@ -4,8 +4,8 @@ tier, persistent work queue, graph capture).
 The plan's task table is integer work and must equal the oracle's
 (oracle.plan_tasks) exactly.  The run's output is compared with the fp64
 attention oracle at the bf16 tolerance of helpers.assert_attention_close.
-Reordering the task table must not change a single output bit (each task's
-partial goes to the slot of its own (row, split)).
+Reordering the run's queue entries must not change a single output bit (each
+entry carries its row and the slot of its (row, split)).
 """
 
 import numpy as np
@@ -48,6 +48,18 @@ def test_plan_table_bit_exact(T, cap, R, seed):
     hdr = plan[:12].cpu().numpy()
     assert hdr[1] == T and hdr[2] == R and np.all(hdr[4:12] == 0)
     assert hdr[3] == (T * (-(-cap // R)) if cap > 0 else 0)
+    # the run's queues: queue x holds the tasks of rows x, x + 8, ... in order,
+    # each as (row, start, length, slot = row_first[row] + split, -1 for a
+    # row's only task)
+    qcount, seg = (v.cpu().numpy() for v in stp.plan_queues(plan, T))
+    for x in range(8):
+        one = lambda r: ref_first[r + 1] - ref_first[r] == 1  # noqa: E731
+        expect = [(ref_tasks[i][0], ref_tasks[i][1], ref_tasks[i][2] - ref_tasks[i][1],
+                   -1 if one(r) else ref_first[r] + ref_tasks[i][3])
+                  for r in range(x, T, 8) for i in range(ref_first[r], ref_first[r + 1])]
+        assert qcount[x] == len(expect)
+        assert np.array_equal(seg[x, :qcount[x]].reshape(-1, 4),
+                              np.asarray(expect, dtype=np.int64).reshape(-1, 4))
 
 
 def test_plan_counts_none_means_cap():
@@ -86,8 +98,9 @@ def test_run_against_oracle(T, H, cap, R):
         assert torch.all(out[2] == 0) and torch.all(torch.isneginf(lse[2]))
 
 
-def test_shuffled_table_and_repeated_runs_bit_identical():
-    """Any order of the task table gives the same bits; one plan serves many runs."""
+def test_shuffled_queues_and_repeated_runs_bit_identical():
+    """Any order of the queue entries (within and across the eight queues)
+    gives the same bits; one plan serves many runs."""
     stp = _stp()
     T, H, cap, R = 10, 128, 500, 48
     q_bits, kv_bits, ids, counts = _random_problem(31, T, H, cap)
@@ -97,9 +110,13 @@ def test_shuffled_table_and_repeated_runs_bit_identical():
     out2, lse2 = stp.decode_run(q, kv, idd, plan, R, 0.05)  # queue heads were reset
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
-    n, _, tasks = stp.plan_view(plan, T)
-    perm = torch.from_numpy(np.random.default_rng(32).permutation(n)).to(plan.device)
-    tasks.copy_(tasks[perm].clone())
+    qcount, seg = stp.plan_queues(plan, T)
+    counts_q = qcount.cpu().numpy()
+    where = [(x, j) for x in range(8) for j in range(int(counts_q[x]))]
+    entries = torch.stack([seg[x, j].clone() for x, j in where])
+    perm = np.random.default_rng(32).permutation(len(where))
+    for (x, j), p in zip(where, perm):  # every entry moves, across queues too
+        seg[x, j].copy_(entries[int(p)])
     out3, lse3 = stp.decode_run(q, kv, idd, plan, R, 0.05)
     torch.cuda.synchronize()
     assert torch.equal(out1, out3) and torch.equal(lse1, lse3)
