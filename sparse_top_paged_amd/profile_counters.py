@@ -6,6 +6,13 @@ benchmark (run by path, on any host; it reads CSV files only).
         <write counter_collection.csv> <kernel source> <out.json> "<command>" [<kernel name>]
     python sparse_top_paged_amd/profile_counters.py counters <out.txt> "<command>" \\
         <counter_collection.csv> [<counter_collection.csv> ...]
+    python sparse_top_paged_amd/profile_counters.py trace <kernel_trace.csv> <out.txt> \\
+        "<command>" [<kernel substring>@<grid size x> ...]
+
+`trace` reads a kernel trace and reports, per kernel and grid size, the
+median duration of its dispatches, with the timeline split into phases at
+the first dispatch of each "kernel@grid" marker given (a benchmark that runs
+several workloads one after the other).
 
 `counters` averages every counter per dispatch for the decode kernel and the
 row-gather diagnostic (whose launches come in two runs of equal length: the
@@ -104,6 +111,42 @@ def traffic(fetch_csv, write_csv, kernel_src, out, command, kernel=DECODE_KERNEL
     open(out, "a").write("\n")
 
 
+def trace(src, out, command, *markers):
+    """Median duration per (phase, kernel, grid) from a kernel trace."""
+    rows = sorted(csv.DictReader(open(src)), key=lambda r: int(r["Start_Timestamp"]))
+    starts = []
+    for m in markers:
+        name, grid = m.rsplit("@", 1)
+        hit = [int(r["Start_Timestamp"]) for r in rows
+               if name in r["Kernel_Name"] and r["Grid_Size_X"] == grid]
+        if hit:
+            starts.append((hit[0], m))
+    starts.sort()
+    groups = defaultdict(list)
+    for r in rows:
+        t0 = int(r["Start_Timestamp"])
+        phase = 0
+        for i, (ts, _) in enumerate(starts):
+            if t0 >= ts:
+                phase = i + 1
+        k = short_name(r["Kernel_Name"])
+        if k.startswith("__amd") or "at::native" in k:
+            continue
+        groups[(phase, k, int(r["Grid_Size_X"]))].append(
+            (int(r["End_Timestamp"]) - t0) / 1e3)
+    lines = ["# rocprofv3 kernel trace, median per kernel and grid size", f"# command: {command}",
+             "# phases: 0 = start" + "".join(f"; {i + 1} = from the first {m}"
+                                                for i, (_, m) in enumerate(starts)),
+             "#", f"{'phase':>5} {'kernel':<52} {'grid_x':>8} {'calls':>6} {'median_us':>10} "
+                  f"{'p10_us':>8} {'p90_us':>8}"]
+    for (phase, k, g), ds in sorted(groups.items()):
+        ds.sort()
+        pick = lambda f: ds[min(len(ds) - 1, int(f * len(ds)))]  # noqa: E731
+        lines.append(f"{phase:>5} {k:<52} {g:>8} {len(ds):>6} {pick(0.5):>10.2f} "
+                     f"{pick(0.1):>8.2f} {pick(0.9):>8.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def counters(out, command, *paths):
     """Per-dispatch means of every collected counter, per kernel of interest."""
     groups = defaultdict(lambda: defaultdict(dict))  # kernel -> dispatch -> counter -> value
@@ -155,5 +198,7 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:8])
     elif sys.argv[1] == "counters":
         counters(*sys.argv[2:])
+    elif sys.argv[1] == "trace":
+        trace(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
