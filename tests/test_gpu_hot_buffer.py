@@ -113,6 +113,14 @@ def test_multistep_full_width_rows():
     assert s[0] > 0
 
 
+def test_multistep_fp8_rows():
+    # 656-byte fp8_ds_mla rows (41 16-byte vectors each) at the real top-k and
+    # hot size: lookup, swap-in and back-up byte for byte against the oracle
+    s = _run_steps(batch=4, steps=4, top_k=2048, window=128, sinks=4, P=64, ctx0=8192,
+                   row_bytes=656)
+    assert s[0] > 0
+
+
 def test_multistep_unstaged_state():
     # hot_size 8192: the LRU order and stored ids no longer fit in LDS beside
     # the hash, so the lookup reads them from global memory
