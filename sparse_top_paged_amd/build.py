@@ -34,9 +34,15 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  dense.hip: its softmax takes maxima of finite
+# scores and -inf masks only, so fmaxf needs no NaN handling; without it the
+# extend kernel's VALU work shrinks (measured 13 % faster, identical output).
+EXTRA_FLAGS = {"dense.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
