@@ -37,7 +37,11 @@ FLAGS = [
 # Per-source extra flags.  dense.hip: its softmax takes maxima of finite
 # scores and -inf masks only, so fmaxf needs no NaN handling; without it the
 # extend kernel's VALU work shrinks (measured 13 % faster, identical output).
-EXTRA_FLAGS = {"dense.hip": ["-fno-honor-nans"]}
+# decode_fp8.hip: MFMA results in VGPRs, so that O^T (128 registers) stays in
+# one register file instead of being moved between AGPRs and VGPRs around
+# the QK accumulators on every tile.
+EXTRA_FLAGS = {"dense.hip": ["-fno-honor-nans"],
+               "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src):

@@ -35,10 +35,12 @@
 // 2^8 rescale; invalid candidates load the zero row and are masked.  Splits
 // write normalised bf16 partial states merged by the split-KV merge kernel.
 // Cost: every wave reads the whole bf16 tile for its 16 heads (about 330 KB
-// of LDS traffic per tile and workgroup), and one wave per SIMD holds Q^T,
-// O^T and the accumulators at once, which leaves the compiler moving
-// accumulators between AGPRs; together they make the per-tile compute,
-// not the row gather, the bound of this kernel.
+// of LDS traffic per tile and workgroup), which makes the per-tile compute,
+// not the row gather, the bound of this kernel.  The MFMAs write VGPRs (a
+// build flag of this file), so O^T stays in one register file across the
+// tile instead of moving between AGPRs and VGPRs around the QK accumulators;
+// bf16 rows are 1184 B apart, so the eight rows a half-wave's transposed V
+// read touches fall on distinct banks.
 
 #include <algorithm>
 
@@ -55,7 +57,7 @@ constexpr int kSlots = 6;                   // loads per thread and tile: 6 * 25
 constexpr int kStageBytes = kSlots * kThreads * 16;  // 24 KiB (the last 224 slots pad)
 constexpr int kStages = 3;                  // raw-row ring (two tiles in flight)
 constexpr int kIdsMax = 1024;               // candidate ids of a split, staged in LDS
-constexpr int kBfStride = 1168;             // bf16 tile row: 576 values + 16 B of bank offset
+constexpr int kBfStride = 1184;             // bf16 tile row: 576 values + 32 B of bank offset
 constexpr int kBfBytes = kTileRows * kBfStride;
 constexpr int kDQK = 576;
 constexpr int kDV = 512;
@@ -308,16 +310,6 @@ void sparse_mla_decode_fp8_kernel(Fp8Args a) {
     const uintx4 rope = *(const __attribute__((address_space(3))) uintx4*)(raw + rp_raw);
     const floatx4 nscale = *(const __attribute__((address_space(3))) floatx4*)(raw + sc_raw);
     const uint32_t vmask = (uint32_t)__ballot(s_ids[r0 + (lane & 31)] >= 0);
-    float sc[2][4][4];  // scales of this lane's accumulator rows 16 mbk + 4 gq + r
-#pragma unroll
-    for (int mbk = 0; mbk < 2; ++mbk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const floatx4 v = *(const __attribute__((address_space(3))) floatx4*)&s_scale[it & 1]
-                                                                                [16 * mbk + 4 * gq + r][0];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) sc[mbk][r][g] = v[g];
-      }
     __builtin_amdgcn_sched_barrier(0);
 
     // S^T = K Q^T: 36 MFMA steps, each with the K read eight steps ahead and a
@@ -359,6 +351,25 @@ void sparse_mla_decode_fp8_kernel(Fp8Args a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // the S^T accumulators live in VGPRs (the AGPRs hold O^T and Q^T; letting
+    // the accumulators take AGPRs makes the compiler move O^T out and back)
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+      asm volatile("" : "+v"(acc[g][0]));
+      asm volatile("" : "+v"(acc[g][1]));
+    }
+    // this tile's scales (rows 16 mbk + 4 gq + r of this lane's accumulators),
+    // read only now: during the QK steps their registers hold K fragments
+    float sc[2][4][4];
+#pragma unroll
+    for (int mbk = 0; mbk < 2; ++mbk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const floatx4 v = *(const __attribute__((address_space(3))) floatx4*)&s_scale[it & 1]
+                                                                                [16 * mbk + 4 * gq + r][0];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) sc[mbk][r][g] = v[g];
+      }
     // V ring for the PV steps, eight steps ahead, read while the softmax runs
     shortx4 vlo[8], vhi[8];
 #pragma unroll
