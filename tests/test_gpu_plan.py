@@ -234,3 +234,23 @@ def test_full_size_sampled(which):
     assert (lse - l2).abs().max().item() < 1e-2
     del kv
     torch.cuda.empty_cache()
+
+
+def test_smaller_batch_in_a_larger_tier():
+    """A batch of 5 rows run in a tier of 8 (rows 5..7 padded with count 0):
+    the real rows equal the 5-row tier's output bit for bit, the padding rows
+    are out = 0, lse = -inf."""
+    stp = _stp()
+    T, Tt, H, cap, R = 5, 8, 64, 260, 64
+    q_bits, kv_bits, ids, counts = _random_problem(51, T, H, cap)
+    kv = bf16_dev(kv_bits)
+    plan = stp.decode_plan(to_dev(counts), T, cap, R)
+    out, lse = stp.decode_run(bf16_dev(q_bits), kv, to_dev(ids), plan, R, 0.05)
+    qp = np.concatenate([q_bits, np.zeros((Tt - T, H, 576), q_bits.dtype)])
+    ip = np.concatenate([ids, np.full((Tt - T, cap), -1, np.int32)])
+    cp = np.concatenate([counts, np.zeros(Tt - T, np.int32)])
+    plan_t = stp.decode_plan(to_dev(cp), Tt, cap, R)
+    out_t, lse_t = stp.decode_run(bf16_dev(qp), kv, to_dev(ip), plan_t, R, 0.05)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t[:T], out) and torch.equal(lse_t[:T], lse)
+    assert torch.all(out_t[T:] == 0) and torch.all(torch.isneginf(lse_t[T:]))
