@@ -179,12 +179,53 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 // Merge of each row's partial slots row_first[t] .. row_first[t + 1] - 1
 // (rows with exactly one task already hold their output and are skipped)
 // (the partition combine of normalised outputs: weights l_p e^(m_p - M) / L
-// over the slots with l_p > 0), in one pass over chunks of eight slots whose
-// loads are all issued together; across chunks the running maximum moves
-// and rescales the sums, as in the online softmax.  A row without a live
+// over the slots with l_p > 0), in one pass over chunks of four (rows of at
+// most four slots) or eight slots whose loads are all issued together;
+// across chunks the running maximum moves and rescales the sums, as in the
+// online softmax.  A row without a live
 // slot gets out = 0 and lse = -inf.  Block (0, 0) also clears the queue
 // heads for the next run.
-constexpr int kMergeChunk = 8;
+// One chunk of up to N slots pb .. min(pb + N, p1) - 1 folded into the
+// running (M, L, acc); every load of the chunk is issued before any use.
+template <int N>
+__device__ __forceinline__ void merge_chunk(const uint16_t* __restrict__ o_norm,
+                                            const float* __restrict__ m_part,
+                                            const float* __restrict__ l_part, int pb, int p1,
+                                            int H, int h, int c, float& M, float& L,
+                                            float4& acc) {
+  float mv[N], lv[N];
+  uint2 ov[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool in = pb + i < p1;
+    const int64_t k = (int64_t)(in ? pb + i : pb) * H + h;  // in bounds either way
+    mv[i] = m_part[k];
+    lv[i] = in ? l_part[k] : 0.f;
+    ov[i] = *(const uint2*)(o_norm + k * kDV + c);
+  }
+  float Mc = M;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (lv[i] > 0.f) Mc = fmaxf(Mc, mv[i]);
+  if (Mc == -INFINITY) return;  // no live slot yet
+  const float f = expf(M - Mc);   // 0 while nothing was live
+  L *= f;
+  acc.x *= f;
+  acc.y *= f;
+  acc.z *= f;
+  acc.w *= f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (!(lv[i] > 0.f)) continue;
+    const float w = expf(mv[i] - Mc) * lv[i];
+    L += w;
+    acc.x += w * __uint_as_float(ov[i].x << 16);
+    acc.y += w * __uint_as_float(ov[i].x & 0xffff0000u);
+    acc.z += w * __uint_as_float(ov[i].y << 16);
+    acc.w += w * __uint_as_float(ov[i].y & 0xffff0000u);
+  }
+  M = Mc;
+}
 
 __global__ __launch_bounds__(kMergeThreads) void task_merge_kernel(
     const uint16_t* __restrict__ o_norm, const float* __restrict__ m_part,
@@ -200,39 +241,11 @@ __global__ __launch_bounds__(kMergeThreads) void task_merge_kernel(
   uint16_t* orow = out + ((int64_t)t * H + h) * kDV;
   float M = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int pb = p0; pb < p1; pb += kMergeChunk) {
-    float mv[kMergeChunk], lv[kMergeChunk];
-    uint2 ov[kMergeChunk];
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i) {
-      const bool in = pb + i < p1;
-      const int64_t k = (int64_t)(in ? pb + i : pb) * H + h;  // in bounds either way
-      mv[i] = m_part[k];
-      lv[i] = in ? l_part[k] : 0.f;
-      ov[i] = *(const uint2*)(o_norm + k * kDV + c);
-    }
-    float Mc = M;
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i)
-      if (lv[i] > 0.f) Mc = fmaxf(Mc, mv[i]);
-    if (Mc == -INFINITY) continue;  // no live slot yet
-    const float f = expf(M - Mc);   // 0 while nothing was live
-    L *= f;
-    acc.x *= f;
-    acc.y *= f;
-    acc.z *= f;
-    acc.w *= f;
-#pragma unroll
-    for (int i = 0; i < kMergeChunk; ++i) {
-      if (!(lv[i] > 0.f)) continue;
-      const float w = expf(mv[i] - Mc) * lv[i];
-      L += w;
-      acc.x += w * __uint_as_float(ov[i].x << 16);
-      acc.y += w * __uint_as_float(ov[i].x & 0xffff0000u);
-      acc.z += w * __uint_as_float(ov[i].y << 16);
-      acc.w += w * __uint_as_float(ov[i].y & 0xffff0000u);
-    }
-    M = Mc;
+  if (p1 - p0 <= 4) {  // the common case: one short chunk
+    if (p1 > p0) merge_chunk<4>(o_norm, m_part, l_part, p0, p1, H, h, c, M, L, acc);
+  } else {
+    for (int pb = p0; pb < p1; pb += 8)
+      merge_chunk<8>(o_norm, m_part, l_part, pb, p1, H, h, c, M, L, acc);
   }
   if (M == -INFINITY) {
     *(uint2*)(orow + c) = make_uint2(0u, 0u);
