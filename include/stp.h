@@ -209,7 +209,7 @@ int stp_backup_rows(const void* hot_cache, int64_t hot_rows, void* host_pool, in
  * workspace of stp_sparse_mla_decode_workspace() bytes (STP_ERR_WORKSPACE if
  * smaller); the workspace may be reused once the call's work has completed
  * on `stream`.
- * The split count is raised to at least ceil(cap / 1024) whatever is asked
+ * The split count is raised to at least ceil(cap / 1120) whatever is asked
  * (a split's ids are staged in LDS).
  * Requirements: T >= 0, H >= 1, cap >= 0, 0 < kv_rows, 0 < scale < inf.
  */
@@ -250,7 +250,7 @@ size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
  *
  * A tier is (T, cap, rows_per_task = R): T rows (pad a smaller batch with
  * rows whose count is 0: they get no task, out = 0 and lse = -inf), at most
- * cap candidates per row, at most R (1 <= R <= 1024) candidate positions per
+ * cap candidates per row, at most R (1 <= R <= 1120) candidate positions per
  * task.  max_tasks = T * ceil(cap / R).
  *
  * stp_decode_plan reads counts [T] (nullable: every row has cap candidates;
@@ -282,7 +282,7 @@ size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
  * overlap in time (they share the queue heads).  Grids depend only on the
  * tier and the device, so plan + run (or run alone) can be captured in a HIP
  * graph and replayed after the counts and candidates change in place.
- * Errors: STP_ERR_INVALID_ARG for bad sizes, R outside [1, 1024] or null
+ * Errors: STP_ERR_INVALID_ARG for bad sizes, R outside [1, 1120] or null
  * pointers; STP_ERR_WORKSPACE when the plan buffer or workspace is smaller
  * than the tier needs.
  */

@@ -60,7 +60,7 @@ constexpr int kTileBytes = 4 * kGroupBytes;                     // 37376
 constexpr int kStages = 4;
 constexpr int kSlotsPerThread = kTileRows * kChunks / kThreads; // 9
 constexpr int kHeadsPerWG = 64;
-constexpr int kIdsMax = 1024;
+constexpr int kIdsMax = 1120;  // 35 tiles: half of a 2180-candidate list fits (what the LDS has left)
 constexpr int kQKSteps = kDQK / 16;                             // 36
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

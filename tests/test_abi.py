@@ -111,15 +111,15 @@ def test_host_side_validation():
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 8, 128, -1, 0.1, fake, None, None) == STP_ERR_INVALID_ARG
     assert ext(fake, fake, fake, 64, fake, fake, fake, 2, 32, 8, 128, 0, 0.1, fake, None, None) == 0
     assert ext(fake, fake, fake, 64, fake, fake, fake, 0, 32, 8, 128, 64, 0.1, fake, None, None) == 0
-    # plan / run: task size in [1, 1024], plan buffer and workspace sized for the tier
+    # plan / run: task size in [1, 1120], plan buffer and workspace sized for the tier
     assert lib.stp_decode_plan_bytes(3, 50, 16) == (36 + 4 * 3 * 4 + 32 * 4) * 4
     assert lib.stp_decode_plan_bytes(3, 0, 16) == 36 * 4
     assert lib.stp_decode_run_workspace(3, 16, 50, 16) == 12 * 16 * 1024 + 2 * 768
     assert lib.stp_decode_plan_rows_per_task(32, 128, 2180) % 32 == 0
-    assert 32 <= lib.stp_decode_plan_rows_per_task(32, 128, 2180) <= 1024
+    assert 32 <= lib.stp_decode_plan_rows_per_task(32, 128, 2180) <= 1120
     plan = lib.stp_decode_plan
     assert plan(fake, 3, 50, 0, fake, 1 << 20, None) == STP_ERR_INVALID_ARG
-    assert plan(fake, 3, 50, 1025, fake, 1 << 20, None) == STP_ERR_INVALID_ARG
+    assert plan(fake, 3, 50, 1121, fake, 1 << 20, None) == STP_ERR_INVALID_ARG
     assert plan(fake, -1, 50, 16, fake, 1 << 20, None) == STP_ERR_INVALID_ARG
     assert plan(fake, 3, 50, 16, fake, 847, None) == STP_ERR_WORKSPACE
     assert plan(fake, 3, 50, 16, None, 1 << 20, None) == STP_ERR_INVALID_ARG
