@@ -65,24 +65,6 @@ typedef __attribute__((address_space(3))) char lds_t;
 __device__ __forceinline__ int key_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int t, int c) { return t * kRowBytes + ((c ^ key_swz(t)) << 4); }
 
-// Word e of a 16-byte vector as two halves.  The word is copied to a scalar
-// first: hipcc's __builtin_bit_cast applied to a vector component directly
-// reads component 0.
-__device__ __forceinline__ halfx2 word_h2(uintx4 w, int e) {
-  const uint32_t we = w[e];
-  return __builtin_bit_cast(halfx2, we);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 using stp::lds_barrier;
 using stp::load_lds_16;
 using stp::pair_max;
