@@ -46,9 +46,11 @@ ROW_BYTES = 1152
 METRIC = "decode query-tokens/sec and effective KV GB/s (% HBM/MFMA roofline), 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 GQA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_decode_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_decode_traffic.json")
 DENSE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "dense.hip")
 COPY_CAL_BYTES = 256 << 20
 DECODE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode.hip")
+FP8_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode_fp8.hip")
 
 
 def parse():
@@ -190,6 +192,32 @@ def throughput_us(fn, n, sets):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / n
+
+
+def graph_us(fn, reps=20, replays=20):
+    """Device time of fn() for a launch too short to hide the host's launch
+    cost: reps calls captured in one HIP graph, the graph replayed between
+    two HIP events, divided by reps * replays."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * replays)
 
 
 def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
@@ -678,6 +706,17 @@ def bench_fp8(args):
     f_us = median_us(lambda k: stp.sparse_mla_decode_fp8(q, kv8, norm[k]["slot"],
                                                          norm[k]["count"], c0.scale, 0, ws8,
                                                          out, lse), n_launch, nsets)
+    # the split merge of the same partial states on its own, so that the fp8
+    # decode kernel's launch time is the call's time less the merge's
+    n_part = T * s8 * H
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    o_norm = ws8[:n_part * 512 * 2].view(torch.bfloat16).view(T, s8, H, 512)
+    m_part = ws8[a256(n_part * 1024):a256(n_part * 1024) + n_part * 4].view(torch.float32)
+    l_off = a256(n_part * 1024) + a256(n_part * 4)
+    l_part = ws8[l_off:l_off + n_part * 4].view(torch.float32)
+    merge_us = graph_us(lambda: stp.splitkv_merge_normalized(
+        o_norm, m_part.view(T, s8, H), l_part.view(T, s8, H), out, lse)) if s8 > 1 else 0.0
+    dec8_us = f_us - merge_us
     del kv8
     torch.cuda.empty_cache()
     kvb = workloads.pool_torch(c0.kv_rows, c0.pool_seed, dev)
@@ -693,6 +732,7 @@ def bench_fp8(args):
     q_bytes = T * H * 576 * 2
     alg8 = sel * 656 + q_bytes + sel * 4
     step_us = n_us + f_us
+    traffic8 = load_traffic(alg8, FP8_TRAFFIC_FILE, FP8_SRC)
     res = {
         "metric": METRIC,
         "value": round(T / (step_us * 1e-6), 1),
@@ -711,8 +751,16 @@ def bench_fp8(args):
                    "top_k": c0.top_k, "row_bytes": 656, "kv_pool_rows": c0.kv_rows,
                    "splits": s8, "candidate_sets": nsets,
                    "mean_selected_rows_per_token": round(sel / T, 2)},
+        "roofline": {"kernel": "sparse_mla_decode_fp8_kernel", "bound": "hbm",
+                     "achieved": round(alg8 / dec8_us / 1e3, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(alg8 / dec8_us / 1e3 / 8000.0, 4), "traffic": traffic8,
+                     "algorithmic_bytes_per_launch": int(alg8),
+                     "avg_launch_us": round(dec8_us, 3),
+                     "launch_time": "decode + merge call less the merge's device time "
+                                    "(20 merges in one HIP graph)"},
         "normalise_us": round(n_us, 2),
         "fp8_decode_and_merge_us": round(f_us, 2),
+        "fp8_merge_us": round(merge_us, 2),
         "bf16_decode_and_merge_us": round(b_us, 2),
         "bf16_splits": sb,
         "kv_bytes_fp8": int(sel * 656),
