@@ -275,9 +275,10 @@ size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
  * row_first[row] + split of the workspace (stp_decode_run_workspace() bytes:
  * bf16 o/l [max_tasks][H][512], then fp32 m and l [max_tasks][H], each
  * 256-byte aligned), and a merge writes out [T, H, 512] bf16 and lse [T, H]
- * (nullable).  The run reads only the queue entries; their order, within a
- * queue or across queues, does not change the result (each entry carries its
- * row and slot), so a caller may reorder them.  The run leaves the queue heads at 0, so
+ * (nullable); a row's only task writes that row's out and lse itself.  The
+ * run reads only the queue entries; their order, within a queue or across
+ * queues, does not change the result (each entry carries its row and slot),
+ * so a caller may reorder them.  The run leaves the queue heads at 0, so
  * one plan serves any number of runs; runs over one plan buffer must not
  * overlap in time (they share the queue heads).  Grids depend only on the
  * tier and the device, so plan + run (or run alone) can be captured in a HIP
@@ -294,7 +295,7 @@ int stp_decode_run(const uint16_t* q, const uint16_t* kv, int64_t kv_rows, const
                    uint16_t* out, float* lse, hipStream_t stream);
 /* Bytes of the plan buffer and of the run workspace of a tier (0 for bad
  * sizes), and a task size R for (T, H, cap): the static split's range
- * rounded up to whole 32-row tiles, at most 1024. */
+ * rounded up to whole 32-row tiles, at most 1120. */
 size_t stp_decode_plan_bytes(int32_t T, int32_t cap, int32_t rows_per_task);
 size_t stp_decode_run_workspace(int32_t T, int32_t H, int32_t cap, int32_t rows_per_task);
 int32_t stp_decode_plan_rows_per_task(int32_t T, int32_t H, int32_t cap);
