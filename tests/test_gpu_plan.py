@@ -254,3 +254,22 @@ def test_smaller_batch_in_a_larger_tier():
     torch.cuda.synchronize()
     assert torch.equal(out_t[:T], out) and torch.equal(lse_t[:T], lse)
     assert torch.all(out_t[T:] == 0) and torch.all(torch.isneginf(lse_t[T:]))
+
+
+def test_one_queue_claimed_by_every_xcd():
+    """One row of 1000 one-candidate tasks: all 2000 work items sit in queue 0,
+    most beyond the pre-assigned ones, so workgroups of every XCD claim them
+    through the queue head; a lost item would leave its slot stale."""
+    stp = _stp()
+    T, H, cap, R = 1, 128, 1000, 1
+    q_bits, kv_bits, ids, counts = _random_problem(61, T, H, cap, rows=1500)
+    counts[:] = cap
+    plan = stp.decode_plan(to_dev(counts), T, cap, R)
+    ws = torch.full((stp.decode_run_workspace_bytes(T, H, cap, R),), 0x7f, dtype=torch.uint8,
+                    device=dev())  # stale slots would read as large finite garbage
+    out, lse = stp.decode_run(bf16_dev(q_bits), bf16_dev(kv_bits), to_dev(ids), plan, R, 0.05,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, counts, 0.05)
+    assert_attention_close(out, lse, o_ref, l_ref, "single queue")
+    assert torch.all(plan[4:12] == 0)  # the merge cleared the queue heads
