@@ -113,6 +113,32 @@ int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req
                           hipStream_t stream);
 
 /*
+ * The same normalisation in two calls, so that the block view, which the
+ * decode does not read, can run on another stream (after the decode, beside
+ * the merge: the decode's workgroups hold every compute unit's LDS).
+ * stp_normalize_indices_deferred takes the arguments of stp_normalize_indices
+ * and writes everything but the block view's logical / page / mask arrays;
+ * blk_indptr then holds per-token intermediate values.  stp_block_view_fill,
+ * enqueued after it with the same tok_out, count_out, req_id, q_pos,
+ * block_table, sizes and block-view arrays, completes the view; until it has
+ * run, blk_indptr is not the CSR index.  The pair's results equal one
+ * stp_normalize_indices call.  Errors as stp_normalize_indices.
+ */
+int stp_normalize_indices_deferred(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                                   const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                                   int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+                                   int32_t window, int32_t num_sinks, int32_t cap,
+                                   int32_t* tok_out, int32_t* slot_out, int32_t* count_out,
+                                   int32_t* dropped_out, int32_t* blk_indptr,
+                                   int32_t* blk_logical, int32_t* blk_page, uint64_t* blk_mask,
+                                   hipStream_t stream);
+int stp_block_view_fill(const int32_t* tok_out, const int32_t* count_out, const int32_t* req_id,
+                        const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                        int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t cap,
+                        int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+                        uint64_t* blk_mask, hipStream_t stream);
+
+/*
  * ---- Stage 2: hot buffer ----------------------------------------------------
  * "HiSparse" walkthrough: overview (SwapIn / BackUp), hot cache
  * initialisation (per-request region of hot_size + 1 rows, 16-byte rows),

@@ -14,7 +14,7 @@ D_QK = 576
 D_V = 512
 
 __all__ = [
-    "StpError", "version", "normalize_indices", "hot_lookup_swapin", "hot_reset", "backup_rows",
+    "StpError", "version", "normalize_indices", "block_view_fill", "hot_lookup_swapin", "hot_reset", "backup_rows",
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
@@ -62,7 +62,7 @@ def host_device_pointer(t):
 
 
 def normalize_indices(topk, req_id, q_pos, block_table, page_size, window, num_sinks, cap=None,
-                      block_view=True, out=None):
+                      block_view=True, out=None, defer_block_view=False):
     """Stage 1.  Returns a dict: tok, slot [T, cap], count, dropped [T] and,
     with block_view, blk_indptr [T+1], blk_logical, blk_page, blk_mask [T*cap]."""
     dev = topk.device
@@ -84,7 +84,8 @@ def normalize_indices(topk, req_id, q_pos, block_table, page_size, window, num_s
             out["blk_page"] = torch.empty((max(1, T * cap),), **i32)
             out["blk_mask"] = torch.empty((max(1, T * cap),), dtype=torch.int64, device=dev)
     bv = "blk_indptr" in out
-    check(lib.stp_normalize_indices(
+    entry = lib.stp_normalize_indices_deferred if defer_block_view else lib.stp_normalize_indices
+    check(entry(
         _dev(topk, "topk", torch.int32, dev), top_k,
         _dev(req_id, "req_id", torch.int32, dev), _dev(q_pos, "q_pos", torch.int32, dev), T,
         _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size,
@@ -98,6 +99,23 @@ def normalize_indices(topk, req_id, q_pos, block_table, page_size, window, num_s
         _dev(out["blk_mask"], "blk_mask", torch.int64, dev) if bv else None,
         _stream(dev)))
     return out
+
+
+def block_view_fill(norm, req_id, q_pos, block_table, page_size):
+    """Complete the block view of normalize_indices(..., defer_block_view=True)
+    on the current stream (norm: the dict that call returned)."""
+    dev = norm["tok"].device
+    T, cap = norm["tok"].shape
+    num_reqs, max_blocks = block_table.shape
+    check(lib.stp_block_view_fill(
+        _dev(norm["tok"], "tok", torch.int32, dev), _dev(norm["count"], "count", torch.int32, dev),
+        _dev(req_id, "req_id", torch.int32, dev), _dev(q_pos, "q_pos", torch.int32, dev), T,
+        _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size, cap,
+        _dev(norm["blk_indptr"], "blk_indptr", torch.int32, dev),
+        _dev(norm["blk_logical"], "blk_logical", torch.int32, dev),
+        _dev(norm["blk_page"], "blk_page", torch.int32, dev),
+        _dev(norm["blk_mask"], "blk_mask", torch.int64, dev), _stream(dev)))
+    return norm
 
 
 def hot_lds_bytes(cap, hot_size):

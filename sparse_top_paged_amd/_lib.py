@@ -27,6 +27,11 @@ SIGNATURES = {
     "stp_normalize_indices": (ctypes.c_int, [
         _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
         _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "stp_normalize_indices_deferred": (ctypes.c_int, [
+        _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+        _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "stp_block_view_fill": (ctypes.c_int, [
+        _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "stp_hot_lookup_swapin": (ctypes.c_int, [
         _p, _i64, _p, _i64, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
     "stp_hot_lds_bytes": (_sz, [_i32, _i32]),

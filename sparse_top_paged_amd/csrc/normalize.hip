@@ -465,16 +465,61 @@ __global__ __launch_bounds__(kFThreads) void block_fill_kernel(FillArgs a) {
   }
 }
 
+// Dynamic LDS above the default limit for every kernel of this file, once.
+int set_lds_attrs() {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)normalize_kernel<true, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<true, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<false, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)normalize_kernel<false, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
+            hipSuccess ||
+        hipFuncSetAttribute((const void*)block_fill_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess ||
+        hipFuncSetAttribute((const void*)block_fill_kernel<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess)
+      return stp::fail(STP_ERR_HIP, "normalize_indices: hipFuncSetAttribute failed");
+    attr_set = true;
+  }
+  return STP_OK;
+}
+
+// The block-view pass of a normalisation whose counts are in blk_indptr.
+int launch_block_fill(const int32_t* tok_out, const int32_t* count_out, const int32_t* req_id,
+                      const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                      int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t cap,
+                      int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+                      uint64_t* blk_mask, hipStream_t stream) {
+  if (num_reqs == 0 || max_blocks == 0) num_reqs = 0;  // every token is a padding row
+  const int nwords = max(1, (int)(((int64_t)max_blocks * page_size + 63) / 64));
+  const size_t bitmap_bytes = (size_t)nwords * sizeof(uint64_t);
+  const bool table_in_lds = bitmap_bytes + (size_t)max_blocks * 4 <= (size_t)kLdsBudget;
+  const uint64_t pdiv = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+  FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,
+              cap, pdiv, nwords, blk_indptr, blk_logical, blk_page, blk_mask};
+  if (table_in_lds)
+    block_fill_kernel<true><<<T, kFThreads, bitmap_bytes + (size_t)max_blocks * 4, stream>>>(fa);
+  else
+    block_fill_kernel<false><<<T, kFThreads, bitmap_bytes, stream>>>(fa);
+  return stp::check_launch("block_fill_kernel");
+}
+
 }  // namespace
 
-extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req_id,
-                                     const int32_t* q_pos, int32_t T,
-                                     const int32_t* block_table, int32_t num_reqs,
-                                     int32_t max_blocks, int32_t page_size, int32_t window,
-                                     int32_t num_sinks, int32_t cap, int32_t* tok_out,
-                                     int32_t* slot_out, int32_t* count_out, int32_t* dropped_out,
-                                     int32_t* blk_indptr, int32_t* blk_logical,
-                                     int32_t* blk_page, uint64_t* blk_mask, hipStream_t stream) {
+static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                          const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                          int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+                          int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out,
+                          int32_t* slot_out, int32_t* count_out, int32_t* dropped_out,
+                          int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+                          uint64_t* blk_mask, hipStream_t stream, bool defer_fill) {
   using stp::fail;
   if (T < 0 || top_k < 0 || num_reqs < 0 || max_blocks < 0 || window < 0 || num_sinks < 0 ||
       cap < 0)
@@ -504,27 +549,7 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
   size_t lds = bitmap_bytes + (table_in_lds ? (size_t)max_blocks * 4 : 0);
   const bool list_in_lds = lds + (size_t)cap * 4 <= (size_t)kLdsBudget;
   if (list_in_lds) lds += (size_t)cap * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)normalize_kernel<true, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
-            hipSuccess ||
-        hipFuncSetAttribute((const void*)normalize_kernel<true, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
-            hipSuccess ||
-        hipFuncSetAttribute((const void*)normalize_kernel<false, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
-            hipSuccess ||
-        hipFuncSetAttribute((const void*)normalize_kernel<false, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) !=
-            hipSuccess ||
-        hipFuncSetAttribute((const void*)block_fill_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess ||
-        hipFuncSetAttribute((const void*)block_fill_kernel<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) != hipSuccess)
-      return fail(STP_ERR_HIP, "normalize_indices: hipFuncSetAttribute failed");
-    attr_set = true;
-  }
+  if (int rc = set_lds_attrs()) return rc;
   const uint64_t pdiv = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
   const int vec_out = cap % 4 == 0 && (uintptr_t)tok_out % 16 == 0 &&
                       (uintptr_t)slot_out % 16 == 0;
@@ -540,14 +565,56 @@ extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const i
   else
     normalize_kernel<false, false><<<T, kNThreads, lds, stream>>>(na);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
-  if (blk_indptr) {
-    FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,
-                cap, pdiv, nwords, blk_indptr, blk_logical, blk_page, blk_mask};
-    if (table_in_lds)
-      block_fill_kernel<true><<<T, kFThreads, bitmap_bytes + (size_t)max_blocks * 4, stream>>>(fa);
-    else
-      block_fill_kernel<false><<<T, kFThreads, bitmap_bytes, stream>>>(fa);
-    if (int rc = stp::check_launch("block_fill_kernel")) return rc;
-  }
+  if (blk_indptr && !defer_fill)
+    return launch_block_fill(tok_out, count_out, req_id, q_pos, T, block_table, num_reqs,
+                             max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
+                             blk_mask, stream);
   return STP_OK;
+}
+
+extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                                     const int32_t* q_pos, int32_t T,
+                                     const int32_t* block_table, int32_t num_reqs,
+                                     int32_t max_blocks, int32_t page_size, int32_t window,
+                                     int32_t num_sinks, int32_t cap, int32_t* tok_out,
+                                     int32_t* slot_out, int32_t* count_out, int32_t* dropped_out,
+                                     int32_t* blk_indptr, int32_t* blk_logical,
+                                     int32_t* blk_page, uint64_t* blk_mask, hipStream_t stream) {
+  return normalize_impl(topk, top_k, req_id, q_pos, T, block_table, num_reqs, max_blocks,
+                        page_size, window, num_sinks, cap, tok_out, slot_out, count_out,
+                        dropped_out, blk_indptr, blk_logical, blk_page, blk_mask, stream, false);
+}
+
+extern "C" int stp_normalize_indices_deferred(
+    const int32_t* topk, int32_t top_k, const int32_t* req_id, const int32_t* q_pos, int32_t T,
+    const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+    int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+    int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr, int32_t* blk_logical,
+    int32_t* blk_page, uint64_t* blk_mask, hipStream_t stream) {
+  return normalize_impl(topk, top_k, req_id, q_pos, T, block_table, num_reqs, max_blocks,
+                        page_size, window, num_sinks, cap, tok_out, slot_out, count_out,
+                        dropped_out, blk_indptr, blk_logical, blk_page, blk_mask, stream, true);
+}
+
+extern "C" int stp_block_view_fill(const int32_t* tok_out, const int32_t* count_out,
+                                   const int32_t* req_id, const int32_t* q_pos, int32_t T,
+                                   const int32_t* block_table, int32_t num_reqs,
+                                   int32_t max_blocks, int32_t page_size, int32_t cap,
+                                   int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+                                   uint64_t* blk_mask, hipStream_t stream) {
+  using stp::fail;
+  if (T < 0 || num_reqs < 0 || max_blocks < 0 || cap < 0)
+    return fail(STP_ERR_INVALID_ARG, "block_view_fill: negative size");
+  if (page_size < 1 || page_size > 64)
+    return fail(STP_ERR_INVALID_ARG, "block_view_fill: page_size %d not in [1, 64]", page_size);
+  if ((int64_t)max_blocks * page_size > kMaxPositions)
+    return fail(STP_ERR_INVALID_ARG, "block_view_fill: max_blocks * page_size too large");
+  if (T == 0) return STP_OK;
+  if (!tok_out || !count_out || !req_id || !q_pos || !blk_indptr || !blk_logical || !blk_page ||
+      !blk_mask || (num_reqs > 0 && max_blocks > 0 && !block_table))
+    return fail(STP_ERR_INVALID_ARG, "block_view_fill: null pointer");
+  if (int rc = set_lds_attrs()) return rc;
+  return launch_block_fill(tok_out, count_out, req_id, q_pos, T, block_table, num_reqs,
+                           max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
+                           blk_mask, stream);
 }

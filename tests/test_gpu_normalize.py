@@ -116,3 +116,41 @@ def test_table_in_global_memory():
     c = workloads.random_small_case(79, T=4, R=2, ctx=300000, top_k=500, window=100, sinks=2,
                                     page_size=1, unmapped_frac=0.01)
     check(c.topk, c.req_id, c.q_pos, c.block_table, c.page_size, c.window, c.num_sinks, c.cap)
+
+
+@pytest.mark.parametrize("case", ["deepseek", "lookback", "global_table", "empty"])
+def test_deferred_block_view_on_side_stream(case):
+    # the normalisation split in two calls, the block view completed on a
+    # second stream: the same arrays as the one-call normalisation
+    import torch
+    import sparse_top_paged_amd as stp
+    if case == "deepseek":
+        c = workloads.deepseek_case()
+    elif case == "lookback":
+        c = workloads.random_small_case(77, T=600, R=5, ctx=900, top_k=60, window=7, sinks=3,
+                                        page_size=16)
+    elif case == "global_table":
+        c = workloads.random_small_case(79, T=4, R=2, ctx=300000, top_k=500, window=100,
+                                        sinks=2, page_size=1, unmapped_frac=0.01)
+    else:
+        c = workloads.random_small_case(80, T=0, R=1, ctx=100, top_k=8, window=2, sinks=1,
+                                        page_size=16)
+    args = [to_dev(np.asarray(a, np.int32)) for a in (c.topk, c.req_id, c.q_pos, c.block_table)]
+    want = stp.normalize_indices(*args, c.page_size, c.window, c.num_sinks, c.cap)
+    torch.cuda.synchronize()
+    want = {k: v.cpu().numpy() for k, v in want.items()}
+    for _ in range(2):
+        got = stp.normalize_indices(*args, c.page_size, c.window, c.num_sinks, c.cap,
+                                    defer_block_view=True)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stp.block_view_fill(got, args[1], args[2], args[3], c.page_size)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in got.items()}
+        for k in KEYS:
+            assert np.array_equal(got[k], want[k]), k
+        nnz = int(want["blk_indptr"][-1])
+        for k in ("blk_logical", "blk_page", "blk_mask"):
+            assert np.array_equal(got[k][:nnz], want[k][:nnz]), k
