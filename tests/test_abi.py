@@ -52,6 +52,20 @@ def test_host_side_validation():
     # cap smaller than top_k + window + sinks
     assert lib.stp_normalize_indices(None, 8, None, None, 1, None, 0, 0, 16, 4, 4, 10, None, None,
                                      None, None, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    # the normalisation split in two: the same checks, before any launch
+    assert lib.stp_normalize_indices_deferred(None, 0, None, None, 1, None, 0, 0, 65, 0, 0, 0,
+                                              None, None, None, None, None, None, None, None,
+                                              None) == STP_ERR_INVALID_ARG
+    assert lib.stp_normalize_indices_deferred(None, 8, None, None, 1, None, 0, 0, 16, 4, 4, 10,
+                                              None, None, None, None, None, None, None, None,
+                                              None) == STP_ERR_INVALID_ARG
+    fill = lib.stp_block_view_fill
+    assert fill(None, None, None, None, -1, None, 0, 0, 16, 4, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    assert fill(None, None, None, None, 1, None, 0, 0, 0, 4, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    assert b"page_size" in lib.stp_last_error()
+    assert fill(None, None, None, None, 1, None, 0, 0, 16, 4, None, None, None, None, None) == STP_ERR_INVALID_ARG
+    assert b"null pointer" in lib.stp_last_error()
+    assert fill(None, None, None, None, 0, None, 0, 0, 16, 4, None, None, None, None, None) == 0
     # 16-byte row rule of the hot buffer (656 passes, 1000 fails)
     assert lib.stp_hot_lookup_swapin(None, 0, None, 1000, None, 0, None, None, None, 16, 17, 0, 0,
                                      None, None, None, None) == STP_ERR_INVALID_ARG
