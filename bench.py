@@ -18,14 +18,16 @@ when it comes round again.
 
 Prints one JSON line.  `value` is query tokens per second over the timed
 steps; `roofline` is the decode kernel's algorithmic bytes per launch over
-its average duration (HIP events on its stream, inside the timed region);
+its average duration, taken from a loop of its own of at least 200 launches
+after the timed steps, each bracketed by HIP events on the kernel's stream;
 `ceilings` times, in the same run, the decode's row gather alone
 (stp_row_gather: the same rows, splits and XCD placement, no arithmetic) and
 a plain device copy, the practical ceilings the decode's rate is set against;
-`cpu_baseline` times the fp64 oracle on a bounded sample on the host.  The
-decode kernel is bracketed by events on every 7th step only: an event pair
-costs a few microseconds of queue time, which would otherwise be counted
-in every step.
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host, on all
+available cores and on one.  Inside the timed steps the decode kernel is
+bracketed by events on every 7th step only (reported beside the roofline
+loop): an event pair costs a few microseconds of queue time, which would
+otherwise be counted in every step.
 """
 
 import argparse
@@ -64,6 +66,8 @@ def parse():
     ap.add_argument("--event-every", type=int, default=7,
                     help="bracket the decode kernel with HIP events on every n-th timed step "
                          "(coprime with --sets, so every candidate set is sampled)")
+    ap.add_argument("--roofline-launches", type=int, default=300,
+                    help="event-bracketed decode launches timed for the roofline (at least 200)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=["deepseek", "hot", "locality", "gqa", "transfer",
                                            "fp8", "plan"],
@@ -115,19 +119,20 @@ def rows_bits(kv, rows):
     return kv[idx].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def cpu_baseline(cases, kv, budget_s):
-    """Time the oracle (normalisation + fp64 attention, all 128 heads) on the
-    batch's query tokens, cycling through them until the budget is spent; the
-    candidate rows are copied to the host first (untimed)."""
-    from threadpoolctl import threadpool_info
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def _oracle_rate(c, rows, host_rows, budget_s):
     import oracle
-
-    c = cases[0]
-    ref = oracle.normalize(c.topk, c.req_id, c.q_pos, c.window, c.num_sinks, c.block_table,
-                           c.page_size, c.cap)
-    rows = [ref["slot"][j, :ref["count"][j]] for j in range(c.T)]
-    host_rows = [rows_bits(kv, r) for r in rows]
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         t = done % c.T
@@ -137,15 +142,48 @@ def cpu_baseline(cases, kv, budget_s):
         oracle.attend_sparse(c.q_bits[t:t + 1], host_rows[t], np.arange(n, dtype=np.int32)[None, :],
                              None, c.scale)
         done += 1
-    el = time.perf_counter() - t0
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(cases, kv, budget_s):
+    """Time the oracle (normalisation + fp64 attention, all 128 heads) on the
+    batch's query tokens, cycling through them until the budget is spent; the
+    candidate rows are copied to the host first (untimed).  Two settings: all
+    the cores this process may use (BLAS at its default thread count), and one
+    core (the calling thread pinned to one CPU, BLAS limited to one thread)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+
+    c = cases[0]
+    ref = oracle.normalize(c.topk, c.req_id, c.q_pos, c.window, c.num_sinks, c.block_table,
+                           c.page_size, c.cap)
+    rows = [ref["slot"][j, :ref["count"][j]] for j in range(c.T)]
+    host_rows = [rows_bits(kv, r) for r in rows]
+    model = cpu_model()
+    avail = sorted(os.sched_getaffinity(0))
+    done, el = _oracle_rate(c, rows, host_rows, budget_s)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    one = {}
+    try:
+        os.sched_setaffinity(0, {avail[0]})
+        with threadpool_limits(limits=1):
+            d1, e1 = _oracle_rate(c, rows, host_rows, budget_s)
+        one = {"value": round(d1 / e1, 2), "unit": "query-tokens/s", "cores": 1,
+               "sample": f"{d1} query-token decodes in {e1:.1f} s, thread pinned to CPU {avail[0]}, "
+                         f"BLAS limited to one thread"}
+    finally:
+        os.sched_setaffinity(0, set(avail))
     return {
         "value": round(done / el, 2),
         "unit": "query-tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done} query-token decodes (the batch's {c.T} tokens cycled), each "
-                  f"normalisation + fp64 attention over all {c.H} heads, {el:.1f} s on the host",
+                  f"normalisation + fp64 attention over all {c.H} heads, {el:.1f} s on the host "
+                  f"({len(avail)} CPUs available, BLAS at {threads} threads)",
+        "cpu_model": model,
+        "one_core": one,
     }
 
 
@@ -243,6 +281,20 @@ def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     us = median_us(lambda k: dst.copy_(src), 20, 1)
     out["device_copy_256MiB"] = {"us": round(us, 3), "gbs": round(2 * COPY_CAL_BYTES / us / 1e3, 1)}
     del src, dst
+    # a plain read of the KV pool (1.2 GB, reduced by torch): what HBM delivers to a
+    # streaming read on this device
+    flat = kv.view(-1)
+    us = median_us(lambda k: flat.sum(dtype=torch.float32), 20, 1)
+    out["device_read_pool"] = {"us": round(us, 3), "gbs": round(flat.numel() * 2 / us / 1e3, 1),
+                               "bytes": flat.numel() * 2, "how": "torch.sum over the bf16 pool"}
+    # the bf16 matrix-core ceiling: a square GEMM through torch (hipBLASLt)
+    n_g = 8192
+    a = torch.randn((n_g, n_g), dtype=torch.bfloat16, device=kv.device)
+    b = torch.randn((n_g, n_g), dtype=torch.bfloat16, device=kv.device)
+    us = median_us(lambda k: torch.matmul(a, b), 20, 1)
+    out["gemm_bf16_8192"] = {"us": round(us, 3), "tflops": round(2 * n_g ** 3 / us / 1e6, 1),
+                             "how": "torch.matmul, bf16, 8192^3"}
+    del a, b
     return out
 
 
@@ -1064,6 +1116,19 @@ def main():
     dec_us = np.asarray([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e3
     merge_us = np.asarray([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e3
 
+    # the roofline's launch duration: a loop of its own, args.roofline_launches
+    # decode launches (the rotated candidate sets), each bracketed by a pair of HIP
+    # events on the stream the kernel runs on, whatever --steps is
+    n_roof = max(200, args.roofline_launches)
+    roof_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                 torch.cuda.Event(enable_timing=True)) for _ in range(n_roof)]
+    torch.cuda.synchronize()
+    for i in range(n_roof):
+        step(args.warmup + args.steps + i, roof_evs[i])
+    torch.cuda.synchronize()
+    roof_us = np.asarray([a.elapsed_time(b) for a, b, _ in roof_evs]) * 1e3
+    roof_merge_us = np.asarray([b.elapsed_time(c) for _, b, c in roof_evs]) * 1e3
+
     ceilings = None if args.no_ceilings else measure_ceilings(stp, kv, norm, args.sets, S,
                                                               (H + 63) // 64)
 
@@ -1071,13 +1136,13 @@ def main():
     q_bytes = T * H * 576 * 2
     o_bytes = T * H * (512 * 2 + 4)
     sel = np.asarray([cnt.sum() for cnt in counts], dtype=np.float64)  # sum of |S_i| per set
-    per_set_steps = np.bincount((args.warmup + np.asarray(sampled)) % args.sets,
-                                minlength=args.sets)
+    roof_idx = args.warmup + args.steps + np.arange(n_roof)
+    per_set_steps = np.bincount(roof_idx % args.sets, minlength=args.sets)
     mean_sel = float((sel * per_set_steps).sum() / per_set_steps.sum())
     kv_bytes = mean_sel * ROW_BYTES
     dec_bytes = kv_bytes + q_bytes + mean_sel * 4 + (o_bytes if S == 1 else 0)
     flops = 2.0 * H * mean_sel * (576 + 512)
-    dec_avg_s = float(dec_us.mean()) * 1e-6
+    dec_avg_s = float(roof_us.mean()) * 1e-6
     step_s = total_ms * 1e-3 / args.steps
     achieved = dec_bytes / dec_avg_s / 1e9
     traffic = load_traffic(dec_bytes)
@@ -1111,8 +1176,18 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(dec_bytes),
-            "avg_launch_us": round(float(dec_us.mean()), 3),
-            "launches_timed": len(sampled),
+            "avg_launch_us": round(float(roof_us.mean()), 3),
+            "median_launch_us": round(float(np.median(roof_us)), 3),
+            "launches_timed": int(n_roof),
+            "timing": "mean over a loop of its own of event-bracketed launches (HIP events on "
+                      "the kernel's stream), after the timed steps",
+            "bytes_counted": "KV rows + queries + candidate ids of one launch (the split path: "
+                             "outputs belong to the merge launch)" if S > 1 else
+                             "KV rows + queries + candidate ids + outputs of one launch",
+            "merge_avg_us": round(float(roof_merge_us.mean()), 3),
+            "call_frac": round((dec_bytes + (o_bytes if S > 1 else 0)) /
+                               ((roof_us.mean() + (roof_merge_us.mean() if S > 1 else 0)) * 1e-6)
+                               / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
@@ -1125,10 +1200,12 @@ def main():
                 round(ceilings["row_gather_each_row_once"]["us"] / (dec_avg_s * 1e6), 4),
         },
         "kernel_us": {
-            "decode_median": round(float(np.median(dec_us)), 3),
-            "decode_p95": round(float(np.percentile(dec_us, 95)), 3),
-            "decode_p99": round(float(np.percentile(dec_us, 99)), 3),
-            "merge_median": round(float(np.median(merge_us)), 3),
+            "decode_median": round(float(np.median(roof_us)), 3),
+            "decode_p95": round(float(np.percentile(roof_us, 95)), 3),
+            "decode_p99": round(float(np.percentile(roof_us, 99)), 3),
+            "merge_median": round(float(np.median(roof_merge_us)), 3),
+            "decode_in_steps_mean": round(float(dec_us.mean()), 3),
+            "decode_in_steps_samples": len(sampled),
         },
         "wall_s_timed": round(t_wall, 4),
     }

@@ -35,7 +35,9 @@ walkthrough (initial state, every intermediate array, final state; stored
 under tests/golden/), the closed form of a cold start on an identity LRU
 order, idempotence of re-applying the same set, and the invariants "LRU stays
 a permutation", "stored ids >= 0 stay distinct", "every resolved entry's hot
-row equals its host row byte for byte".
+row equals its host row byte for byte".  hot_reset: after a multi-step run
+it restores the initial state exactly, a reset row then replays the
+cold-start closed form, and rows left out of a subset keep their state.
 """
 
 import numpy as np
@@ -61,10 +63,16 @@ def hot_reset(state, rows=None):
     """Drop every stale slot of the given rows (all rows when None).
 
     The walkthrough's coordinator relies on a recycled slot's stale state
-    being dropped before reuse (HiSparseCoordinator docstring).
+    being dropped before reuse (HiSparseCoordinator docstring): the row goes
+    back to the initial state (stored id -1 everywhere, identity LRU order).
+    A row index outside the state is data, not an error, and is skipped.
     """
-    rows = range(state.dgi.shape[0]) if rows is None else rows
+    num_rows = state.dgi.shape[0]
+    rows = range(num_rows) if rows is None else rows
     for r in rows:
+        r = int(r)
+        if not 0 <= r < num_rows:
+            continue
         state.dgi[r, :] = -1
         state.lru[r, :] = np.arange(state.hot_size, dtype=np.int16)
 

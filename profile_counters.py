@@ -1,12 +1,12 @@
 """Condense rocprofv3 CSV output into the short text summaries kept beside the
 benchmark (run by path, on any host; it reads CSV files only).
 
-    python sparse_top_paged_amd/profile_counters.py stats <kernel_stats.csv> <out.txt> "<command>"
-    python sparse_top_paged_amd/profile_counters.py traffic <fetch counter_collection.csv> \\
+    python profile_counters.py stats <kernel_stats.csv> <out.txt> "<command>"
+    python profile_counters.py traffic <fetch counter_collection.csv> \\
         <write counter_collection.csv> <kernel source> <out.json> "<command>" [<kernel name>]
-    python sparse_top_paged_amd/profile_counters.py counters <out.txt> "<command>" \\
+    python profile_counters.py counters <out.txt> "<command>" \\
         <counter_collection.csv> [<counter_collection.csv> ...]
-    python sparse_top_paged_amd/profile_counters.py trace <kernel_trace.csv> <out.txt> \\
+    python profile_counters.py trace <kernel_trace.csv> <out.txt> \\
         "<command>" [<kernel substring>@<grid size x> ...]
 
 `trace` reads a kernel trace and reports, per kernel and grid size, the

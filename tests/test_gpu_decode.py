@@ -213,10 +213,12 @@ def test_merge_against_oracle(S):
     assert torch.all(out[2, 3] == 0) and torch.isneginf(lse[2, 3])
 
 
-def _sampled_check(case, kv, out, lse, tokens, where):
-    """Oracle over sampled tokens at full size, from rows copied back from the pool."""
+def _full_check(case, kv, out, lse, tokens, where):
+    """Oracle over the given tokens at full size (every (token, head) element), from rows
+    copied back from the pool."""
     ref = oracle.normalize(case.topk[tokens], case.req_id[tokens], case.q_pos[tokens], case.window,
                            case.num_sinks, case.block_table, case.page_size, case.cap)
+    print(f"[{where}] comparing {len(tokens)} tokens with the oracle", flush=True)
     for j, t in enumerate(tokens):
         n = ref["count"][j]
         rows = ref["slot"][j, :n]
@@ -237,9 +239,8 @@ def test_deepseek_shape_full_size():
                                  block_view=False)
     out, lse = stp.sparse_mla_decode(bf16_dev(c.q_bits), kv, norm["slot"], norm["count"], c.scale)
     torch.cuda.synchronize()
-    _sampled_check(c, kv, out, lse, [0, 13, 31], "deepseek")
-    # every token: finite output, lse finite
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    # every token: the kernel places token t on XCD t % 8 and its split edges vary by token
+    _full_check(c, kv, out, lse, list(range(c.T)), "deepseek")
     del kv
 
 
@@ -255,6 +256,6 @@ def test_long_context_eight_splits(clustered):
     out, lse = stp.sparse_mla_decode(bf16_dev(c.q_bits), kv, norm["slot"], norm["count"], c.scale,
                                      num_splits=8)
     torch.cuda.synchronize()
-    _sampled_check(c, kv, out, lse, [5, 63], "long context")
+    _full_check(c, kv, out, lse, list(range(c.T)), "long context")
     del kv
     torch.cuda.empty_cache()

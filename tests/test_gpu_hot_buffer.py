@@ -138,14 +138,37 @@ def test_missing_host_rows_revoke():
 
 
 def test_reset_subset():
+    # state after real lookups, then a subset reset (with out-of-range row
+    # indices, which are skipped), compared with oracle.hot_reset bit for bit
     import sparse_top_paged_amd as stp
-    dgi = torch.full((4, 8), 7, dtype=torch.int32, device=dev())
-    lru = torch.full((4, 8), 3, dtype=torch.int16, device=dev())
-    stp.hot_reset(dgi, lru, rows=to_dev(np.asarray([1, 3], np.int32)))
+    rng = np.random.default_rng(4)
+    R, H, stride, cap = 5, 64, 128, 40
+    st = oracle.HotState(R, H)
+    host_np = rng.integers(0, 256, size=(3000, 16), dtype=np.uint8)
+    host = pinned_bytes(host_np)
+    hot_np = np.zeros((R * stride, 16), np.uint8)
+    hot = torch.zeros((R * stride, 16), dtype=torch.uint8, device=dev())
+    dgi = to_dev(st.dgi)
+    lru = to_dev(st.lru)
+    for step in range(3):
+        ids = np.full((R, cap), -1, np.int32)
+        for r in range(R):
+            ids[r, :30] = rng.choice(300, size=30, replace=False) + 100 * r
+        newest = np.full(R, -1, np.int32)
+        oracle.hot_lookup_swapin(st, host_np, hot_np, ids, newest, stride, R)
+        stp.hot_lookup_swapin(host, hot, to_dev(ids), to_dev(newest), dgi, lru, stride)
+    rows = np.asarray([1, 3, -2, 9], np.int32)
+    oracle.hot_reset(st, rows=rows)
+    stp.hot_reset(dgi, lru, rows=to_dev(rows))
     torch.cuda.synchronize()
-    d, l = dgi.cpu().numpy(), lru.cpu().numpy()
-    assert np.all(d[[1, 3]] == -1) and np.all(d[[0, 2]] == 7)
-    assert np.all(l[[1, 3]] == np.arange(8)) and np.all(l[[0, 2]] == 3)
+    assert np.array_equal(dgi.cpu().numpy(), st.dgi)
+    assert np.array_equal(lru.cpu().numpy(), st.lru)
+    assert np.any(st.dgi[[0, 2, 4]] >= 0)  # the rows left out still hold their state
+    oracle.hot_reset(st)
+    stp.hot_reset(dgi, lru)
+    torch.cuda.synchronize()
+    assert np.array_equal(dgi.cpu().numpy(), st.dgi)
+    assert np.array_equal(lru.cpu().numpy(), st.lru)
 
 
 def test_backup_skips_out_of_range():

@@ -129,3 +129,64 @@ def test_duplicate_ids_rejected():
     with pytest.raises(AssertionError):
         oracle.hot_lookup_swapin(st, np.zeros((10, 16), np.uint8), np.zeros((16, 16), np.uint8),
                                  np.asarray([[1, 1]], np.int32), np.asarray([-1]), 16, 1)
+
+
+def _run_some_steps(st, c, host, hot, steps):
+    for t in range(steps):
+        res = oracle.normalize(c.topk[t], np.arange(c.batch, dtype=np.int32), c.q_pos(t), c.window,
+                               c.num_sinks, c.block_table, c.page_size, c.cap)
+        oracle.hot_lookup_swapin(st, host, hot, res["slot"], np.full(c.batch, -1, np.int32),
+                                 c.region_stride, c.batch)
+
+
+def test_reset_restores_initial_state():
+    # "HiSparse" walkthrough, HiSparseCoordinator: a recycled request slot's
+    # stale state is dropped before reuse.  The initial state (stored id -1,
+    # identity LRU order) is fixed independently by the cold-start closed form.
+    c = workloads.hot_steps_case(seed=21, batch=4, ctx0=500, steps=4, top_k=24, window=4, sinks=2,
+                                 page_size=16, heads=1)
+    st = oracle.HotState(c.batch, c.hot_size)
+    host = _bytes_pool(c.host_rows, 16, 7)
+    hot = np.zeros((c.batch * c.region_stride, 16), np.uint8)
+    _run_some_steps(st, c, host, hot, c.steps)
+    assert np.any(st.dgi >= 0) and np.any(st.lru != np.arange(c.hot_size))
+    before = st.copy()
+    oracle.hot_reset(st, rows=np.asarray([2, 0], np.int32))
+    for r in (0, 2):
+        assert np.all(st.dgi[r] == -1)
+        assert list(st.lru[r]) == list(range(c.hot_size))
+    for r in (1, 3):  # rows outside the subset keep their state bit for bit
+        assert np.array_equal(st.dgi[r], before.dgi[r])
+        assert np.array_equal(st.lru[r], before.lru[r])
+    oracle.hot_reset(st)
+    fresh = oracle.HotState(c.batch, c.hot_size)
+    assert np.array_equal(st.dgi, fresh.dgi) and np.array_equal(st.lru, fresh.lru)
+
+
+def test_reset_row_replays_cold_start():
+    # after a reset, the next lookup of M distinct ids is the cold-start
+    # closed form: entries take slots 0 .. M-1 in order, LRU = [M..H-1, 0..M-1]
+    H, M = 32, 9
+    st = oracle.HotState(2, H)
+    host = _bytes_pool(400, 16, 8)
+    hot = np.zeros((2 * 64, 16), np.uint8)
+    ids = np.full((2, 12), -1, np.int32)
+    ids[:, :M] = np.arange(200, 200 + M)
+    oracle.hot_lookup_swapin(st, host, hot, ids[:, ::-1].copy(), np.asarray([-1, -1]), 64, 2)
+    ids2 = np.full((2, 12), -1, np.int32)
+    ids2[:, :M] = np.arange(300, 300 + M)
+    oracle.hot_reset(st, rows=[1])
+    out, miss, stats = oracle.hot_lookup_swapin(st, host, hot, ids2, np.asarray([-1, -1]), 64, 2)
+    assert list(out[1, :M]) == [64 + s for s in range(M)]
+    assert list(st.lru[1]) == list(range(M, H)) + list(range(M))
+    assert miss[1, :M].sum() == M
+    # row 0 kept its state: its new misses skip the slots the first call filled
+    assert set(out[0, :M].tolist()).isdisjoint(set(range(M)))
+
+
+def test_reset_skips_rows_outside_state():
+    st = oracle.HotState(2, 8)
+    st.dgi[:] = 5
+    st.lru[:] = 3
+    oracle.hot_reset(st, rows=[-1, 2, 7])
+    assert np.all(st.dgi == 5) and np.all(st.lru == 3)
