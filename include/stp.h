@@ -245,6 +245,27 @@ int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows
                           size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream);
 
 /*
+ * stp_sparse_mla_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * stp_sparse_mla_decode minus (workspace, workspace_bytes); the split
+ * partials live in a scratch array the library holds in device memory, one
+ * copy per GPU, kept until the process ends
+ * (stp_sparse_mla_decode_noalloc_max_bytes() bytes, 36 MiB).  Nothing is
+ * allocated or freed.  A shape whose split path needs more scratch
+ * (stp_sparse_mla_decode_workspace() > the maximum) returns STP_ERR_WORKSPACE
+ * before anything is launched.  The scratch of the current device is used:
+ * call it with the stream's device current.  Every call on a GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (other streams,
+ * other threads) race, so order them on one stream or by events.
+ */
+int stp_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+                                  const int32_t* row_ids, const int32_t* counts, int32_t cap,
+                                  int32_t T, int32_t H, float scale, int32_t num_splits,
+                                  uint16_t* out, float* lse, hipStream_t stream);
+size_t stp_sparse_mla_decode_noalloc_max_bytes(void);
+
+/*
  * Stage 3 over fp8_ds_mla rows ("HiSparse" walkthrough: the 656-byte
  * FP8_DS_MLA row, 512 B quantised latent + 16 B scales + 128 B RoPE;
  * "5.1.1 · 从索引到 Kernel" §7.2: dequantise at tile load).  As

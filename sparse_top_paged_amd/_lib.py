@@ -39,6 +39,9 @@ SIGNATURES = {
     "stp_backup_rows": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _p, _p, _i32, _p]),
     "stp_sparse_mla_decode": (ctypes.c_int, [
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p, _p, _p]),
+    "stp_sparse_mla_decode_noalloc": (ctypes.c_int, [
+        _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p]),
+    "stp_sparse_mla_decode_noalloc_max_bytes": (_sz, []),
     "stp_sparse_mla_decode_fp8": (ctypes.c_int, [
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _sz, _p, _p, _p]),
     "stp_sparse_mla_decode_fp8_splits": (_i32, [_i32, _i32, _i32, _i32]),

@@ -42,6 +42,7 @@
 // the next tile and frees a ring stage.  Invalid candidates load a zero row
 // and are masked to -inf before the exponent.
 
+#include <mutex>
 #include <type_traits>
 
 #include "stp_internal.h"
@@ -900,6 +901,60 @@ extern "C" size_t stp_sparse_mla_decode_workspace(int32_t T, int32_t H, int32_t 
   return align256(n * kDV * 2) + 2 * align256(n * 4);  // bf16 o / l, then m and l
 }
 
+namespace {
+
+// The split path of stp_sparse_mla_decode over a workspace of at least
+// stp_sparse_mla_decode_workspace() bytes: normalised bf16 partial outputs,
+// merged with the partition-combine weights l_s e^(m_s - M) / L.
+int decode_split_path(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
+                      const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T,
+                      int32_t H, float scale, int32_t S, void* workspace, uint16_t* out,
+                      float* lse, hipStream_t stream) {
+  const size_t n = (size_t)T * S * H;
+  char* ws = (char*)workspace;
+  uint16_t* o_norm = (uint16_t*)ws;
+  float* m_part = (float*)(ws + align256(n * kDV * 2));
+  float* l_part = (float*)(ws + align256(n * kDV * 2) + align256(n * 4));
+  if (int rc = launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S,
+                             (float*)o_norm, m_part, l_part, nullptr, nullptr, stream))
+    return rc;
+  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, kDV, out, lse, stream);
+}
+
+// Scratch of stp_sparse_mla_decode_noalloc: the split partials of one call in
+// device memory the library owns (each GPU holds its own copy until the
+// process ends).  Host code never uses the array's name as an address: its
+// device address is looked up once per device (scratch_address) and passed
+// to the kernels like a caller's workspace.
+constexpr size_t kScratchBytes = (size_t)36 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device (with that device current).
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return stp::fail(STP_ERR_HIP, "sparse_mla_decode_noalloc: no current device (or id >= %d)",
+                     kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return stp::fail(STP_ERR_HIP, "sparse_mla_decode_noalloc: hipGetSymbolAddress failed: %s",
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return STP_OK;
+}
+
+}  // namespace
+
 extern "C" int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                                      const int32_t* row_ids, const int32_t* counts, int32_t cap,
                                      int32_t T, int32_t H, float scale, int32_t num_splits,
@@ -917,17 +972,36 @@ extern "C" int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int6
   if (!workspace || workspace_bytes < need)
     return stp::fail(STP_ERR_WORKSPACE, "sparse_mla_decode: workspace of %zu bytes needed, %zu given",
                      need, workspace_bytes);
-  // split path: normalised bf16 partial outputs, merged with the
-  // partition-combine weights l_s e^(m_s - M) / L
-  const size_t n = (size_t)T * S * H;
-  char* ws = (char*)workspace;
-  uint16_t* o_norm = (uint16_t*)ws;
-  float* m_part = (float*)(ws + align256(n * kDV * 2));
-  float* l_part = (float*)(ws + align256(n * kDV * 2) + align256(n * 4));
-  if (int rc = launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S,
-                             (float*)o_norm, m_part, l_part, nullptr, nullptr, stream))
-    return rc;
-  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, kDV, out, lse, stream);
+  return decode_split_path(q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S, workspace, out,
+                           lse, stream);
+}
+
+extern "C" size_t stp_sparse_mla_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int stp_sparse_mla_decode_noalloc(const uint16_t* q, const uint16_t* kv,
+                                             int64_t kv_rows, const int32_t* row_ids,
+                                             const int32_t* counts, int32_t cap, int32_t T,
+                                             int32_t H, float scale, int32_t num_splits,
+                                             uint16_t* out, float* lse, hipStream_t stream) {
+  if (int rc = check_common(q, kv, kv_rows, row_ids, cap, T, H, scale)) return rc;
+  if (num_splits < 0)
+    return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_noalloc: num_splits < 0");
+  if (T == 0) return STP_OK;
+  if (!out) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_noalloc: null out");
+  const int32_t S = choose_splits(T, H, cap, num_splits);
+  if (S == 1)
+    return launch_decode(kOutFinal, q, kv, kv_rows, row_ids, counts, cap, T, H, scale, 1, nullptr,
+                         nullptr, nullptr, out, lse, stream);
+  const size_t need = stp_sparse_mla_decode_workspace(T, H, cap, num_splits);
+  if (need > kScratchBytes)
+    return stp::fail(STP_ERR_WORKSPACE,
+                     "sparse_mla_decode_noalloc: %d splits of T=%d H=%d need %zu bytes of scratch, "
+                     "more than its %zu (ask for fewer splits or split the batch)",
+                     S, T, H, need, kScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  return decode_split_path(q, kv, kv_rows, row_ids, counts, cap, T, H, scale, S, ws, out, lse,
+                           stream);
 }
 
 extern "C" int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* kv,

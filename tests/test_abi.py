@@ -81,6 +81,21 @@ def test_host_side_validation():
                                      fake, None, None) == STP_ERR_WORKSPACE
     assert lib.stp_sparse_mla_decode(fake, fake, 100, fake, None, 64, 1, 16, float("nan"), 1,
                                      None, 0, fake, None, None) == STP_ERR_INVALID_ARG
+    # the no-alloc decode: its scratch holds 36 MiB; a split path that needs more is
+    # rejected before anything is launched, bad arguments as the workspace form
+    noal = lib.stp_sparse_mla_decode_noalloc
+    assert lib.stp_sparse_mla_decode_noalloc_max_bytes() == 36 << 20
+    assert lib.stp_sparse_mla_decode_workspace(64, 128, 16384, 16) > 36 << 20
+    assert noal(fake, fake, 100, fake, None, 16384, 64, 128, 0.04, 16, fake, None,
+                None) == STP_ERR_WORKSPACE
+    assert b"scratch" in lib.stp_last_error()
+    assert noal(fake, fake, 100, fake, None, 64, 1, 16, float("nan"), 1, fake, None,
+                None) == STP_ERR_INVALID_ARG
+    assert noal(fake, fake, 100, fake, None, 64, 1, 16, 0.04, -1, fake, None,
+                None) == STP_ERR_INVALID_ARG
+    assert noal(fake, fake, 100, fake, None, 64, 1, 16, 0.04, 1, None, None,
+                None) == STP_ERR_INVALID_ARG
+    assert noal(fake, fake, 100, fake, None, 64, 0, 16, 0.04, 1, None, None, None) == 0  # T = 0
     assert lib.stp_splitkv_merge(None, None, None, 1, 1, 1, 6, None, None, None) == STP_ERR_INVALID_ARG
     assert stp.decode_splits(32, 128, 2180) >= 1
     assert stp.decode_workspace_bytes(1, 16, 44) == 0          # tiny shape runs unsplit
