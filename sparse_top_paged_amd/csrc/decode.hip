@@ -359,12 +359,22 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   // waves' queue holds the query rows), and handed over with an LDS-only
   // barrier so that nobody waits for the query rows yet
   if (!score) {
+    // every load first, then the stores: one round trip instead of one per
+    // 128 ids
+    constexpr int kPer = (kIdsMax + 127) / 128;
     const int32_t* src_ids = a.row_ids + (int64_t)t * a.cap + lo;
+    int32_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid - 128 + 128 * k;
+      v[k] = i < len ? src_ids[i] : -1;
+    }
     int bad = 0;
-    for (int i = tid - 128; i < ntiles * kTileRows; i += 128) {
-      const int32_t id = i < len ? src_ids[i] : -1;
-      const bool valid = id >= 0 && id < a.kv_rows;
-      L.ids[i] = valid ? id : -1;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid - 128 + 128 * k;
+      const bool valid = v[k] >= 0 && v[k] < a.kv_rows;
+      if (i < ntiles * kTileRows) L.ids[i] = valid ? v[k] : -1;
       bad |= (i < len && !valid) ? 1 : 0;
     }
     const int wbad = __ballot(bad) != 0 ? 1 : 0;
@@ -538,8 +548,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   // the barrier B(i+1) (the score waves read it in iteration i+1).  The 18
   // load instructions of tile i+3 are spread between the MFMAs, one per MFMA
   // pair, so that the wave never stalls on a full load queue.  Past the last
-  // tile the same loads bring zero rows into that free stage, which keeps the
-  // instruction stream and the wait counts the same in every iteration.
+  // tile nothing is loaded (and the wait before the barrier drains the queue).
   for (int i = 1; i <= ntiles; ++i) {
     const int buf = (i - 1) & 1;
     const float a0 = L.alpha[buf * 64 + (lane & 31)];
@@ -558,6 +567,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
     auto load_chunk = [&](auto c) {
       constexpr int kC = decltype(c)::value;
+      if (!real) return;
       if constexpr (kC < kSlotsPerThread)
         load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
       else
@@ -594,10 +604,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     load_chunk(std::integral_constant<int, 17>{});
     if (i == ntiles) break;
     // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
-    wait_vmcnt<2 * kSlotsPerThread>();
+    if (real)
+      wait_vmcnt<2 * kSlotsPerThread>();
+    else
+      wait_vmcnt<0>();
     lds_barrier();  // B(i+1)
   }
-  wait_vmcnt<0>();  // the last (zero-row) loads, before the ring is reused below
+  wait_vmcnt<0>();  // nothing left in flight before the ring is reused below
   lds_barrier();  // statistics published
 
   // lane holds O^T[256 j + 32 mb + 8 (r / 4) + 4 (lane / 32) + r % 4][32 hb + lane % 32]
