@@ -122,7 +122,9 @@ int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req
  * enqueued after it with the same tok_out, count_out, req_id, q_pos,
  * block_table, sizes and block-view arrays, completes the view; until it has
  * run, blk_indptr is not the CSR index.  The pair's results equal one
- * stp_normalize_indices call.  Errors as stp_normalize_indices.
+ * stp_normalize_indices call.  A second fill over arrays it has already
+ * completed changes nothing (tokens whose entry is final are skipped); run
+ * it once per deferred normalisation.  Errors as stp_normalize_indices.
  */
 int stp_normalize_indices_deferred(const int32_t* topk, int32_t top_k, const int32_t* req_id,
                                    const int32_t* q_pos, int32_t T, const int32_t* block_table,

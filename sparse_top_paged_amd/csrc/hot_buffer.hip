@@ -9,14 +9,15 @@
 // "[HiCache] TMA-staged host<->device KV transfer kernel (sm_90+)",
 // Motivation: host-link bandwidth = bytes in flight / round trip.
 //
-// Design for wave64: one 1024-thread workgroup per request row.  Phase 1
-// builds an open-addressing hash (key = global id, value = entry index) in
-// LDS and, when they fit, stages the request's LRU order and stored ids in
-// LDS with the same round trip; phase 2 walks the LRU order in 1024-slot
-// chunks (LDS reads only when staged), and a block-wide scan
-// keeps hits and evictables in walk order (hits from the front of an LDS
-// array, evictables from the back); phase 3 gives misses, in entry order,
-// the evictables from least recent on; phase 4 rewrites the order; phase 5
+// Design for wave64: one 1024-thread workgroup per request row.  The
+// request's candidate ids and, when they fit, its LRU order and stored ids
+// are staged in LDS in one round trip; phase 1 enters the pending entries in
+// an open-addressing table of entry indices (a cell's key is read through the
+// staged candidate list); phase 2 walks the LRU order in 1024-slot chunks
+// (LDS reads only when staged), and a block-wide scan keeps hits and
+// evictables in walk order (hits from the front of an LDS array, evictables
+// from the back); phase 3 lists the misses with a scan in entry order and
+// gives the m-th the m-th evictable; phase 4 rewrites the order; phase 5
 // streams the missing rows from host memory with every thread of the
 // workgroup issuing several independent 16-byte loads before its stores, so
 // that enough bytes are in flight to cover the PCIe round trip.  Order is
@@ -30,33 +31,44 @@ namespace {
 constexpr int kThreads = 256;       // reset and back-up kernels
 constexpr int kSwapThreads = 1024;  // swap-in kernel
 constexpr int kSwapWaves = kSwapThreads / 64;
-constexpr int kEmpty = -1;
 
 __device__ __forceinline__ uint32_t hash_of(int32_t g, int bits) {
   return ((uint32_t)g * 2654435761u) >> (32 - bits);
 }
 
 struct HotLds {
-  int32_t* keys;    // [HS]; after phase 2: global ids of the misses, in miss order
+  int32_t* tab;     // [HS] entry index of a pending id (-1 = empty); after phase 2: miss ids
+  int32_t* cand;    // [cap] the request's candidate ids
   int32_t* dgi;     // [H] staged stored ids (when staged)
-  int16_t* vals;    // [HS]
   int16_t* order;   // [H]: hits at the front, evictables reversed at the back
   int16_t* lru;     // [H] staged LRU order (when staged)
+  int16_t* misses;  // [cap] entry index of the m-th miss
   uint8_t* pend;    // [cap]
 };
 
-// LDS layout: keys, (dgi), vals, order, (lru), pend -- every array aligned to
-// its element size.
-__device__ __forceinline__ HotLds carve(char* smem, int hash_bits, int H, bool staged) {
+// LDS layout: tab, cand, (dgi), order, (lru), misses, pend -- every array
+// aligned to its element size.
+__device__ __forceinline__ HotLds carve(char* smem, int hash_bits, int cap, int H, bool staged) {
   const int HS = 1 << hash_bits;
   HotLds s;
-  s.keys = (int32_t*)smem;
-  s.dgi = s.keys + HS;
-  s.vals = (int16_t*)(s.dgi + (staged ? H : 0));
-  s.order = s.vals + HS;
+  s.tab = (int32_t*)smem;
+  s.cand = s.tab + HS;
+  s.dgi = s.cand + cap;
+  s.order = (int16_t*)(s.dgi + (staged ? H : 0));
   s.lru = s.order + H;
-  s.pend = (uint8_t*)(s.lru + (staged ? H : 0));
+  s.misses = s.lru + (staged ? H : 0);
+  s.pend = (uint8_t*)(s.misses + cap);
   return s;
+}
+
+// Entry index of pending id g in the table, or -1.  The table holds entry
+// indices only; a cell's key is the staged candidate id it points at.
+__device__ __forceinline__ int find_pending(const HotLds& s, int32_t g, int hash_bits, int hmask) {
+  for (uint32_t h = hash_of(g, hash_bits);; h = (h + 1) & hmask) {
+    const int e = s.tab[h];
+    if (e < 0) return -1;
+    if (s.cand[e] == g) return e;
+  }
 }
 
 template <bool kStaged>
@@ -69,6 +81,7 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
     unsigned long long* __restrict__ stats, int hash_bits) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_scan[kSwapWaves];
+  __shared__ int s_bad_order;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* G = global_ids + (int64_t)r * cap;
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
     return;
   }
 
-  const HotLds s = carve(smem, hash_bits, H, kStaged);
+  const HotLds s = carve(smem, hash_bits, cap, H, kStaged);
   const int HS = 1 << hash_bits;
   const int hmask = HS - 1;
   const int64_t base = (int64_t)r * region_stride;
@@ -91,62 +104,50 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
   int32_t* row_dgi = dgi + (int64_t)r * H;
   int16_t* row_lru = lru + (int64_t)r * H;
 
-  for (int k = tid; k < HS; k += kSwapThreads) s.keys[k] = kEmpty;
+  // The request's candidate ids, and (when they fit) its LRU order and stored
+  // ids, all in flight together.
+  for (int k = tid; k < HS; k += kSwapThreads) s.tab[k] = -1;
+  for (int i = tid; i < cap; i += kSwapThreads) s.cand[i] = G[i];
   if (kStaged) {
-    // the LRU order and stored ids, all loads in flight with phase 1's
     for (int p = tid; p < H; p += kSwapThreads) {
       s.lru[p] = row_lru[p];
       s.dgi[p] = row_dgi[p];
     }
   }
+  if (tid == 0) s_bad_order = 0;
   __syncthreads();
 
-  // Phase 1: classify entries; pending ones go into the hash.
+  // Phase 1.  An entry is a padding id (< 0: no row), the request's newest
+  // token (its reserved row base + H), or pending; pending entries are
+  // entered in the table for the walk to find, and their outputs are written
+  // by phase 2 (hits) or phase 3 (misses).
   for (int i = tid; i < cap; i += kSwapThreads) {
-    const int32_t g = G[i];
+    const int32_t g = s.cand[i];
+    const bool pending = g >= 0 && g != newest;
+    if (!pending) row_out[i] = g < 0 ? -1 : (int32_t)(base + H);
     if (row_miss) row_miss[i] = 0;
-    uint8_t p = 0;
-    if (g < 0) {
-      row_out[i] = -1;
-    } else if (g == newest) {
-      row_out[i] = (int32_t)(base + H);
-    } else {
+    s.pend[i] = pending ? 1 : 0;
+    if (pending) {
+      // ids are unique, so an occupied cell holds another id: move on
       uint32_t h = hash_of(g, hash_bits);
-      while (true) {
-        const int32_t old = atomicCAS(&s.keys[h], kEmpty, g);
-        if (old == kEmpty || old == g) {
-          s.vals[h] = (int16_t)i;
-          break;
-        }
-        h = (h + 1) & hmask;
-      }
-      p = 1;
+      while (atomicCAS(&s.tab[h], -1, i) >= 0) h = (h + 1) & hmask;
     }
-    s.pend[i] = p;
   }
   __syncthreads();
 
-  // Phase 2: walk the LRU order, least recent first.
+  // Phase 2: walk the LRU order, least recent first.  Every slot the walk
+  // meets must be a slot of the region (the order is a permutation of
+  // [0, H) as stp_hot_reset and this kernel leave it); if one is not, the
+  // row's state is not ours to read and the row is left untouched.
   int hits = 0, evicts = 0;
   for (int p0 = 0; p0 < H; p0 += kSwapThreads) {
     const int p = p0 + tid;
     const bool in_range = p < H;
-    const int slot = in_range ? (kStaged ? s.lru[p] : row_lru[p]) : -1;
-    const int32_t cached =
-        (slot >= 0 && slot < H) ? (kStaged ? s.dgi[slot] : row_dgi[slot]) : -1;
-    int found = -1;
-    if (cached >= 0) {
-      uint32_t h = hash_of(cached, hash_bits);
-      while (true) {
-        const int32_t k = s.keys[h];
-        if (k == cached) {
-          found = s.vals[h];
-          break;
-        }
-        if (k == kEmpty) break;
-        h = (h + 1) & hmask;
-      }
-    }
+    const int slot = in_range ? (kStaged ? s.lru[p] : row_lru[p]) : 0;
+    const bool slot_ok = slot >= 0 && slot < H;
+    if (in_range && !slot_ok) s_bad_order = 1;
+    const int32_t cached = (in_range && slot_ok) ? (kStaged ? s.dgi[slot] : row_dgi[slot]) : -1;
+    const int found = cached >= 0 ? find_pending(s, cached, hash_bits, hmask) : -1;
     const bool hit = found >= 0;
     const bool evict = in_range && !hit;
     if (hit) {
@@ -162,28 +163,35 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
     evicts += total & 0xffff;
   }
   __syncthreads();
+  if (s_bad_order) {
+    for (int i = tid; i < cap; i += kSwapThreads) {
+      row_out[i] = -1;
+      if (row_miss) row_miss[i] = 0;
+    }
+    return;
+  }
 
-  // Phase 3: misses, in entry order, take evictables from least recent on.
+  // Phase 3: the entries still pending are the misses; the scan lists them
+  // in entry order, and the m-th takes the m-th evictable of the walk (least
+  // recent first).
   int misses = 0;
   for (int i0 = 0; i0 < cap; i0 += kSwapThreads) {
     const int i = i0 + tid;
     const bool miss = i < cap && s.pend[i];
     int total;
     const int pre = stp::block_exclusive_scan<kSwapWaves>(miss ? 1 : 0, s_scan, &total);
-    if (miss) {
-      const int m = misses + pre;
-      const int slot = s.order[H - 1 - m];
-      const int32_t g = G[i];
-      s.keys[m] = g;  // the hash is no longer needed: reuse it as the miss list
-      if (slot < 0 || slot >= H) {  // only reachable from a corrupted LRU state
-        row_out[i] = -1;
-      } else {
-        row_out[i] = (int32_t)(base + slot);
-        if (row_miss) row_miss[i] = 1;
-        row_dgi[slot] = g;
-      }
-    }
+    if (miss) s.misses[misses + pre] = (int16_t)i;
     misses += total;
+  }
+  __syncthreads();
+  for (int m = tid; m < misses; m += kSwapThreads) {
+    const int i = s.misses[m];
+    const int slot = s.order[H - 1 - m];
+    const int32_t g = s.cand[i];
+    s.tab[m] = g;  // the table is no longer needed: the copy's source ids
+    row_out[i] = (int32_t)(base + slot);
+    if (row_miss) row_miss[i] = 1;
+    row_dgi[slot] = g;
   }
   __syncthreads();
 
@@ -217,12 +225,9 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
       if (k < total_vec) {
         const int m = (int)(k / nvec);
         const int64_t e = k - (int64_t)m * nvec;
-        const int32_t g = s.keys[m];
-        const int slot = s.order[H - 1 - m];
-        if (slot >= 0 && slot < H) {
-          dst[u] = (base + slot) * nvec + e;
-          v[u] = (g < host_rows) ? host4[(int64_t)g * nvec + e] : zero;
-        }
+        const int32_t g = s.tab[m];
+        dst[u] = (base + s.order[H - 1 - m]) * nvec + e;
+        v[u] = (g < host_rows) ? host4[(int64_t)g * nvec + e] : zero;
       }
     }
 #pragma unroll
@@ -230,10 +235,8 @@ __global__ __launch_bounds__(kSwapThreads) void hot_swapin_kernel(
       if (dst[u] >= 0) hot4[dst[u]] = v[u];
   }
   __syncthreads();
-  for (int m = tid; m < misses; m += kSwapThreads) {
-    const int slot = s.order[H - 1 - m];
-    if (s.keys[m] >= host_rows && slot >= 0 && slot < H) row_dgi[slot] = -1;  // ownership revoked
-  }
+  for (int m = tid; m < misses; m += kSwapThreads)
+    if (s.tab[m] >= host_rows) row_dgi[s.order[H - 1 - m]] = -1;  // ownership revoked
   if (tid == 0 && stats) {
     atomicAdd(&stats[0], (unsigned long long)hits);
     atomicAdd(&stats[1], (unsigned long long)misses);
@@ -273,7 +276,7 @@ int hash_bits_for(int cap) {
 
 size_t lds_bytes_for(int cap, int H, bool staged = false) {
   const int HS = 1 << hash_bits_for(cap);
-  return (size_t)HS * 4 + (size_t)HS * 2 + (size_t)H * 2 + (size_t)cap +
+  return (size_t)HS * 4 + (size_t)cap * 4 + (size_t)H * 2 + (size_t)cap * 2 + (size_t)cap +
          (staged ? (size_t)H * 6 : 0);
 }
 

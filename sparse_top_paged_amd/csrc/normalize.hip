@@ -356,7 +356,12 @@ __global__ __launch_bounds__(kFThreads) void block_fill_kernel(FillArgs a) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
 
-  const int own = -a.blk_indptr[i + 1] - 1;  // written as -(count + 1); only this WG rewrites it
+  // written as -(count + 1) by the normalisation; only this workgroup turns it
+  // into the inclusive prefix, so a value >= 0 means this token's view is
+  // already complete (a repeated fill over the same arrays): nothing to do
+  const int raw = a.blk_indptr[i + 1];
+  if (raw >= 0) return;
+  const int own = -raw - 1;
   const int n = a.count_out[i];
   const int r = a.req_id[i];
   const int q = a.q_pos[i];

@@ -43,13 +43,15 @@ def test_worked_example(golden):
 
 
 def _run_steps(batch, steps, top_k, window, sinks, P, ctx0, num_real=None, row_bytes=1152,
-               trim_host=0):
+               trim_host=0, hot_size=None):
     """Decode steps through normalise -> lookup/swap-in -> back-up on both sides."""
     import sparse_top_paged_amd as stp
     c = workloads.hot_steps_case(seed=3000 + batch, batch=batch, ctx0=ctx0, steps=steps,
                                  top_k=top_k, window=window, sinks=sinks, page_size=P, heads=1)
     num_real = batch if num_real is None else num_real
     H, stride = c.hot_size, c.region_stride
+    if hot_size is not None:
+        H, stride = hot_size, -(-(hot_size + 1) // 128) * 128
     rng = np.random.default_rng(1)
     host_rows = c.host_rows - trim_host
     host_np = rng.integers(0, 256, size=(host_rows, row_bytes), dtype=np.uint8)
@@ -122,14 +124,52 @@ def test_multistep_fp8_rows():
 
 
 def test_multistep_unstaged_state():
-    # hot_size 8192: the LRU order and stored ids no longer fit in LDS beside
-    # the hash, so the lookup reads them from global memory
+    # hot_size 12288 at top-k 4096: the LRU order and stored ids no longer fit
+    # in LDS beside the table and the staged candidates, so the lookup reads
+    # them from global memory
     import sparse_top_paged_amd as stp
-    H, cap = 8192, 4096 + 8 + 2
-    from sparse_top_paged_amd._lib import lib
+    H, cap = 12288, 4096 + 8 + 2
     assert stp.hot_lds_bytes(cap, H) > 0
-    s = _run_steps(batch=2, steps=3, top_k=4096, window=8, sinks=2, P=64, ctx0=20000)
+    assert stp.hot_lds_bytes(cap, H) + 6 * H > 160 * 1024
+    s = _run_steps(batch=2, steps=3, top_k=4096, window=8, sinks=2, P=64, ctx0=20000,
+                   hot_size=H)
     assert s[0] > 0 and s[1] > 0
+
+
+def test_out_of_range_lru_leaves_row_untouched():
+    # an LRU order holding a slot outside the region is not state this kernel
+    # left: that row's outputs are -1 and its state is not touched; the other
+    # rows follow the oracle
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(9)
+    R, H, stride, cap = 3, 64, 128, 20
+    st = oracle.HotState(R, H)
+    host_np = rng.integers(0, 256, size=(500, 16), dtype=np.uint8)
+    host = pinned_bytes(host_np)
+    hot_np = np.zeros((R * stride, 16), np.uint8)
+    hot = torch.zeros((R * stride, 16), dtype=torch.uint8, device=dev())
+    lru_bad = st.lru.copy()
+    lru_bad[1, 5] = 999
+    dgi = to_dev(st.dgi)
+    lru = to_dev(lru_bad)
+    ids = np.stack([rng.choice(400, size=cap, replace=False) for _ in range(R)]).astype(np.int32)
+    newest = np.full(R, -1, np.int32)
+    out, miss, stats = stp.hot_lookup_swapin(host, hot, to_dev(ids), to_dev(newest), dgi, lru,
+                                             stride)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[1] == -1) and np.all(miss.cpu().numpy()[1] == 0)
+    assert np.array_equal(lru.cpu().numpy()[1], lru_bad[1])
+    assert np.all(dgi.cpu().numpy()[1] == -1)
+    assert np.all(hot.cpu().numpy()[stride:2 * stride] == 0)
+    rows = [0, 2]
+    sub = oracle.HotState(2, H)
+    out_ref, miss_ref, s_ref = oracle.hot_lookup_swapin(sub, host_np, hot_np[:2 * stride].copy(),
+                                                        ids[rows], newest[rows], stride, 2)
+    for k, r in enumerate(rows):
+        assert np.array_equal(o[r] - (r - k) * stride * (o[r] >= 0), out_ref[k])
+        assert np.array_equal(dgi.cpu().numpy()[r], sub.dgi[k])
+    assert stats.cpu().tolist() == s_ref.tolist()
 
 
 def test_missing_host_rows_revoke():

@@ -146,6 +146,8 @@ def test_deferred_block_view_on_side_stream(case):
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             stp.block_view_fill(got, args[1], args[2], args[3], c.page_size)
+            # a repeated fill over the completed arrays changes nothing
+            stp.block_view_fill(got, args[1], args[2], args[3], c.page_size)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         got = {k: v.cpu().numpy() for k, v in got.items()}
