@@ -19,7 +19,8 @@ when it comes round again.
 Prints one JSON line.  `value` is query tokens per second over the timed
 steps; `roofline` is the decode kernel's algorithmic bytes per launch over
 its average duration, taken from a loop of its own of at least 200 launches
-after the timed steps, each bracketed by HIP events on the kernel's stream;
+after the timed steps, enqueued back to back between two HIP events on the
+kernel's stream;
 `ceilings` times, in the same run, the decode's row gather alone
 (stp_row_gather: the same rows, splits and XCD placement, no arithmetic) and
 a plain device copy, the practical ceilings the decode's rate is set against;
@@ -281,12 +282,13 @@ def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     us = median_us(lambda k: dst.copy_(src), 20, 1)
     out["device_copy_256MiB"] = {"us": round(us, 3), "gbs": round(2 * COPY_CAL_BYTES / us / 1e3, 1)}
     del src, dst
-    # a plain read of the KV pool (1.2 GB, reduced by torch): what HBM delivers to a
-    # streaming read on this device
-    flat = kv.view(-1)
-    us = median_us(lambda k: flat.sum(dtype=torch.float32), 20, 1)
-    out["device_read_pool"] = {"us": round(us, 3), "gbs": round(flat.numel() * 2 / us / 1e3, 1),
-                               "bytes": flat.numel() * 2, "how": "torch.sum over the bf16 pool"}
+    # a plain sequential read of the KV pool (1.2 GB, stp_stream_read): what HBM
+    # delivers to a streaming read on this device
+    cs_read = torch.empty((2048,), dtype=torch.int32, device=kv.device)
+    us = median_us(lambda k: stp.stream_read(kv, 2048, checksum=cs_read), 20, 1)
+    nbytes = kv.numel() * kv.element_size()
+    out["device_read_pool"] = {"us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
+                               "bytes": nbytes, "how": "stp_stream_read over the bf16 pool"}
     # the bf16 matrix-core ceiling: a square GEMM through torch (hipBLASLt)
     n_g = 8192
     a = torch.randn((n_g, n_g), dtype=torch.bfloat16, device=kv.device)
@@ -1185,10 +1187,27 @@ def main():
     dec_us = np.asarray([evs[i][0].elapsed_time(evs[i][1]) for i in sampled]) * 1e3
     merge_us = np.asarray([evs[i][1].elapsed_time(evs[i][2]) for i in sampled]) * 1e3
 
-    # the roofline's launch duration: a loop of its own, args.roofline_launches
-    # decode launches (the rotated candidate sets), each bracketed by a pair of HIP
-    # events on the stream the kernel runs on, whatever --steps is
+    # The roofline's launch duration, in a loop of its own whatever --steps is:
+    # args.roofline_launches decode launches (the rotated candidate sets, their
+    # normalisation done beforehand) enqueued back to back between two HIP
+    # events on the kernel's stream, the mean per launch; the same for the
+    # merge.  A pair of events around every single launch also counts the
+    # dispatch (about 2 us here); that per-launch mean is reported beside it.
     n_roof = max(200, args.roofline_launches)
+
+    def dec_only(k):
+        nb = norm[k % args.sets]
+        if S > 1:
+            stp.sparse_mla_decode_partial_normalized(q, kv, nb["slot"], nb["count"], c0.scale, S,
+                                                     o_norm, m_part, l_part)
+        else:
+            stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
+
+    def merge_only(k):
+        stp.splitkv_merge_normalized(o_norm, m_part, l_part, out, lse)
+
+    roof_avg_us = throughput_us(dec_only, n_roof, args.sets)
+    merge_avg_us = throughput_us(merge_only, n_roof, args.sets) if S > 1 else 0.0
     roof_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                  torch.cuda.Event(enable_timing=True)) for _ in range(n_roof)]
     torch.cuda.synchronize()
@@ -1211,7 +1230,7 @@ def main():
     kv_bytes = mean_sel * ROW_BYTES
     dec_bytes = kv_bytes + q_bytes + mean_sel * 4 + (o_bytes if S == 1 else 0)
     flops = 2.0 * H * mean_sel * (576 + 512)
-    dec_avg_s = float(roof_us.mean()) * 1e-6
+    dec_avg_s = roof_avg_us * 1e-6
     step_s = total_ms * 1e-3 / args.steps
     achieved = dec_bytes / dec_avg_s / 1e9
     traffic = load_traffic(dec_bytes)
@@ -1245,18 +1264,18 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(dec_bytes),
-            "avg_launch_us": round(float(roof_us.mean()), 3),
-            "median_launch_us": round(float(np.median(roof_us)), 3),
+            "avg_launch_us": round(roof_avg_us, 3),
             "launches_timed": int(n_roof),
-            "timing": "mean over a loop of its own of event-bracketed launches (HIP events on "
-                      "the kernel's stream), after the timed steps",
+            "timing": "mean over a loop of its own of launches enqueued back to back between "
+                      "two HIP events on the kernel's stream, after the timed steps",
+            "event_pair_mean_us": round(float(roof_us.mean()), 3),
+            "event_pair_median_us": round(float(np.median(roof_us)), 3),
             "bytes_counted": "KV rows + queries + candidate ids of one launch (the split path: "
                              "outputs belong to the merge launch)" if S > 1 else
                              "KV rows + queries + candidate ids + outputs of one launch",
-            "merge_avg_us": round(float(roof_merge_us.mean()), 3),
+            "merge_avg_us": round(merge_avg_us, 3),
             "call_frac": round((dec_bytes + (o_bytes if S > 1 else 0)) /
-                               ((roof_us.mean() + (roof_merge_us.mean() if S > 1 else 0)) * 1e-6)
-                               / 1e9 / HBM_PEAK_GBS, 4),
+                               ((roof_avg_us + merge_avg_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),

@@ -436,6 +436,18 @@ int stp_row_gather(const void* rows, int64_t num_rows, int64_t row_bytes, const 
 int32_t stp_row_gather_blocks(int32_t T, int32_t parts, int32_t replicas);
 
 /*
+ * Diagnostic: what HBM delivers to a plain sequential read on this device
+ * ("5.1.1 · 从索引到 Kernel" §6.1: rates against what the hardware sustains).
+ * Reads bytes (a multiple of 16) from src with `blocks` workgroups of 256
+ * threads, grid-stride over 16-byte units (unit u is read by thread u mod
+ * (256 blocks) of the grid), and writes the xor of the 32-bit words each
+ * workgroup read to checksum[blocks].  Errors: bytes not a multiple of 16,
+ * blocks < 1, null pointers -> STP_ERR_INVALID_ARG.
+ */
+int stp_stream_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* checksum,
+                    hipStream_t stream);
+
+/*
  * ---- Dense paged attention with grouped query heads -------------------------
  * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" §1.1 (decode
  * attention), §1.2 (block table), §1.4 part 4 (grouped query heads: the grid

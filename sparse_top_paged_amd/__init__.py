@@ -18,6 +18,7 @@ __all__ = [
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
+    "stream_read",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
     "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
     "decode_fp8_workspace_bytes", "decode_plan", "decode_run", "decode_plan_bytes",
@@ -315,6 +316,20 @@ def row_gather(rows, row_ids, counts=None, parts=1, replicas=1, checksum=None):
         rows.data_ptr(), rows.shape[0], row_bytes, _dev(row_ids, "row_ids", torch.int32, dev),
         _opt(counts, "counts", torch.int32, dev), cap, T, parts, replicas,
         _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
+    return checksum
+
+
+def stream_read(src, blocks=2048, checksum=None):
+    """Diagnostic: a plain sequential read of a contiguous device tensor (its
+    bytes, a multiple of 16) with `blocks` workgroups; returns the per-workgroup
+    xor checksums (as int32)."""
+    dev = src.device
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    if checksum is None:
+        checksum = torch.empty((blocks,), dtype=torch.int32, device=dev)
+    check(lib.stp_stream_read(src.data_ptr(), src.numel() * src.element_size(), blocks,
+                              _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
     return checksum
 
 

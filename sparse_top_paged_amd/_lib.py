@@ -62,6 +62,7 @@ SIGNATURES = {
     "stp_splitkv_merge_normalized": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "stp_row_gather": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
     "stp_row_gather_blocks": (_i32, [_i32, _i32, _i32]),
+    "stp_stream_read": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
     "stp_paged_gqa_decode": (ctypes.c_int, [
         _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz,
         _p, _p, _p]),

@@ -33,11 +33,14 @@ def expected(rows_u32, ids, counts, parts, replicas, blocks, T):
     return out
 
 
+@pytest.mark.parametrize("row_bytes", [1152, 256, 656, 4096])
 @pytest.mark.parametrize("parts,replicas", [(1, 1), (3, 2), (8, 1), (4, 2)])
-def test_row_gather_checksums(parts, replicas):
+def test_row_gather_checksums(parts, replicas, row_bytes):
+    # 1152 / 256 / 656-byte rows take the LDS ring (9 / 2 / 6 lines, the last
+    # one partial for 656), 4096-byte rows the register pipeline
     import sparse_top_paged_amd as stp
-    rng = np.random.default_rng(11 + parts * 10 + replicas)
-    num_rows, row_bytes, T, cap = 700, 1152, 11, 90
+    rng = np.random.default_rng(11 + parts * 10 + replicas + row_bytes)
+    num_rows, T, cap = 700, 11, 90
     rows = rng.integers(0, 256, size=(num_rows, row_bytes), dtype=np.uint8)
     ids = rng.integers(-1, num_rows + 20, size=(T, cap)).astype(np.int32)
     counts = rng.integers(0, cap + 1, size=T).astype(np.int32)
@@ -52,3 +55,20 @@ def test_row_gather_checksums(parts, replicas):
             assert got[bid] == exp[bid], f"block {bid}"
         else:
             assert got[bid] == 0x5A5A5A5A, f"block {bid} past the last token was written"
+
+
+@pytest.mark.parametrize("n16,blocks", [(1, 1), (1000, 3), (4096 * 5 + 17, 4), (300000, 64)])
+def test_stream_read_checksums(n16, blocks):
+    # unit u is read by thread u mod (256 blocks): workgroup b folds the units
+    # whose residue lies in [256 b, 256 b + 256)
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(n16 + blocks)
+    words = rng.integers(0, 2 ** 32, size=(n16, 4), dtype=np.uint64).astype(np.uint32)
+    src = to_dev(words.view(np.int32))
+    got = stp.stream_read(src, blocks).cpu().numpy().view(np.uint32)
+    unit_xor = np.bitwise_xor.reduce(words, axis=1)
+    owner = (np.arange(n16) % (256 * blocks)) // 256
+    for b in range(blocks):
+        sel = unit_xor[owner == b]
+        exp = np.bitwise_xor.reduce(sel) if len(sel) else np.uint32(0)
+        assert got[b] == exp, f"block {b}"
