@@ -171,11 +171,15 @@ def test_partial_states_normalized(splits):
     assert_attention_close(out, lse, o_ref, l_ref, f"normalized partial+merge splits={splits}")
 
 
-@pytest.mark.parametrize("S", [1, 2, 8, 33])
-def test_merge_normalized_against_oracle(S):
+@pytest.mark.parametrize("S,dv", [(1, 512), (2, 512), (8, 512), (33, 512), (3, 36), (5, 1024),
+                                  (4, 8)])
+def test_merge_normalized_against_oracle(S, dv):
+    # dv % 8 == 0 with S <= 8: 16-byte slices, four heads per workgroup
+    # (dv 1024: two slices per thread; dv 8: one thread per head); dv 36 and
+    # S 33: two heads per workgroup, 8-byte slices
     import sparse_top_paged_amd as stp
-    rng = np.random.default_rng(100 + S)
-    T, H, dv = 3, 20, 512
+    rng = np.random.default_rng(100 + S + dv)
+    T, H = 3, 20
     m = (rng.standard_normal((T, S, H)) * 4).astype(np.float32)
     l = rng.uniform(0.5, 30, size=(T, S, H)).astype(np.float32)
     on_bits = workloads.normal_bf16(rng, (T, S, H, dv))
@@ -189,7 +193,7 @@ def test_merge_normalized_against_oracle(S):
     torch.cuda.synchronize()
     on = oracle.bf16_bits_to_f64(on_bits)
     o_ref, l_ref = oracle.merge_normalized(on, m.astype(np.float64), l.astype(np.float64))
-    assert_attention_close(out, lse, o_ref, l_ref, f"merge normalized S={S}")
+    assert_attention_close(out, lse, o_ref, l_ref, f"merge normalized S={S} dv={dv}")
     assert torch.all(out[2, 3] == 0) and torch.isneginf(lse[2, 3])
 
 
