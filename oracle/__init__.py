@@ -38,7 +38,7 @@ from .attention import (
 from .merge import merge, merge_normalized
 from .dense import decode_slots, extend_attention, extend_metadata, paged_gqa_decode
 from .transfer import kv_transfer
-from .fp8 import attend_sparse_fp8, dequant_rows, e4m3_to_f64
+from .fp8 import attend_sparse_fp8, dequant_rows, e4m3_to_f64, f32_to_bf16, reconstruct
 from .plan import plan_tasks, run_tasks
 
 __all__ = [
@@ -47,7 +47,7 @@ __all__ = [
     "bf16_bits_to_f64", "attend_sparse", "attend_partial", "attend_dense_masked",
     "attend_fsum", "shifted_causal_mask", "split_ranges",
     "merge", "merge_normalized", "kv_transfer",
-    "attend_sparse_fp8", "dequant_rows", "e4m3_to_f64",
+    "attend_sparse_fp8", "dequant_rows", "e4m3_to_f64", "f32_to_bf16", "reconstruct",
     "decode_slots", "extend_attention", "extend_metadata", "paged_gqa_decode",
     "plan_tasks", "run_tasks",
 ]

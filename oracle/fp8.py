@@ -8,8 +8,8 @@ shape and the FP8_DS_MLA_ROW_BYTES constant with its comment; "5.1.1 Â· ä»Žç´¢å¼
 QK / AV): a 656-byte row holds 512 bytes of quantised latent (NoPE) values,
 16 bytes of scales and 128 bytes of RoPE values.  Read here as:
   * bytes 0..511: 512 FP8 E4M3 codes (the OCP "fn" variant: bias 7, no
-    infinities, S.1111.111 is NaN), latent value i = e4m3(code_i) *
-    scale_{i // 128};
+    infinities, S.1111.111 is NaN), latent value i reconstructed from code_i
+    and scale_{i // 128};
   * bytes 512..527: the four scales, float32 little-endian, one per 128
     latent values;
   * bytes 528..655: the 64 RoPE values, bf16 little-endian.
@@ -17,11 +17,23 @@ The dequantised row is the 576-value key (latent then RoPE) and its first
 512 values are the value vector, as for the bf16 rows of the same cache.
 Attention over such rows is attend_sparse over the dequantised rows.
 
+Reconstruction.  Â§7.2 has the scale applied as soon as the tile is loaded,
+the reconstructed values then feeding QK and AV, and the correctness
+baseline computing with the same reconstructed KV, so that the kernel's own
+error is seen apart from the quantisation error.  The page fixes no type for
+the reconstructed values; the reading taken is the type the products take
+in the rest of the path, bf16: value = bf16(f32(e4m3(code)) * f32(scale)),
+the product rounded to float32 and then to bf16, both to nearest, ties to
+even.  dequant_rows(rows, exact=True) gives the exact fp64 product instead
+(the quantisation error's reference).
+
 Pins (tests/test_oracle_fp8.py): the decoder against torch's float8_e4m3fn
 for all 256 codes, and its printed special values (1, 448, 2^-6, 2^-9, -0,
 NaN); the byte layout 512 + 16 + 128 = 656 of the page; a hand-built row
-dequantised by hand; attention over fp8 rows whose dequantised values are
-exact in bf16 equals the pinned bf16 attention over those values.
+dequantised by hand; the reconstruction's rounding on hand-worked cases
+(ties to even both ways, 0.37, overflow to infinity) and its error bound
+against the exact product; attention over fp8 rows whose dequantised values
+are exact in bf16 equals the pinned bf16 attention over those values.
 """
 
 import numpy as np
@@ -47,12 +59,34 @@ def e4m3_to_f64(codes):
     return sign * mag
 
 
-def dequant_rows(rows):
-    """[n, 656] uint8 rows -> [n, 576] float64 keys (latent, then RoPE)."""
+def f32_to_bf16(x):
+    """float32 values -> the nearest bf16 values (ties to even), as float64.
+    NaN stays NaN; values past the largest bf16 round to infinity."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    upper = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+    r = (upper.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(x), np.nan, r)
+
+
+def reconstruct(codes, scales):
+    """bf16(f32(e4m3(code)) * f32(scale)), broadcasting codes against scales."""
+    with np.errstate(over="ignore"):  # a product past float32's range is infinite
+        prod = e4m3_to_f64(codes).astype(np.float32) * np.asarray(scales, dtype=np.float32)
+    return f32_to_bf16(prod)
+
+
+def dequant_rows(rows, exact=False):
+    """[n, 656] uint8 rows -> [n, 576] float64 keys (latent, then RoPE); the
+    latent values reconstructed in bf16 (exact=True: the exact products)."""
     rows = np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1, ROW_BYTES)
     n = rows.shape[0]
-    scales = rows[:, SCALE_OFF:ROPE_OFF].copy().view("<f4").astype(np.float64)  # [n, 4]
-    latent = e4m3_to_f64(rows[:, :NOPE]).reshape(n, NOPE // GROUP, GROUP) * scales[:, :, None]
+    scales = rows[:, SCALE_OFF:ROPE_OFF].copy().view("<f4")  # [n, 4] float32
+    codes = rows[:, :NOPE].reshape(n, NOPE // GROUP, GROUP)
+    if exact:
+        latent = e4m3_to_f64(codes) * scales.astype(np.float64)[:, :, None]
+    else:
+        latent = reconstruct(codes, scales[:, :, None])
     rope = bf16_bits_to_f64(rows[:, ROPE_OFF:].copy().view("<u2"))
     return np.concatenate([latent.reshape(n, NOPE), rope], axis=1)
 

@@ -2,8 +2,10 @@
 
 The E4M3 decoder against torch's float8_e4m3fn for all 256 codes and its
 special values; the 512 + 16 + 128 = 656 byte layout of the HiSparse page; a
-hand-built row dequantised by hand; attention over fp8 rows whose values are
-exact in bf16 equals the pinned bf16 attention over the same values.
+hand-built row dequantised by hand; the bf16 reconstruction of the latent
+values on hand-worked roundings and against the exact product's error bound;
+attention over fp8 rows whose values are exact in bf16 equals the pinned bf16
+attention over the same values.
 """
 
 import math
@@ -68,3 +70,37 @@ def test_attention_reduces_to_bf16_attention():
     o8, l8 = oracle.attend_sparse_fp8(q, rows, ids, counts, 576 ** -0.5)
     ob, lb = oracle.attend_sparse(q, kv_bits, ids, counts, 576 ** -0.5)
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
+def test_reconstruction_rounds_to_nearest_even():
+    """bf16(f32(code) * f32(scale)) on cases worked by hand: bf16 keeps 8
+    significant bits, so 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (even:
+    1), 1 + 3 2^-8 halfway between 1 + 2^-7 and 1 + 2^-6 (even: 1 + 2^-6);
+    0.37 = 1.0111101 0111... x 2^-2 rounds down to 1.0111101 x 2^-2; 448 x
+    2^120 is past float32's range."""
+    r = oracle.reconstruct
+    one, c448, c_m2 = 0x38, 0x7E, 0xC0                   # 1.0, 448, -2
+    assert r([one], [1.0 + 2.0 ** -8])[0] == 1.0
+    assert r([one], [1.0 + 3 * 2.0 ** -8])[0] == 1.0 + 2.0 ** -6
+    assert r([one], [1.0 + 5 * 2.0 ** -9])[0] == 1.0 + 2.0 ** -7   # above half: up
+    assert r([one], [0.37])[0] == 0.369140625
+    assert r([c_m2], [0.37])[0] == -0.73828125
+    assert r([c448], [2.0 ** -20])[0] == 448.0 * 2.0 ** -20       # powers of two: exact
+    assert np.isposinf(r([c448], [2.0 ** 120])[0])
+    assert np.isnan(r([0x7F], [1.0])[0])
+    k = oracle.dequant_rows(np.zeros((1, 656), np.uint8))[0]
+    assert not np.any(k) and np.count_nonzero(np.signbit(k)) == 0
+
+
+def test_reconstruction_error_bound():
+    """|bf16(f32(x s)) - x s| <= 2^-8 |x s| (half a bf16 ulp, 2^-9 relative,
+    after a float32 rounding of 2^-24): the reconstruction stays within the
+    bound of the exact product over random codes and scales."""
+    rng = np.random.default_rng(9)
+    rows = workloads.fp8_rows(rng, 64)
+    exact = oracle.dequant_rows(rows, exact=True)
+    rec = oracle.dequant_rows(rows)
+    ok = np.isfinite(exact)
+    assert np.all(np.abs(rec[ok] - exact[ok]) <= 2.0 ** -8 * np.abs(exact[ok]))
+    assert np.array_equal(rec[:, 512:], exact[:, 512:])           # RoPE values as stored
+    assert np.count_nonzero(rec[ok] != exact[ok]) > 0              # arbitrary scales do round
