@@ -53,7 +53,7 @@ FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_decode_traffic.json")
 DENSE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "dense.hip")
 COPY_CAL_BYTES = 256 << 20
 DECODE_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode.hip")
-FP8_SRC = os.path.join(ROOT, "sparse_top_paged_amd", "csrc", "decode_fp8.hip")
+FP8_SRC = DECODE_SRC
 
 
 def parse():
@@ -797,10 +797,10 @@ def bench_fp8(args):
     """The DeepSeek-shaped step over fp8_ds_mla rows: the same 32 tokens, 128
     heads, context 32768, top-k 2048 + 128 + 4, page 64, with a 1,048,576-row
     pool of 656-byte rows (688 MB) instead of 1152-byte bf16 rows (1.21 GB).
-    Eight candidate sets rotate.  Timed (median of HIP event pairs): the
-    normalisation, and each decode entry point with its automatic splits
-    (decode + merge): fp8 rows and, for comparison, bf16 rows of the same
-    shape.  KV bytes per call: selected rows x 656 (fp8) or x 1152 (bf16)."""
+    Eight candidate sets rotate.  Timed: the normalisation (median of HIP
+    event pairs), and each decode entry point with its automatic splits
+    (decode + merge, calls back to back between two HIP events): fp8 rows and,
+    for comparison, bf16 rows of the same shape.  KV bytes per call: selected rows x 656 (fp8) or x 1152 (bf16)."""
     import torch
 
     import sparse_top_paged_amd as stp
@@ -826,9 +826,9 @@ def bench_fp8(args):
     s8 = stp.decode_fp8_splits(T, H, cap)
     ws8 = torch.empty((max(1, stp.decode_fp8_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
                       device=dev)
-    f_us = median_us(lambda k: stp.sparse_mla_decode_fp8(q, kv8, norm[k]["slot"],
-                                                         norm[k]["count"], c0.scale, 0, ws8,
-                                                         out, lse), n_launch, nsets)
+    f_us = throughput_us(lambda k: stp.sparse_mla_decode_fp8(q, kv8, norm[k]["slot"],
+                                                             norm[k]["count"], c0.scale, 0, ws8,
+                                                             out, lse), n_launch, nsets)
     # the split merge of the same partial states on its own, so that the fp8
     # decode kernel's launch time is the call's time less the merge's
     n_part = T * s8 * H
@@ -846,8 +846,9 @@ def bench_fp8(args):
     sb = stp.decode_splits(T, H, cap)
     wsb = torch.empty((max(1, stp.decode_workspace_bytes(T, H, cap)),), dtype=torch.uint8,
                       device=dev)
-    b_us = median_us(lambda k: stp.sparse_mla_decode(q, kvb, norm[k]["slot"], norm[k]["count"],
-                                                     c0.scale, 0, wsb, out, lse), n_launch, nsets)
+    b_us = throughput_us(lambda k: stp.sparse_mla_decode(q, kvb, norm[k]["slot"],
+                                                         norm[k]["count"], c0.scale, 0, wsb, out,
+                                                         lse), n_launch, nsets)
     topks = [t(c.topk) for c in cases]
     n_us = median_us(lambda k: stp.normalize_indices(topks[k], req, qpos, table, c0.page_size,
                                                      c0.window, c0.num_sinks, cap, out=norm[k]),
@@ -874,13 +875,14 @@ def bench_fp8(args):
                    "top_k": c0.top_k, "row_bytes": 656, "kv_pool_rows": c0.kv_rows,
                    "splits": s8, "candidate_sets": nsets,
                    "mean_selected_rows_per_token": round(sel / T, 2)},
-        "roofline": {"kernel": "sparse_mla_decode_fp8_kernel", "bound": "hbm",
+        "roofline": {"kernel": "sparse_mla_decode_kernel (fp8 rows)", "bound": "hbm",
                      "achieved": round(alg8 / dec8_us / 1e3, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(alg8 / dec8_us / 1e3 / 8000.0, 4), "traffic": traffic8,
                      "algorithmic_bytes_per_launch": int(alg8),
                      "avg_launch_us": round(dec8_us, 3),
-                     "launch_time": "decode + merge call less the merge's device time "
-                                    "(20 merges in one HIP graph)"},
+                     "launch_time": "decode + merge call (calls back to back between two "
+                                    "HIP events) less the merge's device time (20 merges in "
+                                    "one HIP graph)"},
         "normalise_us": round(n_us, 2),
         "fp8_decode_and_merge_us": round(f_us, 2),
         "fp8_merge_us": round(merge_us, 2),

@@ -274,10 +274,15 @@ size_t stp_sparse_mla_decode_noalloc_max_bytes(void);
  * stp_sparse_mla_decode, with kv [kv_rows, 656] uint8 rows: latent value i =
  * e4m3(byte i) * scale[i / 128] (OCP FP8 E4M3; scale = float32 at bytes
  * 512 + 4 (i / 128)), RoPE values bf16 at bytes 528..655; the key is the 576
- * values, the value vector the first 512.  The scales are applied in fp32,
- * the codes converted exactly.  num_splits 0 = automatic; more than one
- * split needs stp_sparse_mla_decode_fp8_workspace() bytes.  At most 1024
- * candidate ids per split (raised automatically).
+ * values, the value vector the first 512.  Each latent value is
+ * reconstructed right after the row is loaded as bf16(f32(code) * scale)
+ * (both roundings to nearest even), the RoPE values taken as they are, and
+ * attention runs over the reconstructed rows exactly as stp_sparse_mla_decode
+ * over bf16 rows ("5.1.1 · 从索引到 Kernel" §7.2: apply the scale at tile load
+ * and check against the same reconstructed values).  num_splits 0 =
+ * automatic (the bf16 rule); more than one split needs
+ * stp_sparse_mla_decode_fp8_workspace() bytes.  At most 1120 candidate ids
+ * per split (raised automatically).  kv must be 16-byte aligned.
  * Requirements: T >= 0, H >= 1, cap >= 0, kv_rows > 0, 0 < scale < inf.
  */
 int stp_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_rows,

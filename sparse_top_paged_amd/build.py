@@ -37,13 +37,11 @@ FLAGS = [
 # Per-source extra flags.  dense.hip: its softmax takes maxima of finite
 # scores and -inf masks only, so fmaxf needs no NaN handling; without it the
 # extend kernel's VALU work shrinks (measured 13 % faster, identical output).
-# dense.hip and decode_fp8.hip: MFMA results in VGPRs, so that accumulators
-# stay in one register file instead of being moved between AGPRs and VGPRs
-# (fp8 decode: O^T around the QK accumulators on every tile).  Not decode.hip,
-# whose output waves keep O^T in 256 AGPRs (the flag makes it 12 % slower).
+# dense.hip: MFMA results in VGPRs, so that accumulators stay in one register
+# file instead of being moved between AGPRs and VGPRs.  Not decode.hip, whose
+# output waves keep O^T in 256 AGPRs (the flag makes it 12 % slower).
 _VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {"dense.hip": ["-fno-honor-nans", *_VGPR_MFMA],
-               "decode_fp8.hip": _VGPR_MFMA}
+EXTRA_FLAGS = {"dense.hip": ["-fno-honor-nans", *_VGPR_MFMA]}
 
 
 def _compile(src):

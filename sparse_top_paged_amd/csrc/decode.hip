@@ -73,6 +73,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
@@ -81,6 +82,35 @@ typedef __attribute__((address_space(3))) shortx8 lds_shortx8;
 
 // Source of every masked-out row: loads stay in bounds and bring zeros.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytes] = {};
+
+// fp8_ds_mla rows: 512 E4M3 latent codes, four float32 scales (one per 128
+// values), 64 bf16 RoPE values.  The output waves stage them through
+// registers and write the dequantised row, bf16(f32(code) * scale) for the
+// latent values and the RoPE values as they are, into the tile layout of the
+// ring, so that every later step is the bf16 path's.  Output wave j handles
+// the 16 rows of its two groups 2 j + h (h = 0, 1): lane l takes row l / 8 of
+// the group and, of it, 16-byte chunk l % 8 of each 128-byte latent line
+// (codes 128 line + 16 (l % 8) .. + 15), RoPE chunk l % 8 and the four scales.
+constexpr int kFp8RowBytes = 656;
+constexpr int kFp8ScaleOff = 512;
+constexpr int kFp8RopeOff = 528;
+
+struct Fp8Rows {
+  uintx4 lat[2][4];  // [h][line]
+  floatx4 scl[2];    // [h]
+  uintx4 rope[2];    // [h]
+};
+
+// bf16(f32(code) * scale) of the eight codes in (w0, w1), packed in order
+__device__ __forceinline__ uintx4 dequant8(uint32_t w0, uint32_t w1, float sc) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  return uintx4{stp::pack_bf16x2(a.x * sc, a.y * sc), stp::pack_bf16x2(b.x * sc, b.y * sc),
+                stp::pack_bf16x2(c.x * sc, c.y * sc), stp::pack_bf16x2(d.x * sc, d.y * sc)};
+}
 
 // LDS tile layout: four groups of 8 rows (one group per wave when loading),
 // each group nine 1 KiB blocks; block b holds chunks 8 b .. 8 b + 7 (one
@@ -115,6 +145,8 @@ struct DecodeArgs {
   const int32_t* qent;
   int qcap;
   int32_t* queue;
+  // fp8_ds_mla rows (656 B) instead of kv, for the fp8 row format
+  const uint8_t* kv8;
 };
 
 // Output modes of the decode kernel.
@@ -316,8 +348,10 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
 }
 
 // One work item: token t, candidate positions lo .. lo + len - 1 of its list,
-// head group hg; split partials go to slot `part` ([part][H][512]).
-template <int kMode>
+// head group hg; split partials go to slot `part` ([part][H][512]).  kFp8:
+// the rows are fp8_ds_mla rows (a.kv8), dequantised on their way into the
+// ring.
+template <int kMode, bool kFp8 = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
                                             int hg, int64_t part) {
@@ -403,9 +437,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   auto tile_mask = [&](int i) {
     return (uint32_t)__ballot(L.ids[i * kTileRows + (lane & 31)] >= 0);
   };
-  if (!score) {
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
+  if constexpr (!kFp8) {
+    if (!score) {
+      if (ntiles > 0) issue(0, 0);
+      if (ntiles > 1) issue(1, 1);
+    }
   }
 
   // Pipeline over the ring of kStages = 4 tiles, with P(i) the published P^T
@@ -528,28 +564,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) o[hb][mb] = floatx16{};
   shortx4 v0[2][8], v1[2][8];
-  wait_vmcnt<0>();  // tiles 0 and 1
-  lds_barrier();    // B(0): stages 2 and 3 are free again
-  if (ntiles > 0) {
-    if (ntiles > 2) issue(2, 2);
-    read_v(L.tiles, v0, v1);
-    // tile 2 must have landed before B(1) (tile 3 may stay in flight)
-    if (ntiles > 3) {
-      issue(3, 3);
-      wait_vmcnt<2 * kSlotsPerThread>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // B(1): P(0) published
-  }
-  // iteration i (1 <= i <= ntiles): enqueue tile i+3 into the stage of tile
-  // i-1 (its V^T is in registers, its K was read two iterations ago); apply
-  // P(i-1) to V(i-1); read V(i) for the next iteration; tile i+2 lands before
-  // the barrier B(i+1) (the score waves read it in iteration i+1).  The 18
-  // load instructions of tile i+3 are spread between the MFMAs, one per MFMA
-  // pair, so that the wave never stalls on a full load queue.  Past the last
-  // tile nothing is loaded (and the wait before the barrier drains the queue).
-  for (int i = 1; i <= ntiles; ++i) {
+
+  // One output iteration i (1 <= i <= ntiles) but for the work on the tile
+  // after next: apply P(i-1) to V(i-1), read V(i) for the next iteration; the
+  // 18 steps of the next tile's loads (bf16 rows) or of the row staging (fp8
+  // rows), step(k), sit between the MFMA pairs and after the last one.
+  // Returns whether tile i was the last.
+  auto pv_iteration = [&](int i, auto&& step) {
     const int buf = (i - 1) & 1;
     const float a0 = L.alpha[buf * 64 + (lane & 31)];
     const float a1 = L.alpha[buf * 64 + 32 + (lane & 31)];
@@ -560,20 +581,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       for (int kap = 0; kap < 2; ++kap)
         pf[hb][kap] = *(const __attribute__((address_space(3))) bf16x8*)(
             L.pbuf + ((buf * 2 + hb) * 2 + kap) * 1024 + lane * 16);
-    const bool real = i + 3 < ntiles;
-    const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row + ld_col;
-    const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row + ld_col;
-    const int st3 = (i + 3) % kStages;
-    const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
-    auto load_chunk = [&](auto c) {
-      constexpr int kC = decltype(c)::value;
-      if (!real) return;
-      if constexpr (kC < kSlotsPerThread)
-        load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
-      else
-        load_lds_16<(kC - kSlotsPerThread) * 128>(src1,
-                                                  dst1 + (kC - kSlotsPerThread) * (1024 - 128));
-    };
     // alpha = 0 only while nothing has been accumulated (O^T is still zero)
     if (__ballot((a0 != 1.f && a0 != 0.f) || (a1 != 1.f && a1 != 0.f))) {
 #pragma unroll
@@ -596,19 +603,170 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
                                                             pf[hb][kap], o[hb][mb], 0, 0, 0);
       v0[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 0, mb));
       v1[kap][mb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vaddr(vn, kap, 1, mb));
-      load_chunk(std::integral_constant<int, kap * 8 + mb>{});
+      step(std::integral_constant<int, kap * 8 + mb>{});
       __builtin_amdgcn_sched_barrier(0);
     };
     static_for<2>([&](auto kc) { static_for<8>([&](auto mc) { pv_pair(kc, mc); }); });
-    load_chunk(std::integral_constant<int, 16>{});
-    load_chunk(std::integral_constant<int, 17>{});
-    if (i == ntiles) break;
-    // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
-    if (real)
-      wait_vmcnt<2 * kSlotsPerThread>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();  // B(i+1)
+    step(std::integral_constant<int, 16>{});
+    step(std::integral_constant<int, 17>{});
+    return i == ntiles;
+  };
+
+  if constexpr (!kFp8) {
+    wait_vmcnt<0>();  // tiles 0 and 1
+    lds_barrier();    // B(0): stages 2 and 3 are free again
+    if (ntiles > 0) {
+      if (ntiles > 2) issue(2, 2);
+      read_v(L.tiles, v0, v1);
+      // tile 2 must have landed before B(1) (tile 3 may stay in flight)
+      if (ntiles > 3) {
+        issue(3, 3);
+        wait_vmcnt<2 * kSlotsPerThread>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();  // B(1): P(0) published
+    }
+    // iteration i (1 <= i <= ntiles): enqueue tile i+3 into the stage of tile
+    // i-1 (its V^T is in registers, its K was read two iterations ago); apply
+    // P(i-1) to V(i-1); read V(i) for the next iteration; tile i+2 lands before
+    // the barrier B(i+1) (the score waves read it in iteration i+1).  The 18
+    // load instructions of tile i+3 are spread between the MFMAs, one per MFMA
+    // pair, so that the wave never stalls on a full load queue.  Past the last
+    // tile nothing is loaded (and the wait before the barrier drains the queue).
+    for (int i = 1; i <= ntiles; ++i) {
+      const bool real = i + 3 < ntiles;
+      const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row + ld_col;
+      const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row + ld_col;
+      const int st3 = (i + 3) % kStages;
+      const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
+      auto load_chunk = [&](auto c) {
+        constexpr int kC = decltype(c)::value;
+        if (!real) return;
+        if constexpr (kC < kSlotsPerThread)
+          load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
+        else
+          load_lds_16<(kC - kSlotsPerThread) * 128>(src1,
+                                                    dst1 + (kC - kSlotsPerThread) * (1024 - 128));
+      };
+      if (pv_iteration(i, load_chunk)) break;
+      // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
+      if (real)
+        wait_vmcnt<2 * kSlotsPerThread>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();  // B(i+1)
+    }
+  } else {
+    // fp8 rows through registers: tile t is loaded during iteration t - 3
+    // (into one buffer of registers, a line at a time as the previous tile's
+    // line leaves it) and dequantised into its ring stage during iteration
+    // t - 2 (stage (t - 2) % 4 is then free: tile t - 4's V^T was read in
+    // iteration t - 4 and its K before).  Tiles 0 and 1 are written before
+    // B(0), tile 2 between B(0) and B(1); past the last tile the zero row is
+    // loaded, so every iteration does the same work.
+    const int rl = lane >> 3, u = lane & 7;
+    auto fp8_row = [&](int tile, int h) {
+      const int id = tile < ntiles ? L.ids[tile * kTileRows + (2 * j + h) * kGroupRows + rl] : -1;
+      return id >= 0 ? a.kv8 + (int64_t)id * kFp8RowBytes : zero_row;
+    };
+    // LDS offsets in a stage: latent chunk 16 line + 2 u + half of group row
+    // rl sits in block 2 line + u / 4 at position ((2 u + half) % 8) ^ rl;
+    // RoPE chunk u in block 8 at position u ^ rl
+    int lat_off[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      lat_off[half] = (u >> 2) * 1024 + rl * 128 + ((((2 * u + half) & 7) ^ rl) << 4);
+    const int rope_off = 8 * 1024 + rl * 128 + ((u ^ rl) << 4);
+    // global (not flat) loads: a flat load also counts against the LDS
+    // counter, so every LDS wait would wait for the rows in flight too
+    typedef const __attribute__((address_space(1))) uintx4 g_uintx4;
+    typedef const __attribute__((address_space(1))) floatx4 g_floatx4;
+    auto load_latent = [&](Fp8Rows& b, int h, int line, const uint8_t* p) {
+      b.lat[h][line] = *(g_uintx4*)(p + 128 * line + 16 * u);
+    };
+    auto load_rope = [&](Fp8Rows& b, int h, const uint8_t* p) {
+      b.rope[h] = *(g_uintx4*)(p + kFp8RopeOff + 16 * u);
+    };
+    auto load_scales = [&](floatx4& sc, const uint8_t* p) { sc = *(g_floatx4*)(p + kFp8ScaleOff); };
+    auto load_all = [&](Fp8Rows& b, int tile) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* p = fp8_row(tile, h);
+        load_scales(b.scl[h], p);
+#pragma unroll
+        for (int line = 0; line < 4; ++line) load_latent(b, h, line, p);
+        load_rope(b, h, p);
+      }
+    };
+    auto store_half = [&](const Fp8Rows& b, int h, int line, int half, lds_t* stage) {
+      const uintx4 d = b.lat[h][line];
+      const uintx4 w = half ? dequant8(d[2], d[3], b.scl[h][line])
+                            : dequant8(d[0], d[1], b.scl[h][line]);
+      *(__attribute__((address_space(3))) uintx4*)(
+          stage + (2 * j + h) * kGroupBytes + 2 * line * 1024 + lat_off[half]) = w;
+    };
+    auto store_rope = [&](const Fp8Rows& b, int h, lds_t* stage) {
+      *(__attribute__((address_space(3))) uintx4*)(stage + (2 * j + h) * kGroupBytes +
+                                                    rope_off) = b.rope[h];
+    };
+    auto store_all = [&](const Fp8Rows& b, lds_t* stage) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int line = 0; line < 4; ++line) {
+          store_half(b, h, line, 0, stage);
+          store_half(b, h, line, 1, stage);
+        }
+        store_rope(b, h, stage);
+      }
+    };
+    Fp8Rows fb;
+    {
+      Fp8Rows f0;  // prologue only
+      load_all(f0, 0);
+      load_all(fb, 1);
+      store_all(f0, L.tiles);
+    }
+    store_all(fb, L.tiles + kTileBytes);
+    load_all(fb, 2);
+    lds_barrier();  // B(0): tiles 0 and 1 written, stages 2 and 3 free again
+    if (ntiles > 0) {
+      store_all(fb, L.tiles + 2 * kTileBytes);
+      load_all(fb, 3);
+      read_v(L.tiles, v0, v1);
+      lds_barrier();  // B(1): P(0) published, tile 2 written
+    }
+    // iteration i: dequantise tile i+2 into its stage while loading tile i+3
+    // into the same registers: tile i+3's scales first (into registers of
+    // their own, taken over at the end), then a latent half-line per MFMA
+    // pair (the line reloaded after its second half), the RoPE chunks after
+    // the last pair
+    for (int i = 1; i <= ntiles; ++i) {
+      lds_t* stage = L.tiles + ((i + 2) % kStages) * kTileBytes;
+      const uint8_t* p0 = fp8_row(i + 3, 0);
+      const uint8_t* p1 = fp8_row(i + 3, 1);
+      floatx4 nscl[2];
+      load_scales(nscl[0], p0);
+      load_scales(nscl[1], p1);
+      auto step = [&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < 16) {
+          constexpr int h = k >> 3, line = (k >> 1) & 3, half = k & 1;
+          store_half(fb, h, line, half, stage);
+          if constexpr (half == 1) load_latent(fb, h, line, h ? p1 : p0);
+        } else {
+          constexpr int h = k - 16;
+          store_rope(fb, h, stage);
+          load_rope(fb, h, h ? p1 : p0);
+        }
+      };
+      const bool last = pv_iteration(i, step);
+      fb.scl[0] = nscl[0];
+      fb.scl[1] = nscl[1];
+      if (last) break;
+      lds_barrier();  // B(i+1): tile i+2 written
+    }
   }
   wait_vmcnt<0>();  // nothing left in flight before the ring is reused below
   lds_barrier();  // statistics published
@@ -696,7 +854,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
 // slot is -1); the others write partial states for the merge.  A workgroup ends
 // when no queue has an unclaimed item (every queue is finite and its head
 // only grows, so every workgroup exits).
-template <int kMode, bool kQueue>
+template <int kMode, bool kQueue, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
@@ -726,7 +884,7 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const int chunk = (n + a.S - 1) / a.S;
     const int lo = min(n, s * chunk);
     const int len = min(n, lo + chunk) - lo;
-    decode_item<kMode>(a, L, s_bad, zero_row, t, lo, len, hg, (int64_t)t * a.S + s);
+    decode_item<kMode, kFp8>(a, L, s_bad, zero_row, t, lo, len, hg, (int64_t)t * a.S + s);
   } else {
     const int grid = gridDim.x;
     const int x = blockIdx.x & 7;
@@ -856,10 +1014,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
                   const int32_t* row_ids, const int32_t* counts, int32_t cap, int32_t T, int32_t H,
                   float scale, int32_t S, float* o_part, float* m_part, float* l_part,
-                  uint16_t* out, float* lse, hipStream_t stream) {
+                  uint16_t* out, float* lse, hipStream_t stream, const uint8_t* kv8 = nullptr) {
   DecodeArgs a{};
   a.q = q;
   a.kv = kv;
+  a.kv8 = kv8;
   a.kv_rows = kv_rows;
   a.row_ids = row_ids;
   a.counts = counts;
@@ -876,7 +1035,13 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
   a.lse = lse;
   const int64_t blocks = (int64_t)8 * ((T + 7) / 8) * S * a.G;
   if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: grid too large");
-  if (mode == kOutPartialF32)
+  if (kv8) {  // fp8_ds_mla rows: the final output or normalised partials
+    if (mode == kOutPartialBf16)
+      sparse_mla_decode_kernel<kOutPartialBf16, false, true>
+          <<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+    else
+      sparse_mla_decode_kernel<kOutFinal, false, true><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+  } else if (mode == kOutPartialF32)
     sparse_mla_decode_kernel<kOutPartialF32, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
   else if (mode == kOutPartialBf16)
     sparse_mla_decode_kernel<kOutPartialBf16, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
@@ -1053,6 +1218,51 @@ extern "C" int stp_sparse_mla_decode_partial_normalized(
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial_normalized: null output");
   return launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale,
                        num_splits, (float*)o_norm, m_part, l_part, nullptr, nullptr, stream);
+}
+
+// fp8_ds_mla rows: the same launch and split path, the rows dequantised on
+// their way into the ring.
+extern "C" int32_t stp_sparse_mla_decode_fp8_splits(int32_t T, int32_t H, int32_t cap,
+                                                    int32_t num_splits) {
+  return stp_sparse_mla_decode_splits(T, H, cap, num_splits);
+}
+
+extern "C" size_t stp_sparse_mla_decode_fp8_workspace(int32_t T, int32_t H, int32_t cap,
+                                                      int32_t num_splits) {
+  return stp_sparse_mla_decode_workspace(T, H, cap, num_splits);
+}
+
+extern "C" int stp_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_rows,
+                                         const int32_t* row_ids, const int32_t* counts,
+                                         int32_t cap, int32_t T, int32_t H, float scale,
+                                         int32_t num_splits, void* workspace,
+                                         size_t workspace_bytes, uint16_t* out, float* lse,
+                                         hipStream_t stream) {
+  using stp::fail;
+  if (int rc = check_common(q, (const uint16_t*)kv, kv_rows, row_ids, cap, T, H, scale)) return rc;
+  if (num_splits < 0)
+    return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_fp8: num_splits < 0");
+  if (T == 0) return STP_OK;
+  if (!out) return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_fp8: null out");
+  if ((uintptr_t)kv % 16 != 0)
+    return fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_fp8: kv must be 16-byte aligned");
+  const int32_t S = choose_splits(T, H, cap, num_splits);
+  if (S == 1)
+    return launch_decode(kOutFinal, q, nullptr, kv_rows, row_ids, counts, cap, T, H, scale, 1,
+                         nullptr, nullptr, nullptr, out, lse, stream, kv);
+  const size_t need = stp_sparse_mla_decode_workspace(T, H, cap, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(STP_ERR_WORKSPACE, "sparse_mla_decode_fp8: workspace of %zu bytes needed, %zu given",
+                need, workspace_bytes);
+  const size_t n = (size_t)T * S * H;
+  char* ws = (char*)workspace;
+  uint16_t* o_norm = (uint16_t*)ws;
+  float* m_part = (float*)(ws + align256(n * kDV * 2));
+  float* l_part = (float*)(ws + align256(n * kDV * 2) + align256(n * 4));
+  if (int rc = launch_decode(kOutPartialBf16, q, nullptr, kv_rows, row_ids, counts, cap, T, H,
+                             scale, S, (float*)o_norm, m_part, l_part, nullptr, nullptr, stream, kv))
+    return rc;
+  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, kDV, out, lse, stream);
 }
 
 namespace stp {
