@@ -155,7 +155,9 @@ def counters(out, command, *paths):
             k = short_name(r["Kernel_Name"])
             if DECODE_KERNEL in k:
                 k = "sparse_mla_decode_kernel"
-            elif "row_gather_kernel" not in k:
+            elif "row_gather" in k:  # the register or the LDS-ring variant
+                k = "row_gather_kernel"
+            else:
                 continue
             d = groups[k][(path, int(r["Dispatch_Id"]))]
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
