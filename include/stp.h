@@ -237,8 +237,10 @@ int stp_backup_rows(const void* hot_cache, int64_t hot_rows, void* host_pool, in
  * workspace of stp_sparse_mla_decode_workspace() bytes (STP_ERR_WORKSPACE if
  * smaller); the workspace may be reused once the call's work has completed
  * on `stream`.
- * The split count is raised to at least ceil(cap / 1120) whatever is asked
- * (a split's ids are staged in LDS).
+ * num_splits = 1 is a single pass per token: no partial states, no merge.
+ * A split of more than 1120 candidates (the ids a workgroup stages in LDS at
+ * once) keeps them in a ring of 35 32-row tiles refilled as it goes; the
+ * automatic count stays within 1120 per split.
  * Requirements: T >= 0, H >= 1, cap >= 0, 0 < kv_rows, 0 < scale < inf.
  */
 int stp_sparse_mla_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_rows,
@@ -281,8 +283,8 @@ size_t stp_sparse_mla_decode_noalloc_max_bytes(void);
  * over bf16 rows ("5.1.1 · 从索引到 Kernel" §7.2: apply the scale at tile load
  * and check against the same reconstructed values).  num_splits 0 =
  * automatic (the bf16 rule); more than one split needs
- * stp_sparse_mla_decode_fp8_workspace() bytes.  At most 1120 candidate ids
- * per split (raised automatically).  kv must be 16-byte aligned.
+ * stp_sparse_mla_decode_fp8_workspace() bytes.  Splits of any length, as
+ * for bf16 rows.  kv must be 16-byte aligned.
  * Requirements: T >= 0, H >= 1, cap >= 0, kv_rows > 0, 0 < scale < inf.
  */
 int stp_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* kv, int64_t kv_rows,

@@ -62,6 +62,7 @@ constexpr int kStages = 4;
 constexpr int kSlotsPerThread = kTileRows * kChunks / kThreads; // 9
 constexpr int kHeadsPerWG = 64;
 constexpr int kIdsMax = 1120;  // 35 tiles: half of a 2180-candidate list fits (what the LDS has left)
+constexpr int kIdTiles = kIdsMax / 32;  // a longer split keeps its ids in a ring of this many tiles
 constexpr int kQKSteps = kDQK / 16;                             // 36
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -166,6 +167,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 using stp::scale_acc;
 
 using stp::load_lds_16;
+
+// 4 bytes per lane from global memory straight into LDS (global_load_lds_dword):
+// LDS address m0 + 4 * lane; untracked by the compiler, like load_lds_16.
+__device__ __forceinline__ void load_lds_4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds_addr));
+}
 using stp::pair_max;
 using stp::pair_sum;
 
@@ -350,8 +357,13 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
 // One work item: token t, candidate positions lo .. lo + len - 1 of its list,
 // head group hg; split partials go to slot `part` ([part][H][512]).  kFp8:
 // the rows are fp8_ds_mla rows (a.kv8), dequantised on their way into the
-// ring.
-template <int kMode, bool kFp8 = false>
+// ring.  kLong: the split may hold more candidates than the LDS id list
+// (kIdsMax): the list is then a ring of kIdTiles tiles, tile t in slot
+// t % kIdTiles; the first kIdTiles tiles are staged as usual, and in output
+// iteration i the slot of tile i - 1 (whose ids every wave is done with after
+// B(i)) takes tile i + kIdTiles - 1's ids by LDS DMA, as they are in
+// memory: position and range checks then happen where ids are read.
+template <int kMode, bool kFp8 = false, bool kLong = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
                                             int hg, int64_t part) {
@@ -404,11 +416,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       v[k] = i < len ? src_ids[i] : -1;
     }
     int bad = 0;
+    const int staged = kLong ? min(ntiles * kTileRows, kIdsMax) : ntiles * kTileRows;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int i = tid - 128 + 128 * k;
       const bool valid = v[k] >= 0 && v[k] < a.kv_rows;
-      if (i < ntiles * kTileRows) L.ids[i] = valid ? v[k] : -1;
+      if (i < staged) L.ids[i] = valid ? v[k] : -1;
       bad |= (i < len && !valid) ? 1 : 0;
     }
     const int wbad = __ballot(bad) != 0 ? 1 : 0;
@@ -416,13 +429,36 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   }
   lds_barrier();
   // a split with an invalid id masks every tile, otherwise only its last tile
-  // (the rows past its end) needs a mask
-  const bool mask_all = (s_bad[0] | s_bad[1]) != 0;
+  // (the rows past its end) needs a mask (a long split: every tile, its later
+  // ids are not seen before their turn)
+  const bool mask_all = kLong || (s_bad[0] | s_bad[1]) != 0;
+
+  // id of row r of tile i, -1 for an invalid candidate or a row past the end
+  auto id_at = [&](int i, int r) {
+    if constexpr (kLong) {
+      const int id = L.ids[(i % kIdTiles) * kTileRows + r];
+      return (i * kTileRows + r < len && id >= 0 && id < a.kv_rows) ? id : -1;
+    } else {
+      return L.ids[i * kTileRows + r];
+    }
+  };
+  // kLong: in output iteration i, load tile i + kIdTiles - 1's ids into the
+  // slot of tile i - 1 (output wave 0, one id per lane)
+  auto refill_ids = [&](int i) {
+    if constexpr (kLong) {
+      const int tn = i + kIdTiles - 1;
+      if (j == 0 && lane < kTileRows && tn * kTileRows + lane < len) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(L.ids + (tn % kIdTiles) * kTileRows));
+        load_lds_4(a.row_ids + (int64_t)t * a.cap + lo + tn * kTileRows + lane, dst);
+      }
+    }
+  };
 
   // source of this lane's row of group grp of tile i (the zero row for an
   // invalid candidate)
   auto row_src = [&](int i, int grp) {
-    const int id = L.ids[i * kTileRows + grp * kGroupRows + (lane >> 3)];
+    const int id = id_at(i, grp * kGroupRows + (lane >> 3));
     return (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : zero_row) + ld_col;
   };
   auto issue_group = [&](int i, int st, int grp) {
@@ -434,9 +470,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     issue_group(i, st, 2 * j);
     issue_group(i, st, 2 * j + 1);
   };
-  auto tile_mask = [&](int i) {
-    return (uint32_t)__ballot(L.ids[i * kTileRows + (lane & 31)] >= 0);
-  };
+  auto tile_mask = [&](int i) { return (uint32_t)__ballot(id_at(i, lane & 31) >= 0); };
   if constexpr (!kFp8) {
     if (!score) {
       if (ntiles > 0) issue(0, 0);
@@ -635,6 +669,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // pair, so that the wave never stalls on a full load queue.  Past the last
     // tile nothing is loaded (and the wait before the barrier drains the queue).
     for (int i = 1; i <= ntiles; ++i) {
+      refill_ids(i);  // (kLong) lands before B(i+1): the wait below leaves only tile i+3's loads
       const bool real = i + 3 < ntiles;
       const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row + ld_col;
       const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row + ld_col;
@@ -667,7 +702,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // loaded, so every iteration does the same work.
     const int rl = lane >> 3, u = lane & 7;
     auto fp8_row = [&](int tile, int h) {
-      const int id = tile < ntiles ? L.ids[tile * kTileRows + (2 * j + h) * kGroupRows + rl] : -1;
+      const int id = tile < ntiles ? id_at(tile, (2 * j + h) * kGroupRows + rl) : -1;
       return id >= 0 ? a.kv8 + (int64_t)id * kFp8RowBytes : zero_row;
     };
     // LDS offsets in a stage: latent chunk 16 line + 2 u + half of group row
@@ -743,6 +778,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // pair (the line reloaded after its second half), the RoPE chunks after
     // the last pair
     for (int i = 1; i <= ntiles; ++i) {
+      refill_ids(i);
       lds_t* stage = L.tiles + ((i + 2) % kStages) * kTileBytes;
       const uint8_t* p0 = fp8_row(i + 3, 0);
       const uint8_t* p1 = fp8_row(i + 3, 1);
@@ -765,6 +801,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       fb.scl[0] = nscl[0];
       fb.scl[1] = nscl[1];
       if (last) break;
+      // (kLong) the id refill of the previous iteration has landed: only this
+      // iteration's 12 row loads may still be in flight
+      if constexpr (kLong) wait_vmcnt<12>();
       lds_barrier();  // B(i+1): tile i+2 written
     }
   }
@@ -854,7 +893,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
 // slot is -1); the others write partial states for the merge.  A workgroup ends
 // when no queue has an unclaimed item (every queue is finite and its head
 // only grows, so every workgroup exits).
-template <int kMode, bool kQueue, bool kFp8 = false>
+template <int kMode, bool kQueue, bool kFp8 = false, bool kLong = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
@@ -884,7 +923,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const int chunk = (n + a.S - 1) / a.S;
     const int lo = min(n, s * chunk);
     const int len = min(n, lo + chunk) - lo;
-    decode_item<kMode, kFp8>(a, L, s_bad, zero_row, t, lo, len, hg, (int64_t)t * a.S + s);
+    decode_item<kMode, kFp8, kLong>(a, L, s_bad, zero_row, t, lo, len, hg,
+                                    (int64_t)t * a.S + s);
   } else {
     const int grid = gridDim.x;
     const int x = blockIdx.x & 7;
@@ -987,12 +1027,14 @@ using stp::device_cus;
 // tiles of its split), and splitting adds the merge launch plus partial
 // states for it to read.  Costs in tile units: about four tiles of prologue
 // and epilogue per workgroup; the merge three tiles plus about 0.9 tile per
-// split per 32 query tokens.  A split's ids must fit the LDS list (kIdsMax).
-// The count depends on the current device's compute units.
+// split per 32 query tokens.  The automatic count keeps a split's ids within
+// the LDS list (kIdsMax); a requested count is taken as it is (longer splits
+// run with the id ring).  The count depends on the current device's compute
+// units.
 int32_t choose_splits(int32_t T, int32_t H, int32_t cap, int32_t requested) {
   const int G = (H + kHeadsPerWG - 1) / kHeadsPerWG;
   const int s_min = max(1, (cap + kIdsMax - 1) / kIdsMax);
-  if (requested > 0) return max(requested, s_min);
+  if (requested > 0) return requested;
   const int64_t cus = device_cus();
   int best = s_min;
   double best_cost = 1e300;
@@ -1035,18 +1077,26 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
   a.lse = lse;
   const int64_t blocks = (int64_t)8 * ((T + 7) / 8) * S * a.G;
   if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode: grid too large");
+  // a split longer than the LDS id list takes the id ring (kLong)
+  const bool lng = (cap + S - 1) / S > kIdsMax;
+  auto go = [&](auto kern) { kern<<<(unsigned)blocks, kThreads, 0, stream>>>(a); };
   if (kv8) {  // fp8_ds_mla rows: the final output or normalised partials
     if (mode == kOutPartialBf16)
-      sparse_mla_decode_kernel<kOutPartialBf16, false, true>
-          <<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+      lng ? go(sparse_mla_decode_kernel<kOutPartialBf16, false, true, true>)
+          : go(sparse_mla_decode_kernel<kOutPartialBf16, false, true, false>);
     else
-      sparse_mla_decode_kernel<kOutFinal, false, true><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
-  } else if (mode == kOutPartialF32)
-    sparse_mla_decode_kernel<kOutPartialF32, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
-  else if (mode == kOutPartialBf16)
-    sparse_mla_decode_kernel<kOutPartialBf16, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
-  else
-    sparse_mla_decode_kernel<kOutFinal, false><<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+      lng ? go(sparse_mla_decode_kernel<kOutFinal, false, true, true>)
+          : go(sparse_mla_decode_kernel<kOutFinal, false, true, false>);
+  } else if (mode == kOutPartialF32) {
+    lng ? go(sparse_mla_decode_kernel<kOutPartialF32, false, false, true>)
+        : go(sparse_mla_decode_kernel<kOutPartialF32, false, false, false>);
+  } else if (mode == kOutPartialBf16) {
+    lng ? go(sparse_mla_decode_kernel<kOutPartialBf16, false, false, true>)
+        : go(sparse_mla_decode_kernel<kOutPartialBf16, false, false, false>);
+  } else {
+    lng ? go(sparse_mla_decode_kernel<kOutFinal, false, false, true>)
+        : go(sparse_mla_decode_kernel<kOutFinal, false, false, false>);
+  }
   return stp::check_launch("sparse_mla_decode_kernel");
 }
 
@@ -1191,9 +1241,6 @@ extern "C" int stp_sparse_mla_decode_partial(const uint16_t* q, const uint16_t* 
   if (int rc = check_common(q, kv, kv_rows, row_ids, cap, T, H, scale)) return rc;
   if (num_splits < 1)
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial: num_splits must be >= 1");
-  if ((cap + num_splits - 1) / num_splits > kIdsMax)
-    return stp::fail(STP_ERR_INVALID_ARG,
-                     "sparse_mla_decode_partial: ceil(cap / num_splits) exceeds %d", kIdsMax);
   if (T == 0) return STP_OK;
   if (!o_part || !m_part || !l_part)
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial: null output");
@@ -1209,10 +1256,6 @@ extern "C" int stp_sparse_mla_decode_partial_normalized(
   if (num_splits < 1)
     return stp::fail(STP_ERR_INVALID_ARG,
                      "sparse_mla_decode_partial_normalized: num_splits must be >= 1");
-  if ((cap + num_splits - 1) / num_splits > kIdsMax)
-    return stp::fail(STP_ERR_INVALID_ARG,
-                     "sparse_mla_decode_partial_normalized: ceil(cap / num_splits) exceeds %d",
-                     kIdsMax);
   if (T == 0) return STP_OK;
   if (!o_norm || !m_part || !l_part)
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial_normalized: null output");

@@ -263,3 +263,66 @@ def test_long_context_eight_splits(clustered):
     _full_check(c, kv, out, lse, list(range(c.T)), "long context")
     del kv
     torch.cuda.empty_cache()
+
+
+def _long_lists(rng, T, H, cap, rows):
+    """Lists longer than the 1120 ids a workgroup stages at once: full, ragged
+    and short counts, valid ids left in the list past each count (they must
+    not be read), and invalid ids (negative, past the pool) in later tiles."""
+    kv_bits = workloads.normal_bf16(rng, (rows, 576))
+    q_bits = workloads.normal_bf16(rng, (T, H, 576))
+    ids = np.stack([rng.choice(rows, size=cap, replace=False) for _ in range(T)]).astype(np.int32)
+    counts = np.asarray([cap, cap - 1, 1121, 1120, 1119, 35 * 32 * 2 + 17, 40, 0][:T], np.int32)
+    for t in range(T):
+        if counts[t] > 1500:
+            ids[t, 1500] = -7                 # invalid ids past the first ring turn
+            ids[t, counts[t] - 2] = rows + 3
+    return q_bits, kv_bits, ids, counts
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_long_splits_single_pass(splits):
+    """num_splits = 1 is one pass per token over all 3000 candidates (no merge);
+    2 splits give 1500 each: both longer than the LDS id list, so the ids go
+    through the ring (35 tiles) and are range-checked where they are read."""
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(77 + splits)
+    T, H, cap, rows = 8, 64, 3000, 6000
+    q_bits, kv_bits, ids, counts = _long_lists(rng, T, H, cap, rows)
+    assert stp.decode_splits(T, H, cap, splits) == splits
+    assert stp.decode_workspace_bytes(T, H, cap, 1) == 0
+    out, lse = _decode(q_bits, bf16_dev(kv_bits), ids, counts, 0.04, splits)
+    o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, counts, 0.04)
+    assert_attention_close(out, lse, o_ref, l_ref, f"long lists, {splits} split(s)")
+    assert torch.all(out[7] == 0) and torch.all(torch.isneginf(lse[7]))
+
+
+def test_long_split_partial_states():
+    """The unnormalised partial states of two 1500-candidate splits, merged,
+    against the oracle's partials and the single pass."""
+    import sparse_top_paged_amd as stp
+    rng = np.random.default_rng(78)
+    T, H, cap, rows = 6, 64, 3000, 6000
+    q_bits, kv_bits, ids, counts = _long_lists(rng, T, H, cap, rows)
+    q, kv = bf16_dev(q_bits), bf16_dev(kv_bits)
+    o_p, m_p, l_p = stp.sparse_mla_decode_partial(q, kv, to_dev(ids), to_dev(counts), 0.04, 2)
+    out, lse = stp.splitkv_merge(o_p, m_p, l_p)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attend_sparse(q_bits, kv_bits, ids, counts, 0.04)
+    assert_attention_close(out, lse, o_ref, l_ref, "long partial states, merged")
+
+
+def test_deepseek_shape_single_pass():
+    """The 32-token, 2180-candidate decode with num_splits = 1: one pass per
+    (token, head group) over the whole list, every token against the oracle."""
+    import sparse_top_paged_amd as stp
+    c = workloads.deepseek_case()
+    kv = workloads.pool_torch(c.kv_rows, c.pool_seed, dev())
+    norm = stp.normalize_indices(to_dev(c.topk), to_dev(c.req_id), to_dev(c.q_pos),
+                                 to_dev(c.block_table), c.page_size, c.window, c.num_sinks, c.cap,
+                                 block_view=False)
+    out, lse = stp.sparse_mla_decode(bf16_dev(c.q_bits), kv, norm["slot"], norm["count"], c.scale,
+                                     num_splits=1)
+    torch.cuda.synchronize()
+    _full_check(c, kv, out, lse, list(range(c.T)), "single pass")
+    del kv

@@ -72,6 +72,24 @@ def test_random_ragged(H, cap, splits):
     assert_attention_close(out, lse, o_ref, l_ref, f"H {H} cap {cap} splits {splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+def test_long_splits(splits):
+    """Splits longer than the 1120 ids staged at once (the id ring): one pass
+    over 2600 candidates, or two of 1300; ids out of range in later tiles,
+    counts short of the list (valid ids left past them)."""
+    rng = np.random.default_rng(90 + splits)
+    kv_rows, T, H, cap = 4000, 4, 64, 2600
+    rows = workloads.fp8_rows(rng, kv_rows)
+    q = workloads.normal_bf16(rng, (T, H, 576))
+    ids = np.stack([rng.choice(kv_rows, size=cap, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[:, 1700] = -3
+    ids[:, 2300] = kv_rows + 9
+    counts = np.asarray([cap, 2301, 1121, 700], np.int32)
+    out, lse = _decode(q, rows, ids, counts, 576 ** -0.5, splits)
+    o_ref, l_ref = oracle.attend_sparse_fp8(q, rows, ids, counts, 576 ** -0.5)
+    assert_attention_close(out, lse, o_ref, l_ref, f"fp8 long splits {splits}")
+
+
 def test_empty_sets():
     rng = np.random.default_rng(5)
     rows = workloads.fp8_rows(rng, 50)
