@@ -262,8 +262,11 @@ def graph_us(fn, reps=20, replays=20):
 def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     """Practical ceilings measured in the same run: the decode's row gather with
     nothing else (the rows of each candidate set read once per head group, as
-    the decode reads them, and read once in all), and a plain device copy."""
+    the decode reads them, and read once in all), a plain device copy, a
+    sequential read of the pool and a bf16 GEMM."""
     import torch
+
+    from sparse_top_paged_amd import diag
     T = norm[0]["slot"].shape[0]
     rows = kv.view(torch.uint8).view(kv.shape[0], -1)
     kv_bytes = [int(nb["count"].sum().item()) * ROW_BYTES for nb in norm]
@@ -271,9 +274,9 @@ def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     out = {}
     for name, parts, reps in [("row_gather_decode_placement", splits, head_groups),
                               ("row_gather_each_row_once", splits * head_groups, 1)]:
-        cs = torch.empty((stp._lib.lib.stp_row_gather_blocks(T, parts, reps),), dtype=torch.int32,
+        cs = torch.empty((diag.row_gather_blocks(T, parts, reps),), dtype=torch.int32,
                          device=kv.device)
-        us = median_us(lambda k: stp.row_gather(rows, norm[k]["slot"], norm[k]["count"], parts,
+        us = median_us(lambda k: diag.row_gather(rows, norm[k]["slot"], norm[k]["count"], parts,
                                                 reps, checksum=cs), n, sets)
         out[name] = {"us": round(us, 3), "kv_gbs": round(mean_kv / us / 1e3, 1),
                      "parts": parts, "replicas": reps}
@@ -285,7 +288,7 @@ def measure_ceilings(stp, kv, norm, sets, splits, head_groups, n=200):
     # a plain sequential read of the KV pool (1.2 GB, stp_stream_read): what HBM
     # delivers to a streaming read on this device
     cs_read = torch.empty((2048,), dtype=torch.int32, device=kv.device)
-    us = median_us(lambda k: stp.stream_read(kv, 2048, checksum=cs_read), 20, 1)
+    us = median_us(lambda k: diag.stream_read(kv, 2048, checksum=cs_read), 20, 1)
     nbytes = kv.numel() * kv.element_size()
     out["device_read_pool"] = {"us": round(us, 3), "gbs": round(nbytes / us / 1e3, 1),
                                "bytes": nbytes, "how": "stp_stream_read over the bf16 pool"}
@@ -631,6 +634,7 @@ def bench_gqa(args):
 
     import sparse_top_paged_amd as stp
     import workloads
+    from sparse_top_paged_amd import diag
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -662,8 +666,8 @@ def bench_gqa(args):
                 ids[b * Hkv + g, :n] = sl * Hkv + g
         ids_d, cnt_d = t(ids), t(np.repeat(c.ctx_lens, Hkv).astype(np.int32))
         krows, vrows = kd.view(torch.uint8).view(-1, 256), vd.view(torch.uint8).view(-1, 256)
-        ceil_us = median_us(lambda k: (stp.row_gather(krows, ids_d, cnt_d, parts=2),
-                                       stp.row_gather(vrows, ids_d, cnt_d, parts=2)), n_launch, 1)
+        ceil_us = median_us(lambda k: (diag.row_gather(krows, ids_d, cnt_d, parts=2),
+                                       diag.row_gather(vrows, ids_d, cnt_d, parts=2)), n_launch, 1)
         del ids_d
     traffic = load_traffic(d_alg, GQA_TRAFFIC_FILE, DENSE_SRC)
     del kd, vd

@@ -420,41 +420,6 @@ int stp_splitkv_merge_normalized(const uint16_t* o_norm, const float* m_part,
                                  uint16_t* out, float* lse, hipStream_t stream);
 
 /*
- * Diagnostic: the bandwidth ceiling of the decode's row gather ("5.1.1 · 从
- * 索引到 Kernel" §2, eq. (8)-(9): decode time is set by the candidate rows'
- * bytes).  Reads every byte of the rows row_ids[t, lo:lo+len] of each query
- * token t, for `parts` contiguous ranges per token (lo, len as the decode's
- * splits: ranges of ceil(counts[t] / parts) entries), each range read by
- * `replicas` workgroups (as the decode reads a range once per group of 64
- * query heads), with the decode's placement of workgroups on XCDs.  Computes
- * nothing but an xor of the words read, one uint32 per workgroup in
- * checksum[stp_row_gather_blocks(T, parts, replicas)].
- *   rows       [num_rows, row_bytes] bytes (row_bytes a multiple of 16)
- *   row_ids    [T, cap] int32; -1 and ids outside [0, num_rows) read nothing
- *   counts     [T] or NULL (then cap)
- * Errors: sizes < 0 or parts / replicas < 1, ceil(cap / parts) > 4096,
- * row_bytes not a positive multiple of 16 -> STP_ERR_INVALID_ARG.
- */
-int stp_row_gather(const void* rows, int64_t num_rows, int64_t row_bytes, const int32_t* row_ids,
-                   const int32_t* counts, int32_t cap, int32_t T, int32_t parts, int32_t replicas,
-                   uint32_t* checksum, hipStream_t stream);
-
-/* Workgroups (= checksum words) of stp_row_gather; 0 for invalid sizes. */
-int32_t stp_row_gather_blocks(int32_t T, int32_t parts, int32_t replicas);
-
-/*
- * Diagnostic: what HBM delivers to a plain sequential read on this device
- * ("5.1.1 · 从索引到 Kernel" §6.1: rates against what the hardware sustains).
- * Reads bytes (a multiple of 16) from src with `blocks` workgroups of 256
- * threads, grid-stride over 16-byte units (unit u is read by thread u mod
- * (256 blocks) of the grid), and writes the xor of the 32-bit words each
- * workgroup read to checksum[blocks].  Errors: bytes not a multiple of 16,
- * blocks < 1, null pointers -> STP_ERR_INVALID_ARG.
- */
-int stp_stream_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* checksum,
-                    hipStream_t stream);
-
-/*
  * ---- Dense paged attention with grouped query heads -------------------------
  * "PagedAttention 与 RadixAttention：上游机制与海光实现对照" §1.1 (decode
  * attention), §1.2 (block table), §1.4 part 4 (grouped query heads: the grid

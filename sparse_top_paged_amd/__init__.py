@@ -299,40 +299,6 @@ def splitkv_merge_normalized(o_norm, m_part, l_part, out=None, lse=None):
     return out, lse
 
 
-def row_gather(rows, row_ids, counts=None, parts=1, replicas=1, checksum=None):
-    """Diagnostic: read the candidate rows exactly as the decode splits and
-    places them, computing only an xor per workgroup.  rows: uint8
-    [num_rows, row_bytes] (or any 2-D contiguous tensor, taken as bytes);
-    row_ids [T, cap] int32.  Returns the uint32 checksums (as int32)."""
-    dev = rows.device
-    if rows.dim() != 2 or not rows.is_contiguous() or not rows.is_cuda:
-        raise ValueError("rows must be a contiguous 2-D device tensor")
-    T, cap = row_ids.shape
-    row_bytes = rows.shape[1] * rows.element_size()
-    nblk = lib.stp_row_gather_blocks(T, parts, replicas)
-    if checksum is None:
-        checksum = torch.empty((max(1, nblk),), dtype=torch.int32, device=dev)
-    check(lib.stp_row_gather(
-        rows.data_ptr(), rows.shape[0], row_bytes, _dev(row_ids, "row_ids", torch.int32, dev),
-        _opt(counts, "counts", torch.int32, dev), cap, T, parts, replicas,
-        _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
-    return checksum
-
-
-def stream_read(src, blocks=2048, checksum=None):
-    """Diagnostic: a plain sequential read of a contiguous device tensor (its
-    bytes, a multiple of 16) with `blocks` workgroups; returns the per-workgroup
-    xor checksums (as int32)."""
-    dev = src.device
-    if not src.is_cuda or not src.is_contiguous():
-        raise ValueError("src must be a contiguous device tensor")
-    if checksum is None:
-        checksum = torch.empty((blocks,), dtype=torch.int32, device=dev)
-    check(lib.stp_stream_read(src.data_ptr(), src.numel() * src.element_size(), blocks,
-                              _dev(checksum, "checksum", torch.int32, dev), _stream(dev)))
-    return checksum
-
-
 def _pool(k_pool, v_pool):
     if k_pool.dim() != 3 or k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must both be [slots, Hkv, head_dim]")

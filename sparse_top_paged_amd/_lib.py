@@ -60,9 +60,6 @@ SIGNATURES = {
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "stp_splitkv_merge": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "stp_splitkv_merge_normalized": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
-    "stp_row_gather": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
-    "stp_row_gather_blocks": (_i32, [_i32, _i32, _i32]),
-    "stp_stream_read": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
     "stp_paged_gqa_decode": (ctypes.c_int, [
         _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz,
         _p, _p, _p]),
@@ -75,19 +72,28 @@ SIGNATURES = {
 }
 
 
+# the measurement kernels of include/stp_diag.h (libstp_diag.so)
+DIAG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstp_diag.so")
+DIAG_SIGNATURES = {
+    "stp_row_gather": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "stp_row_gather_blocks": (_i32, [_i32, _i32, _i32]),
+    "stp_stream_read": (ctypes.c_int, [_p, _i64, _i32, _p, _p]),
+}
+
+
 class StpError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"stp status {status}: {message}")
         self.status = status
 
 
-def load(path=LIB_PATH):
+def load(path=LIB_PATH, signatures=None):
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build the HIP library first "
             "(python sparse_top_paged_amd/build.py or __graft_entry__.build())")
     lib = ctypes.CDLL(path)
-    for name, (res, args) in SIGNATURES.items():
+    for name, (res, args) in (SIGNATURES if signatures is None else signatures).items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args

@@ -3,7 +3,9 @@
     python sparse_top_paged_amd/build.py
 
 Compiles every csrc/*.hip with hipcc and links the shared library next to
-this file.  Always rebuilds.
+this file; csrc/diag.hip (the measurement kernels of include/stp_diag.h)
+goes into libstp_diag.so beside it, linked against libstp.so.  Always
+rebuilds.
 """
 
 import concurrent.futures
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libstp.so")
+DIAG_LIB = os.path.join(HERE, "libstp_diag.so")
+DIAG_SOURCES = {"diag.hip"}
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -57,19 +61,26 @@ def _compile(src):
     return obj
 
 
+def _link(objs, out, extra=()):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *extra, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link of {out} failed:\n{res.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose=True):
     os.makedirs(OBJ_DIR, exist_ok=True)
     sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    is_diag = [os.path.basename(src) in DIAG_SOURCES for src in sources]
+    _link([o for o, d in zip(objs, is_diag) if not d], LIB)
+    _link([o for o, d in zip(objs, is_diag) if d], DIAG_LIB,
+          [f"-L{HERE}", "-lstp", "-Wl,-rpath,$ORIGIN"])
     if verbose:
-        print(f"built {LIB} from {len(sources)} sources")
+        print(f"built {LIB} from {len(sources) - sum(is_diag)} sources and {DIAG_LIB}")
     return LIB
 
 

@@ -13,10 +13,12 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "stp.h")
 LIB = os.path.join(ROOT, "sparse_top_paged_amd", "libstp.so")
+DIAG_HEADER = os.path.join(ROOT, "include", "stp_diag.h")
+DIAG_LIB = os.path.join(ROOT, "sparse_top_paged_amd", "libstp_diag.so")
 
 
-def declared():
-    text = open(HEADER).read()
+def declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(stp_\w+)\s*\(", text)))
 
@@ -39,6 +41,29 @@ def test_library_exports_every_declared_symbol():
 def test_binding_declares_every_symbol():
     from sparse_top_paged_amd._lib import SIGNATURES
     assert sorted(SIGNATURES) == declared()
+
+
+def test_measurement_kernels_live_in_their_own_library():
+    """include/stp_diag.h's calls are exported by libstp_diag.so, declared by
+    the binding's diagnostic table, and absent from libstp.so."""
+    from sparse_top_paged_amd._lib import DIAG_SIGNATURES, STP_ERR_INVALID_ARG
+    from sparse_top_paged_amd import diag
+    names = declared(DIAG_HEADER)
+    assert names == sorted(DIAG_SIGNATURES) and "stp_row_gather" in names
+    assert not set(names) & set(declared())
+    dl = ctypes.CDLL(DIAG_LIB)
+    assert all(hasattr(dl, n) for n in names)
+    main = ctypes.CDLL(LIB)
+    assert not any(hasattr(main, n) for n in names)
+    # row size must be a multiple of 16, ranges must fit its id list
+    fake = ctypes.c_void_p(16)
+    g = diag.dlib.stp_row_gather
+    assert g(fake, 10, 1000, fake, None, 8, 1, 1, 1, fake, None) == STP_ERR_INVALID_ARG
+    assert g(fake, 10, 1152, fake, None, 8200, 1, 2, 1, fake, None) == STP_ERR_INVALID_ARG
+    assert g(fake, 10, 1152, fake, None, 8, 0, 1, 1, fake, None) == 0  # T = 0
+    assert diag.row_gather_blocks(32, 4, 2) == 256
+    assert diag.row_gather_blocks(33, 8, 1) == 320
+    assert diag.dlib.stp_stream_read(fake, 20, 4, fake, None) == STP_ERR_INVALID_ARG
 
 
 def test_host_side_validation():
@@ -101,12 +126,6 @@ def test_host_side_validation():
     assert stp.decode_workspace_bytes(1, 16, 44) == 0          # tiny shape runs unsplit
     assert stp.hot_lds_bytes(2180, 4096) > 0
     assert stp.hot_lds_bytes(40000, 32767) == 0
-    # row-gather diagnostic: row size must be a multiple of 16, ranges must fit its id list
-    assert lib.stp_row_gather(fake, 10, 1000, fake, None, 8, 1, 1, 1, fake, None) == STP_ERR_INVALID_ARG
-    assert lib.stp_row_gather(fake, 10, 1152, fake, None, 8200, 1, 2, 1, fake, None) == STP_ERR_INVALID_ARG
-    assert lib.stp_row_gather(fake, 10, 1152, fake, None, 8, 0, 1, 1, fake, None) == 0  # T = 0
-    assert lib.stp_row_gather_blocks(32, 4, 2) == 256
-    assert lib.stp_row_gather_blocks(33, 8, 1) == 320
     # dense paged attention: head_dim 128 only, whole groups of at most 16 (decode)
     # or 4 (extend) query heads per KV head, positive finite scale, page size >= 1
     dec = lib.stp_paged_gqa_decode

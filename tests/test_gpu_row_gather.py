@@ -38,16 +38,16 @@ def expected(rows_u32, ids, counts, parts, replicas, blocks, T):
 def test_row_gather_checksums(parts, replicas, row_bytes):
     # 1152 / 256 / 656-byte rows take the LDS ring (9 / 2 / 6 lines, the last
     # one partial for 656), 4096-byte rows the register pipeline
-    import sparse_top_paged_amd as stp
+    from sparse_top_paged_amd import diag
     rng = np.random.default_rng(11 + parts * 10 + replicas + row_bytes)
     num_rows, T, cap = 700, 11, 90
     rows = rng.integers(0, 256, size=(num_rows, row_bytes), dtype=np.uint8)
     ids = rng.integers(-1, num_rows + 20, size=(T, cap)).astype(np.int32)
     counts = rng.integers(0, cap + 1, size=T).astype(np.int32)
     counts[0] = cap
-    blocks = stp._lib.lib.stp_row_gather_blocks(T, parts, replicas)
+    blocks = diag.row_gather_blocks(T, parts, replicas)
     sentinel = torch.full((blocks,), 0x5A5A5A5A, dtype=torch.int32, device=dev())
-    stp.row_gather(to_dev(rows), to_dev(ids), to_dev(counts), parts, replicas, checksum=sentinel)
+    diag.row_gather(to_dev(rows), to_dev(ids), to_dev(counts), parts, replicas, checksum=sentinel)
     got = sentinel.cpu().numpy().view(np.uint32)
     exp = expected(rows.view(np.uint32), ids, counts, parts, replicas, blocks, T)
     for bid in range(blocks):
@@ -61,11 +61,11 @@ def test_row_gather_checksums(parts, replicas, row_bytes):
 def test_stream_read_checksums(n16, blocks):
     # unit u is read by thread u mod (256 blocks): workgroup b folds the units
     # whose residue lies in [256 b, 256 b + 256)
-    import sparse_top_paged_amd as stp
+    from sparse_top_paged_amd import diag
     rng = np.random.default_rng(n16 + blocks)
     words = rng.integers(0, 2 ** 32, size=(n16, 4), dtype=np.uint64).astype(np.uint32)
     src = to_dev(words.view(np.int32))
-    got = stp.stream_read(src, blocks).cpu().numpy().view(np.uint32)
+    got = diag.stream_read(src, blocks).cpu().numpy().view(np.uint32)
     unit_xor = np.bitwise_xor.reduce(words, axis=1)
     owner = (np.arange(n16) % (256 * blocks)) // 256
     for b in range(blocks):
