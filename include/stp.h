@@ -119,9 +119,11 @@ int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req
  * stp_normalize_indices_deferred takes the arguments of stp_normalize_indices
  * and writes everything but the block view's logical / page / mask arrays;
  * blk_indptr then holds per-token intermediate values.  stp_block_view_fill,
- * enqueued after it with the same tok_out, count_out, req_id, q_pos,
+ * enqueued after it with the same tok_out, slot_out, req_id, q_pos,
  * block_table, sizes and block-view arrays, completes the view; until it has
- * run, blk_indptr is not the CSR index.  The pair's results equal one
+ * run, blk_indptr is not the CSR index.  It takes each block's page from the
+ * slot ids (slot / page_size) and reads the page table only when the
+ * per-token bitmap and pages do not fit in LDS.  The pair's results equal one
  * stp_normalize_indices call.  A second fill over arrays it has already
  * completed changes nothing (tokens whose entry is final are skipped); run
  * it once per deferred normalisation.  Errors as stp_normalize_indices.
@@ -134,7 +136,7 @@ int stp_normalize_indices_deferred(const int32_t* topk, int32_t top_k, const int
                                    int32_t* dropped_out, int32_t* blk_indptr,
                                    int32_t* blk_logical, int32_t* blk_page, uint64_t* blk_mask,
                                    hipStream_t stream);
-int stp_block_view_fill(const int32_t* tok_out, const int32_t* count_out, const int32_t* req_id,
+int stp_block_view_fill(const int32_t* tok_out, const int32_t* slot_out, const int32_t* req_id,
                         const int32_t* q_pos, int32_t T, const int32_t* block_table,
                         int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t cap,
                         int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
@@ -418,6 +420,31 @@ int stp_splitkv_merge(const float* o_part, const float* m_part, const float* l_p
 int stp_splitkv_merge_normalized(const uint16_t* o_norm, const float* m_part,
                                  const float* l_part, int32_t T, int32_t S, int32_t H, int32_t dv,
                                  uint16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * stp_splitkv_merge_normalized and stp_block_view_fill of the same T tokens
+ * in one call.  Both run after the decode and neither reads the other's
+ * output ("5.1.1 · 从索引到 Kernel" §4.2 eq. (10): the index stage's time is
+ * part of every step), so when the merge's slices are 16 bytes wide
+ * (dv % 8 == 0, S <= 8) and the block view's per-token LDS (the position
+ * bitmap, 8 * ceil(max_blocks * page_size / 64) bytes, and the blocks'
+ * pages, 4 * max_blocks bytes) fits in 64 KiB, a single launch carries both: the
+ * first T workgroups complete the block view, the others merge.  Otherwise
+ * the call enqueues the fill and then the merge.  The results are those of
+ * the two calls.  Arguments, layouts, requirements and errors are those of
+ * the two calls (the block-view arrays as left by
+ * stp_normalize_indices_deferred); T counts both the merge's tokens and the
+ * normalised tokens.
+ */
+int stp_splitkv_merge_with_block_view(const uint16_t* o_norm, const float* m_part,
+                                      const float* l_part, int32_t T, int32_t S, int32_t H,
+                                      int32_t dv, uint16_t* out, float* lse,
+                                      const int32_t* tok_out, const int32_t* slot_out,
+                                      const int32_t* req_id, const int32_t* q_pos,
+                                      const int32_t* block_table, int32_t num_reqs,
+                                      int32_t max_blocks, int32_t page_size, int32_t cap,
+                                      int32_t* blk_indptr, int32_t* blk_logical,
+                                      int32_t* blk_page, uint64_t* blk_mask, hipStream_t stream);
 
 /*
  * ---- Dense paged attention with grouped query heads -------------------------

@@ -17,8 +17,8 @@ __all__ = [
     "StpError", "version", "normalize_indices", "block_view_fill", "hot_lookup_swapin", "hot_reset", "backup_rows",
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
-    "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer", "row_gather",
-    "stream_read",
+    "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer",
+    "splitkv_merge_with_block_view",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
     "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
     "decode_fp8_workspace_bytes", "decode_plan", "decode_run", "decode_plan_bytes",
@@ -109,7 +109,7 @@ def block_view_fill(norm, req_id, q_pos, block_table, page_size):
     T, cap = norm["tok"].shape
     num_reqs, max_blocks = block_table.shape
     check(lib.stp_block_view_fill(
-        _dev(norm["tok"], "tok", torch.int32, dev), _dev(norm["count"], "count", torch.int32, dev),
+        _dev(norm["tok"], "tok", torch.int32, dev), _dev(norm["slot"], "slot", torch.int32, dev),
         _dev(req_id, "req_id", torch.int32, dev), _dev(q_pos, "q_pos", torch.int32, dev), T,
         _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size, cap,
         _dev(norm["blk_indptr"], "blk_indptr", torch.int32, dev),
@@ -298,6 +298,34 @@ def splitkv_merge_normalized(o_norm, m_part, l_part, out=None, lse=None):
         _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev), _stream(dev)))
     return out, lse
 
+
+
+def splitkv_merge_with_block_view(o_norm, m_part, l_part, norm, req_id, q_pos, block_table,
+                                  page_size, out=None, lse=None):
+    """splitkv_merge_normalized and block_view_fill of the same tokens in one
+    call (norm: the dict of normalize_indices(..., defer_block_view=True))."""
+    dev = o_norm.device
+    T, S, H, dv = o_norm.shape
+    Tn, cap = norm["tok"].shape
+    if Tn != T:
+        raise ValueError("the merge and the normalisation must cover the same tokens")
+    num_reqs, max_blocks = block_table.shape
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    check(lib.stp_splitkv_merge_with_block_view(
+        _dev(o_norm, "o_norm", torch.bfloat16, dev), _dev(m_part, "m_part", torch.float32, dev),
+        _dev(l_part, "l_part", torch.float32, dev), T, S, H, dv,
+        _dev(out, "out", torch.bfloat16, dev), _opt(lse, "lse", torch.float32, dev),
+        _dev(norm["tok"], "tok", torch.int32, dev), _dev(norm["slot"], "slot", torch.int32, dev),
+        _dev(req_id, "req_id", torch.int32, dev), _dev(q_pos, "q_pos", torch.int32, dev),
+        _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size, cap,
+        _dev(norm["blk_indptr"], "blk_indptr", torch.int32, dev),
+        _dev(norm["blk_logical"], "blk_logical", torch.int32, dev),
+        _dev(norm["blk_page"], "blk_page", torch.int32, dev),
+        _dev(norm["blk_mask"], "blk_mask", torch.int64, dev), _stream(dev)))
+    return out, lse
 
 def _pool(k_pool, v_pool):
     if k_pool.dim() != 3 or k_pool.shape != v_pool.shape:

@@ -13,6 +13,7 @@
 // decode's) covers four heads per workgroup with 16-byte slices, every load
 // issued before the first use.
 
+#include "block_view.h"
 #include "stp_internal.h"
 
 namespace {
@@ -191,14 +192,14 @@ __device__ __forceinline__ void merge_norm_wide(const uint16_t* __restrict__ o_n
   if (lse && c0 == 0) lse[(int64_t)t * H + h] = M + logf(L);
 }
 
-__global__ __launch_bounds__(kThreads) void splitkv_merge_norm_wide_kernel(
-    const uint16_t* __restrict__ o_norm, const float* __restrict__ m_part,
-    const float* __restrict__ l_part, int S, int H, int dv, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
-  const int t = blockIdx.x;
-  const int h = blockIdx.y * (kThreads / kPerHeadWide) + (threadIdx.x / kPerHeadWide);
-  const int c0 = (threadIdx.x % kPerHeadWide) * 8;
-  if (h >= H || c0 >= dv) return;
+// merge_norm_wide for a run-time S in [1, 8] (thread: head h of token t,
+// values c0 .. c0 + 7 of every 512).
+__device__ __forceinline__ void merge_norm_wide_any(const uint16_t* __restrict__ o_norm,
+                                                    const float* __restrict__ m_part,
+                                                    const float* __restrict__ l_part, int S,
+                                                    int t, int h, int H, int dv, int c0,
+                                                    uint16_t* __restrict__ out,
+                                                    float* __restrict__ lse) {
   uint16_t* orow = out + ((int64_t)t * H + h) * dv;
   switch (S) {
     case 1: return merge_norm_wide<1>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
@@ -211,6 +212,48 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_norm_wide_kernel(
     case 8: return merge_norm_wide<8>(o_norm, m_part, l_part, t, h, H, dv, c0, orow, lse);
     default: return;
   }
+}
+
+__global__ __launch_bounds__(kThreads) void splitkv_merge_norm_wide_kernel(
+    const uint16_t* __restrict__ o_norm, const float* __restrict__ m_part,
+    const float* __restrict__ l_part, int S, int H, int dv, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int h = blockIdx.y * (kThreads / kPerHeadWide) + (threadIdx.x / kPerHeadWide);
+  const int c0 = (threadIdx.x % kPerHeadWide) * 8;
+  if (h >= H || c0 >= dv) return;
+  merge_norm_wide_any(o_norm, m_part, l_part, S, blockIdx.x, h, H, dv, c0, out, lse);
+}
+
+// The wide merge and the block-view pass of the same step in one launch.
+// Both follow the decode and neither reads the other's output, so one launch
+// pays one ramp and one drain for both.  Workgroups [0, T) run the block-view
+// pass of token blockIdx.x; they come first so that their longer chains of
+// dependent round trips start first.  Every later workgroup merges 16 heads
+// of one token, 64 threads per head as in the wide merge.
+constexpr int kMergeHeadsBv = stp::bv::kFThreads / kPerHeadWide;
+
+// One instantiation per split count: the registers of the largest merge
+// would otherwise set the occupancy of every launch.
+template <int S>
+__global__ __launch_bounds__(stp::bv::kFThreads) void merge_block_view_kernel(
+    stp::bv::FillArgs fa, int T, const uint16_t* __restrict__ o_norm,
+    const float* __restrict__ m_part, const float* __restrict__ l_part, int H, int dv,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  extern __shared__ uint64_t bitmap[];
+  __shared__ int s_red[stp::bv::kFWaves];
+  __shared__ int s_scan[stp::bv::kFWaves];
+  const int b = blockIdx.x;
+  if (b < T) {
+    stp::bv::block_fill_token<true>(fa, b, bitmap, s_red, s_scan);
+    return;
+  }
+  const int hblocks = (H + kMergeHeadsBv - 1) / kMergeHeadsBv;
+  const int t = (b - T) / hblocks;
+  const int h = ((b - T) % hblocks) * kMergeHeadsBv + threadIdx.x / kPerHeadWide;
+  const int c0 = (threadIdx.x % kPerHeadWide) * 8;
+  if (h >= H || c0 >= dv) return;
+  merge_norm_wide<S>(o_norm, m_part, l_part, t, h, H, dv, c0, out + ((int64_t)t * H + h) * dv,
+                     lse);
 }
 
 __global__ __launch_bounds__(kThreads) void splitkv_merge_norm_kernel(
@@ -289,6 +332,43 @@ int launch_merge_normalized(const uint16_t* o_norm, const float* m_part, const f
   return check_launch("splitkv_merge_norm_kernel");
 }
 
+int launch_merge_block_view(const uint16_t* o_norm, const float* m_part, const float* l_part,
+                            int T, int S, int H, int dv, uint16_t* out, float* lse,
+                            const BlockViewPass& bvp, hipStream_t stream) {
+  const int nwords = max(1, (int)(((int64_t)bvp.max_blocks * bvp.page_size + 63) / 64));
+  const size_t lds = (size_t)nwords * sizeof(uint64_t) + (size_t)bvp.max_blocks * 4;
+  // one launch when the wide merge applies and the bitmap and the blocks'
+  // pages fit the default dynamic LDS; otherwise the two launches one after
+  // the other
+  if (!(dv % 8 == 0 && S <= 8 && lds <= 64 * 1024)) {
+    if (int rc = launch_block_fill(bvp, T, stream)) return rc;
+    return launch_merge_normalized(o_norm, m_part, l_part, T, S, H, dv, out, lse, stream);
+  }
+  const int num_reqs = (bvp.num_reqs == 0 || bvp.max_blocks == 0) ? 0 : bvp.num_reqs;
+  const uint64_t pdiv = ((1ull << 32) + (uint64_t)bvp.page_size - 1) / (uint64_t)bvp.page_size;
+  bv::FillArgs fa{bvp.tok_out, bvp.slot_out, bvp.req_id, bvp.q_pos, bvp.block_table, num_reqs,
+                  bvp.max_blocks, bvp.page_size, bvp.cap, pdiv, nwords, bvp.blk_indptr,
+                  bvp.blk_logical, bvp.blk_page, bvp.blk_mask};
+  const int hblocks = (H + kMergeHeadsBv - 1) / kMergeHeadsBv;
+  const int64_t grid = (int64_t)T + (int64_t)T * hblocks;
+  if (grid > INT32_MAX) return fail(STP_ERR_INVALID_ARG, "merge_block_view: grid too large");
+  auto go = [&](auto s) {
+    merge_block_view_kernel<decltype(s)::value><<<(unsigned)grid, bv::kFThreads, lds, stream>>>(
+        fa, T, o_norm, m_part, l_part, H, dv, out, lse);
+  };
+  switch (S) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    case 7: go(std::integral_constant<int, 7>{}); break;
+    default: go(std::integral_constant<int, 8>{}); break;
+  }
+  return check_launch("merge_block_view_kernel");
+}
+
 int launch_merge(const float* o_part, const float* m_part, const float* l_part, int T, int S,
                  int H, int dv, uint16_t* out, float* lse, hipStream_t stream) {
   dim3 grid(T, (H + 1) / 2);
@@ -324,4 +404,31 @@ extern "C" int stp_splitkv_merge_normalized(const uint16_t* o_norm, const float*
   if (!o_norm || !m_part || !l_part || !out)
     return fail(STP_ERR_INVALID_ARG, "splitkv_merge_normalized: null pointer");
   return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, dv, out, lse, stream);
+}
+
+extern "C" int stp_splitkv_merge_with_block_view(
+    const uint16_t* o_norm, const float* m_part, const float* l_part, int32_t T, int32_t S,
+    int32_t H, int32_t dv, uint16_t* out, float* lse, const int32_t* tok_out,
+    const int32_t* slot_out, const int32_t* req_id, const int32_t* q_pos,
+    const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+    int32_t cap, int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+    uint64_t* blk_mask, hipStream_t stream) {
+  using stp::fail;
+  if (T < 0 || S < 1 || H < 1 || dv < 1 || dv % 4 != 0)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge_with_block_view: bad sizes T=%d S=%d H=%d dv=%d",
+                T, S, H, dv);
+  if (H > 2 * 65535)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge_with_block_view: H %d too large", H);
+  if (int rc = stp::check_block_view_args("splitkv_merge_with_block_view", tok_out, slot_out,
+                                          req_id, q_pos, T, block_table, num_reqs, max_blocks,
+                                          page_size, cap, blk_indptr, blk_logical, blk_page,
+                                          blk_mask))
+    return rc;
+  if (T == 0) return STP_OK;
+  if (!o_norm || !m_part || !l_part || !out)
+    return fail(STP_ERR_INVALID_ARG, "splitkv_merge_with_block_view: null pointer");
+  const stp::BlockViewPass bvp{tok_out,    slot_out,   req_id,      q_pos,    block_table,
+                               num_reqs,   max_blocks, page_size,   cap,      blk_indptr,
+                               blk_logical, blk_page,  blk_mask};
+  return stp::launch_merge_block_view(o_norm, m_part, l_part, T, S, H, dv, out, lse, bvp, stream);
 }

@@ -10,7 +10,7 @@
 // the kernels are built to keep the chain of dependent memory round trips
 // short rather than to stream bytes.
 //
-// normalize_kernel: one 256-thread workgroup per query token holds a bitmap
+// normalize_kernel: one 1024-thread workgroup per query token holds a bitmap
 // of the token's visible positions in LDS (plus the request's page-table row
 // when it fits).  The token's D entries are loaded before anything else (they
 // do not depend on the request), then D, W and A set bits with LDS atomicOr
@@ -20,18 +20,18 @@
 // their own lane, dense ones (the window) by the whole wave, one lane per
 // bit.  Block division uses a precomputed 2^32 / P multiplier.
 //
-// block_fill_kernel (block view only): one workgroup per token rebuilds the
-// token's bitmap from its sorted S, derives the touched blocks and their
-// in-page masks, and writes them at the token's CSR offset.  The offset is a
-// prefix over the other tokens' block counts; the first kernel stores each
-// count as -(count + 1) in blk_indptr[i + 1] and this kernel replaces it by
-// the inclusive prefix, so a workgroup reading its predecessors sees, for
-// each, either the raw count or an inclusive prefix that ends the look-back.
-// Both are valid whatever the order of the workgroups, so nothing waits.
+// block_fill_kernel (block view only): one workgroup per token runs the
+// block-view pass (block_view.h): the token's CSR offset by a wait-free
+// look-back over the counts the first kernel left in blk_indptr, then its
+// touched blocks, their pages and in-page masks from a bitmap rebuilt out of
+// the token's sorted S and slot ids.
 
+#include "block_view.h"
 #include "stp_internal.h"
 
 namespace {
+
+using namespace stp::bv;
 
 constexpr int kMaxPositions = 1 << 20;     // bitmap of 128 KiB LDS
 constexpr int kLdsBudget = 150 * 1024;     // dynamic LDS a workgroup may use
@@ -42,9 +42,6 @@ constexpr int kDenseWord = 8;              // words with more bits go wave-wide
 constexpr int kNThreads = STP_NORM_THREADS;  // normalize_kernel's workgroup
 constexpr int kNWaves = kNThreads / 64;
 constexpr int kNDPer = kNThreads >= 1024 ? 2 : (kNThreads >= 512 ? 4 : 8);  // D entries per thread
-constexpr int kFThreads = 1024;            // block_fill_kernel's workgroup
-constexpr int kFWaves = kFThreads / 64;
-constexpr int kFDPer = 2;                  // entries of S per thread in flight
 
 struct NormArgs {
   const int32_t* topk;
@@ -61,32 +58,6 @@ struct NormArgs {
   int32_t* dropped_out;
   int32_t* blk_indptr;  // nullable; receives -(block count + 1) per token
 };
-
-__device__ __forceinline__ int div_p(int t, uint64_t pdiv) {
-  return (int)(((uint64_t)(uint32_t)t * pdiv) >> 32);
-}
-
-// Bits of positions [lo, hi) (0 < hi - lo <= 64) taken from the bitmap.
-__device__ __forceinline__ uint64_t bits_in_range(const uint64_t* bm, int lo, int hi) {
-  const int w0 = lo >> 6, w1 = (hi - 1) >> 6;
-  const int a = lo & 63;
-  uint64_t acc = bm[w0] >> a;
-  if (w1 != w0) acc |= bm[w1] << (64 - a);
-  const int n = hi - lo;
-  return n == 64 ? acc : (acc & ((1ull << n) - 1));
-}
-
-template <int kW>
-__device__ __forceinline__ int block_sum(int v, int* scratch) {
-  v = stp::wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int s = 0;
-#pragma unroll
-  for (int w = 0; w < kW; ++w) s += scratch[w];
-  return s;
-}
 
 // LDS of normalize_kernel: the bitmap (nwords_alloc words), then the
 // request's page-table row (kTableLds), then the emitted list S (kListLds).
@@ -330,144 +301,12 @@ __global__ __launch_bounds__(kNThreads) void normalize_kernel(NormArgs a) {
   }
 }
 
-struct FillArgs {
-  const int32_t* tok_out;
-  const int32_t* count_out;
-  const int32_t* req_id;
-  const int32_t* q_pos;
-  const int32_t* block_table;
-  int num_reqs, max_blocks, P, cap;
-  uint64_t pdiv;
-  int nwords_alloc;  // bitmap words; the staged table row follows them in LDS
-  int32_t* blk_indptr;
-  int32_t* blk_logical;
-  int32_t* blk_page;
-  uint64_t* blk_mask;
-};
-
-// Per token: CSR offset by look-back, then the touched blocks from a bitmap
-// rebuilt out of the token's sorted S.  The request's page-table row is
-// staged in LDS (after the bitmap) while the look-back runs, when it fits.
-template <bool kTableLds>
+template <bool kPageLds>
 __global__ __launch_bounds__(kFThreads) void block_fill_kernel(FillArgs a) {
   extern __shared__ uint64_t bitmap[];
   __shared__ int s_red[kFWaves];
   __shared__ int s_scan[kFWaves];
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x;
-
-  // written as -(count + 1) by the normalisation; only this workgroup turns it
-  // into the inclusive prefix, so a value >= 0 means this token's view is
-  // already complete (a repeated fill over the same arrays): nothing to do
-  const int raw = a.blk_indptr[i + 1];
-  if (raw >= 0) return;
-  const int own = -raw - 1;
-  const int n = a.count_out[i];
-  const int r = a.req_id[i];
-  const int q = a.q_pos[i];
-  const bool pad = r < 0 || r >= a.num_reqs || q < 0;
-  const int32_t* tok = a.tok_out + (int64_t)i * a.cap;
-  // the token's first entries of S and its table row, loaded while the
-  // look-back runs
-  int tv[kFDPer];
-#pragma unroll
-  for (int u = 0; u < kFDPer; ++u) {
-    const int j = tid + u * kFThreads;
-    tv[u] = j < n ? tok[j] : -1;
-  }
-  const int P = a.P;
-  const int limit = pad ? 0 : min(q, a.max_blocks * P - 1);
-  const int nwords = (limit >> 6) + 1;
-  const int used_blocks = div_p(limit, a.pdiv) + 1;
-  const int32_t* g_table = a.block_table + (int64_t)(pad ? 0 : r) * a.max_blocks;
-  int32_t* l_table = (int32_t*)(bitmap + a.nwords_alloc);
-  // the first look-back window's entries (tokens i-1 .. i-kFThreads; never
-  // this token's own entry), in flight with the loads above
-  const int k_first = i - 1 - tid;
-  const int v_first = k_first >= 0 ? a.blk_indptr[k_first + 1] : -1;
-  if (kTableLds && !pad && own > 0) {
-    for (int b0 = 0; b0 < used_blocks; b0 += 2 * kFThreads) {
-      int pv[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int b = b0 + tid + u * kFThreads;
-        pv[u] = b < used_blocks ? g_table[b] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int b = b0 + tid + u * kFThreads;
-        if (b < used_blocks) l_table[b] = pv[u];
-      }
-    }
-  }
-  __syncthreads();  // every thread has its `own` before thread 0 rewrites the entry
-
-  // Look-back over tokens i-1, i-2, ...: raw counts until an inclusive prefix.
-  int prefix = 0;
-  for (int hi = i; hi > 0; hi -= kFThreads) {
-    const int k = hi - 1 - tid;  // token index this thread reads
-    const int v = hi == i ? v_first : (k >= 0 ? a.blk_indptr[k + 1] : -1);
-    // the newest (largest k) inclusive prefix in this window, if any
-    const int kp = (k >= 0 && v >= 0) ? k : -1;
-    // (an LDS atomic max over the workgroup)
-    __syncthreads();
-    if (tid == 0) s_red[0] = -1;
-    __syncthreads();
-    if (kp >= 0) atomicMax(&s_red[0], kp);
-    __syncthreads();
-    const int kstar = s_red[0];
-    int contrib = 0;
-    if (k >= 0 && k > kstar) contrib = -v - 1;  // raw count after the newest prefix
-    if (k >= 0 && k == kstar) contrib = v;      // the prefix itself
-    prefix += block_sum<kFWaves>(contrib, s_red);
-    if (kstar >= 0) break;
-  }
-
-  if (tid == 0) {
-    if (i == 0) a.blk_indptr[0] = 0;
-    a.blk_indptr[i + 1] = prefix + own;
-  }
-  if (own == 0 || pad) return;
-
-  const int32_t* table = kTableLds ? l_table : g_table;
-  for (int w = tid; w < nwords; w += kFThreads) bitmap[w] = 0;
-  __syncthreads();
-  auto set_bits = [&](const int (&v)[kFDPer]) {
-#pragma unroll
-    for (int u = 0; u < kFDPer; ++u)
-      if (v[u] >= 0) atomicOr((unsigned long long*)&bitmap[v[u] >> 6], 1ull << (v[u] & 63));
-  };
-  set_bits(tv);
-  for (int j0 = kFDPer * kFThreads; j0 < n; j0 += kFDPer * kFThreads) {
-#pragma unroll
-    for (int u = 0; u < kFDPer; ++u) {
-      const int j = j0 + tid + u * kFThreads;
-      tv[u] = j < n ? tok[j] : -1;
-    }
-    set_bits(tv);
-  }
-  __syncthreads();
-
-  // Blocks in chunks of kFThreads, one per thread: in-page mask, page,
-  // position by a block-wide scan of the flags.
-  int k0 = prefix;
-  for (int c0 = 0; c0 < used_blocks; c0 += kFThreads) {
-    const int b = c0 + tid;
-    uint64_t m = 0;
-    if (b < used_blocks) {
-      const int lo = b * P, hi = min(lo + P, limit + 1);
-      m = bits_in_range(bitmap, lo, hi);
-    }
-    const int page = m ? table[b] : 0;
-    int tot;
-    const int k = k0 + stp::block_exclusive_scan<kFWaves>(m ? 1 : 0, s_scan, &tot);
-    if (m) {
-      a.blk_logical[k] = b;
-      a.blk_page[k] = page;
-      a.blk_mask[k] = m;
-    }
-    k0 += tot;
-  }
+  block_fill_token<kPageLds>(a, blockIdx.x, bitmap, s_red, s_scan);
 }
 
 // Dynamic LDS above the default limit for every kernel of this file, once.
@@ -496,27 +335,47 @@ int set_lds_attrs() {
   return STP_OK;
 }
 
-// The block-view pass of a normalisation whose counts are in blk_indptr.
-int launch_block_fill(const int32_t* tok_out, const int32_t* count_out, const int32_t* req_id,
-                      const int32_t* q_pos, int32_t T, const int32_t* block_table,
-                      int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t cap,
-                      int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
-                      uint64_t* blk_mask, hipStream_t stream) {
-  if (num_reqs == 0 || max_blocks == 0) num_reqs = 0;  // every token is a padding row
-  const int nwords = max(1, (int)(((int64_t)max_blocks * page_size + 63) / 64));
+}  // namespace
+
+namespace stp {
+
+int launch_block_fill(const BlockViewPass& p, int32_t T, hipStream_t stream) {
+  if (int rc = set_lds_attrs()) return rc;
+  // no request with a mapped page: every token is a padding row
+  const int num_reqs = (p.num_reqs == 0 || p.max_blocks == 0) ? 0 : p.num_reqs;
+  const int nwords = max(1, (int)(((int64_t)p.max_blocks * p.page_size + 63) / 64));
   const size_t bitmap_bytes = (size_t)nwords * sizeof(uint64_t);
-  const bool table_in_lds = bitmap_bytes + (size_t)max_blocks * 4 <= (size_t)kLdsBudget;
-  const uint64_t pdiv = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
-  FillArgs fa{tok_out, count_out, req_id, q_pos, block_table, num_reqs, max_blocks, page_size,
-              cap, pdiv, nwords, blk_indptr, blk_logical, blk_page, blk_mask};
-  if (table_in_lds)
-    block_fill_kernel<true><<<T, kFThreads, bitmap_bytes + (size_t)max_blocks * 4, stream>>>(fa);
+  const bool pages_in_lds = bitmap_bytes + (size_t)p.max_blocks * 4 <= (size_t)kLdsBudget;
+  const uint64_t pdiv = ((1ull << 32) + (uint64_t)p.page_size - 1) / (uint64_t)p.page_size;
+  FillArgs fa{p.tok_out, p.slot_out, p.req_id, p.q_pos, p.block_table, num_reqs,
+              p.max_blocks, p.page_size, p.cap, pdiv, nwords, p.blk_indptr, p.blk_logical,
+              p.blk_page, p.blk_mask};
+  if (pages_in_lds)
+    block_fill_kernel<true><<<T, kFThreads, bitmap_bytes + (size_t)p.max_blocks * 4, stream>>>(fa);
   else
     block_fill_kernel<false><<<T, kFThreads, bitmap_bytes, stream>>>(fa);
-  return stp::check_launch("block_fill_kernel");
+  return check_launch("block_fill_kernel");
 }
 
-}  // namespace
+int check_block_view_args(const char* what, const int32_t* tok_out, const int32_t* slot_out,
+                          const int32_t* req_id, const int32_t* q_pos, int32_t T,
+                          const int32_t* block_table, int32_t num_reqs, int32_t max_blocks,
+                          int32_t page_size, int32_t cap, int32_t* blk_indptr,
+                          int32_t* blk_logical, int32_t* blk_page, uint64_t* blk_mask) {
+  if (T < 0 || num_reqs < 0 || max_blocks < 0 || cap < 0)
+    return fail(STP_ERR_INVALID_ARG, "%s: negative size", what);
+  if (page_size < 1 || page_size > 64)
+    return fail(STP_ERR_INVALID_ARG, "%s: page_size %d not in [1, 64]", what, page_size);
+  if ((int64_t)max_blocks * page_size > kMaxPositions)
+    return fail(STP_ERR_INVALID_ARG, "%s: max_blocks * page_size too large", what);
+  if (T == 0) return STP_OK;
+  if (!tok_out || !slot_out || !req_id || !q_pos || !blk_indptr || !blk_logical || !blk_page ||
+      !blk_mask || (num_reqs > 0 && max_blocks > 0 && !block_table))
+    return fail(STP_ERR_INVALID_ARG, "%s: null pointer", what);
+  return STP_OK;
+}
+
+}  // namespace stp
 
 static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req_id,
                           const int32_t* q_pos, int32_t T, const int32_t* block_table,
@@ -571,9 +430,10 @@ static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req
     normalize_kernel<false, false><<<T, kNThreads, lds, stream>>>(na);
   if (int rc = stp::check_launch("normalize_kernel")) return rc;
   if (blk_indptr && !defer_fill)
-    return launch_block_fill(tok_out, count_out, req_id, q_pos, T, block_table, num_reqs,
-                             max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
-                             blk_mask, stream);
+    return stp::launch_block_fill({tok_out, slot_out, req_id, q_pos, block_table, num_reqs,
+                                   max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
+                                   blk_mask},
+                                  T, stream);
   return STP_OK;
 }
 
@@ -601,25 +461,19 @@ extern "C" int stp_normalize_indices_deferred(
                         dropped_out, blk_indptr, blk_logical, blk_page, blk_mask, stream, true);
 }
 
-extern "C" int stp_block_view_fill(const int32_t* tok_out, const int32_t* count_out,
+extern "C" int stp_block_view_fill(const int32_t* tok_out, const int32_t* slot_out,
                                    const int32_t* req_id, const int32_t* q_pos, int32_t T,
                                    const int32_t* block_table, int32_t num_reqs,
                                    int32_t max_blocks, int32_t page_size, int32_t cap,
                                    int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
                                    uint64_t* blk_mask, hipStream_t stream) {
-  using stp::fail;
-  if (T < 0 || num_reqs < 0 || max_blocks < 0 || cap < 0)
-    return fail(STP_ERR_INVALID_ARG, "block_view_fill: negative size");
-  if (page_size < 1 || page_size > 64)
-    return fail(STP_ERR_INVALID_ARG, "block_view_fill: page_size %d not in [1, 64]", page_size);
-  if ((int64_t)max_blocks * page_size > kMaxPositions)
-    return fail(STP_ERR_INVALID_ARG, "block_view_fill: max_blocks * page_size too large");
+  if (int rc = stp::check_block_view_args("block_view_fill", tok_out, slot_out, req_id, q_pos, T,
+                                          block_table, num_reqs, max_blocks, page_size, cap,
+                                          blk_indptr, blk_logical, blk_page, blk_mask))
+    return rc;
   if (T == 0) return STP_OK;
-  if (!tok_out || !count_out || !req_id || !q_pos || !blk_indptr || !blk_logical || !blk_page ||
-      !blk_mask || (num_reqs > 0 && max_blocks > 0 && !block_table))
-    return fail(STP_ERR_INVALID_ARG, "block_view_fill: null pointer");
-  if (int rc = set_lds_attrs()) return rc;
-  return launch_block_fill(tok_out, count_out, req_id, q_pos, T, block_table, num_reqs,
-                           max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
-                           blk_mask, stream);
+  return stp::launch_block_fill({tok_out, slot_out, req_id, q_pos, block_table, num_reqs,
+                                 max_blocks, page_size, cap, blk_indptr, blk_logical, blk_page,
+                                 blk_mask},
+                                T, stream);
 }

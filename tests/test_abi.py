@@ -91,6 +91,21 @@ def test_host_side_validation():
     assert fill(None, None, None, None, 1, None, 0, 0, 16, 4, None, None, None, None, None) == STP_ERR_INVALID_ARG
     assert b"null pointer" in lib.stp_last_error()
     assert fill(None, None, None, None, 0, None, 0, 0, 16, 4, None, None, None, None, None) == 0
+    # the merge and the block view in one call: both sets of checks before any launch
+    mbv = lib.stp_splitkv_merge_with_block_view
+    fake = ctypes.c_void_p(16)
+    assert mbv(fake, fake, fake, 2, 0, 4, 512, fake, None, fake, fake, fake, fake, fake, 1, 4, 16,
+               8, fake, fake, fake, fake, None) == STP_ERR_INVALID_ARG
+    assert mbv(fake, fake, fake, 2, 2, 4, 512, fake, None, fake, fake, fake, fake, fake, 1, 4, 65,
+               8, fake, fake, fake, fake, None) == STP_ERR_INVALID_ARG
+    assert b"page_size" in lib.stp_last_error()
+    assert mbv(fake, fake, fake, 2, 2, 4, 512, fake, None, fake, fake, fake, fake, fake, 1, 4, 16,
+               8, None, fake, fake, fake, None) == STP_ERR_INVALID_ARG
+    assert b"null pointer" in lib.stp_last_error()
+    assert mbv(None, fake, fake, 2, 2, 4, 512, fake, None, fake, fake, fake, fake, fake, 1, 4, 16,
+               8, fake, fake, fake, fake, None) == STP_ERR_INVALID_ARG
+    assert mbv(None, None, None, 0, 2, 4, 512, None, None, None, None, None, None, None, 0, 0, 16,
+               8, None, None, None, None, None) == 0  # T = 0
     # 16-byte row rule of the hot buffer (656 passes, 1000 fails)
     assert lib.stp_hot_lookup_swapin(None, 0, None, 1000, None, 0, None, None, None, 16, 17, 0, 0,
                                      None, None, None, None) == STP_ERR_INVALID_ARG
