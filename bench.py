@@ -1142,8 +1142,9 @@ def main():
     S = stp.decode_splits(T, H, cap, args.splits)
     norm = [stp.normalize_indices(tk, req, qpos, table, c0.page_size, c0.window, c0.num_sinks,
                                   cap) for tk in topks]
-    # the split path of stp_sparse_mla_decode, called stage by stage so that the
-    # decode kernel can be timed on its own: normalised bf16 partials + merge
+    # the split path of stp_normalize_and_decode, called stage by stage so
+    # that its decode launch can be timed on its own: normalised bf16
+    # partials, then the merge
     o_norm = torch.empty((T, S, H, 512), dtype=torch.bfloat16, device=dev)
     m_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
     l_part = torch.empty((T, S, H), dtype=torch.float32, device=dev)
@@ -1152,25 +1153,33 @@ def main():
     torch.cuda.synchronize()
     counts = [n["count"].cpu().numpy().astype(np.int64) for n in norm]
 
-    # One step: the normalisation (its block view deferred when there is a
-    # merge), the decode, then the merge and the block view in one launch.
+    # One step: the normalisation inside the decode launch (block view
+    # deferred), then the merge and the block view in one launch; a single
+    # pass completes the block view in a launch of its own.
+    def fused(k):
+        if S > 1:
+            return stp.normalize_and_decode_partial_normalized(
+                topks[k], req, qpos, table, c0.page_size, c0.window, c0.num_sinks, q, kv,
+                c0.scale, S, o_norm, m_part, l_part, cap, norm=norm[k])
+        stp.normalize_and_decode(topks[k], req, qpos, table, c0.page_size, c0.window,
+                                 c0.num_sinks, q, kv, c0.scale, 1, cap, norm=norm_lists[k],
+                                 out=out, lse=lse)
+        return norm[k]
+
+    norm_lists = [{key: nb[key] for key in ("tok", "slot", "count", "dropped")} for nb in norm]
+
     def step(i, ev=None):
         k = i % args.sets
-        nb = stp.normalize_indices(topks[k], req, qpos, table, c0.page_size, c0.window,
-                                   c0.num_sinks, cap, out=norm[k], defer_block_view=S > 1)
         if ev is not None:
             ev[0].record()
+        nb = fused(k)
+        if ev is not None:
+            ev[1].record()
         if S > 1:
-            stp.sparse_mla_decode_partial_normalized(q, kv, nb["slot"], nb["count"], c0.scale, S,
-                                                     o_norm, m_part, l_part)
-            if ev is not None:
-                ev[1].record()
             stp.splitkv_merge_with_block_view(o_norm, m_part, l_part, nb, req, qpos, table,
                                               c0.page_size, out=out, lse=lse)
         else:
-            stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
-            if ev is not None:
-                ev[1].record()
+            stp.block_view_fill(nb, req, qpos, table, c0.page_size)
         if ev is not None:
             ev[2].record()
 
@@ -1205,6 +1214,11 @@ def main():
     n_roof = max(200, args.roofline_launches)
 
     def dec_only(k):
+        fused(k)
+
+    # the decode kernel alone, over the lists the normalisation wrote (for
+    # comparison with the launch that builds them itself)
+    def plain_decode(k):
         nb = norm[k % args.sets]
         if S > 1:
             stp.sparse_mla_decode_partial_normalized(q, kv, nb["slot"], nb["count"], c0.scale, S,
@@ -1216,6 +1230,7 @@ def main():
         stp.splitkv_merge_normalized(o_norm, m_part, l_part, out, lse)
 
     roof_avg_us = throughput_us(dec_only, n_roof, args.sets)
+    plain_avg_us = throughput_us(plain_decode, n_roof, args.sets)
     merge_avg_us = throughput_us(merge_only, n_roof, args.sets) if S > 1 else 0.0
     roof_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                  torch.cuda.Event(enable_timing=True)) for _ in range(n_roof)]
@@ -1237,7 +1252,14 @@ def main():
     per_set_steps = np.bincount(roof_idx % args.sets, minlength=args.sets)
     mean_sel = float((sel * per_set_steps).sum() / per_set_steps.sum())
     kv_bytes = mean_sel * ROW_BYTES
-    dec_bytes = kv_bytes + q_bytes + mean_sel * 4 + (o_bytes if S == 1 else 0)
+    # the launch also reads each token's top-k ids and page-table row (up to
+    # its position) and writes its lists (tok_out, slot_out: cap entries each)
+    P = c0.page_size
+    max_pos = c0.block_table.shape[1] * P - 1
+    table_bytes = float(sum((min(int(qp), max_pos) // P + 1) * 4 for qp in c0.q_pos))
+    norm_bytes = T * c0.top_k * 4 + table_bytes + T * cap * 8
+    dec_bytes = kv_bytes + q_bytes + norm_bytes + (o_bytes if S == 1 else 0)
+    plain_bytes = kv_bytes + q_bytes + mean_sel * 4 + (o_bytes if S == 1 else 0)
     flops = 2.0 * H * mean_sel * (576 + 512)
     dec_avg_s = roof_avg_us * 1e-6
     step_s = total_ms * 1e-3 / args.steps
@@ -1265,7 +1287,7 @@ def main():
             "mean_selected_rows_per_token": round(mean_sel / T, 2),
         },
         "roofline": {
-            "kernel": "sparse_mla_decode_kernel",
+            "kernel": "sparse_mla_decode_kernel (with normalisation)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -1279,16 +1301,18 @@ def main():
                       "two HIP events on the kernel's stream, after the timed steps",
             "event_pair_mean_us": round(float(roof_us.mean()), 3),
             "event_pair_median_us": round(float(np.median(roof_us)), 3),
-            "bytes_counted": "KV rows + queries + candidate ids of one launch (the split path: "
-                             "outputs belong to the merge launch)" if S > 1 else
-                             "KV rows + queries + candidate ids + outputs of one launch",
+            "bytes_counted": "KV rows + queries + top-k ids + page-table rows + the lists "
+                             "written, of one launch (the split path: outputs belong to the "
+                             "merge launch)" if S > 1 else
+                             "KV rows + queries + top-k ids + page-table rows + the lists "
+                             "written + outputs, of one launch",
             "merge_avg_us": round(merge_avg_us, 3),
             "call_frac": round((dec_bytes + (o_bytes if S > 1 else 0)) /
                                ((roof_avg_us + merge_avg_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(flops / dec_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         },
-        "step_launches": "normalise (block view deferred), decode, merge with block view"
-                         if S > 1 else "normalise with block view, decode",
+        "step_launches": "decode with the normalisation in its launch, merge with block view"
+                         if S > 1 else "decode with the normalisation in its launch, block view",
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
         "ceilings": ceilings,
         "decode_vs_ceilings": None if ceilings is None else {
@@ -1297,6 +1321,11 @@ def main():
                 round(ceilings["row_gather_decode_placement"]["us"] / (dec_avg_s * 1e6), 4),
             "frac_of_row_gather_each_row_once":
                 round(ceilings["row_gather_each_row_once"]["us"] / (dec_avg_s * 1e6), 4),
+        },
+        "decode_kernel_alone": {
+            "kernel": "sparse_mla_decode_kernel over the normalisation's lists",
+            "avg_launch_us": round(plain_avg_us, 3),
+            "frac": round(plain_bytes / (plain_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "kernel_us": {
             "decode_median": round(float(np.median(roof_us)), 3),

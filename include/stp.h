@@ -397,6 +397,50 @@ int stp_sparse_mla_decode_partial_normalized(const uint16_t* q, const uint16_t* 
                                              hipStream_t stream);
 
 /*
+ * ---- Normalisation and decode in one call -------------------------------------
+ * "5.1.1 · 从索引到 Kernel" §4.2 eq. (10): the index stage's time adds to
+ * every decode step, so the decode launch can build the candidate lists
+ * itself.  stp_normalize_and_decode equals stp_normalize_indices(topk ...
+ * blk_mask) followed by stp_sparse_mla_decode(q, kv, kv_rows, slot_out,
+ * count_out, cap, T, H, scale, num_splits, workspace, workspace_bytes, out,
+ * lse): the same normalisation outputs (block view included when blk_indptr
+ * is given) and the same attention output, bit for bit.  Arguments, layouts,
+ * requirements and errors are those of the two calls; the workspace is
+ * stp_sparse_mla_decode_workspace(T, H, cap, num_splits) bytes.
+ * When every split fits the decode's LDS id list (ceil(cap / S) <= 1120) and
+ * the per-token bitmap and page-table row fit 72 KiB
+ * (8 * ceil(max_blocks * page_size / 64) + 4 * max_blocks bytes), each decode
+ * workgroup builds its token's list in LDS and stages its split's slots
+ * directly (head group 0 also writes tok_out / slot_out for its split), so
+ * no launch stands between the two stages; otherwise the normalisation runs
+ * as its own launch first.  The split path then runs the merge, and the
+ * block view in the merge's launch (stp_splitkv_merge_with_block_view); a
+ * single pass completes the block view in a launch of its own.
+ *
+ * stp_normalize_and_decode_partial_normalized stops before the merge: it
+ * equals stp_normalize_indices_deferred (blk_indptr nullable, left in the
+ * deferred state) followed by stp_sparse_mla_decode_partial_normalized with
+ * num_splits = S >= 1.  stp_splitkv_merge_with_block_view completes both.
+ */
+int stp_normalize_and_decode(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                             const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                             int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+                             int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out,
+                             int32_t* slot_out, int32_t* count_out, int32_t* dropped_out,
+                             int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
+                             uint64_t* blk_mask, const uint16_t* q, const uint16_t* kv,
+                             int64_t kv_rows, int32_t H, float scale, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, uint16_t* out, float* lse,
+                             hipStream_t stream);
+int stp_normalize_and_decode_partial_normalized(
+    const int32_t* topk, int32_t top_k, const int32_t* req_id, const int32_t* q_pos, int32_t T,
+    const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+    int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+    int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr, const uint16_t* q,
+    const uint16_t* kv, int64_t kv_rows, int32_t H, float scale, int32_t num_splits,
+    uint16_t* o_norm, float* m_part, float* l_part, hipStream_t stream);
+
+/*
  * ---- Stage 4: split-KV merge -------------------------------------------------
  * "5.1.1 · 从索引到 Kernel" §3.2 eq. (7) for any number of splits, §7.1 (an
  * empty split, l_s = 0, takes no part); "PagedAttention 与 RadixAttention"

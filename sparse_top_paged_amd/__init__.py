@@ -18,7 +18,8 @@ __all__ = [
     "sparse_mla_decode", "sparse_mla_decode_partial", "sparse_mla_decode_partial_normalized",
     "splitkv_merge", "splitkv_merge_normalized", "decode_splits",
     "decode_workspace_bytes", "hot_lds_bytes", "host_device_pointer",
-    "splitkv_merge_with_block_view",
+    "splitkv_merge_with_block_view", "normalize_and_decode",
+    "normalize_and_decode_partial_normalized",
     "paged_gqa_decode", "paged_gqa_decode_splits", "paged_gqa_decode_workspace_bytes",
     "extend_attention", "kv_transfer", "sparse_mla_decode_fp8", "decode_fp8_splits",
     "decode_fp8_workspace_bytes", "decode_plan", "decode_run", "decode_plan_bytes",
@@ -247,6 +248,95 @@ def sparse_mla_decode_partial(q, kv, row_ids, counts=None, scale=D_QK ** -0.5, n
         _stream(dev)))
     return o_part, m_part, l_part
 
+
+
+def _norm_out(T, cap, dev, block_view):
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = {"tok": torch.empty((T, cap), **i32), "slot": torch.empty((T, cap), **i32),
+           "count": torch.empty((T,), **i32), "dropped": torch.empty((T,), **i32)}
+    if block_view:
+        out["blk_indptr"] = torch.empty((T + 1,), **i32)
+        out["blk_logical"] = torch.empty((max(1, T * cap),), **i32)
+        out["blk_page"] = torch.empty((max(1, T * cap),), **i32)
+        out["blk_mask"] = torch.empty((max(1, T * cap),), dtype=torch.int64, device=dev)
+    return out
+
+
+def _norm_args(topk, req_id, q_pos, block_table, page_size, window, num_sinks, cap, norm, dev):
+    T, top_k = topk.shape
+    num_reqs, max_blocks = block_table.shape
+    return [_dev(topk, "topk", torch.int32, dev), top_k, _dev(req_id, "req_id", torch.int32, dev),
+            _dev(q_pos, "q_pos", torch.int32, dev), T,
+            _dev(block_table, "block_table", torch.int32, dev), num_reqs, max_blocks, page_size,
+            window, num_sinks, cap, _dev(norm["tok"], "tok", torch.int32, dev),
+            _dev(norm["slot"], "slot", torch.int32, dev),
+            _dev(norm["count"], "count", torch.int32, dev),
+            _opt(norm.get("dropped"), "dropped", torch.int32, dev),
+            _opt(norm.get("blk_indptr"), "blk_indptr", torch.int32, dev)]
+
+
+def normalize_and_decode(topk, req_id, q_pos, block_table, page_size, window, num_sinks, q, kv,
+                         scale=D_QK ** -0.5, num_splits=0, cap=None, block_view=True, norm=None,
+                         workspace=None, out=None, lse=None):
+    """normalize_indices and sparse_mla_decode over its lists in one call.
+    Returns (out [T, H, 512] bf16, lse [T, H] float32, norm) with norm the dict
+    normalize_indices returns."""
+    dev = q.device
+    T, top_k = topk.shape
+    H = q.shape[1]
+    if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D_QK:
+        raise ValueError("q must be [T, H, 576] for the T rows of topk")
+    if kv.dim() != 2 or kv.shape[1] != D_QK:
+        raise ValueError("kv must be [rows, 576]")
+    if cap is None:
+        cap = top_k + window + num_sinks
+    if norm is None:
+        norm = _norm_out(T, cap, dev, block_view)
+    bv = "blk_indptr" in norm
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(T, H, cap, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace", torch.uint8, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    args = _norm_args(topk, req_id, q_pos, block_table, page_size, window, num_sinks, cap, norm,
+                      dev)
+    check(lib.stp_normalize_and_decode(
+        *args, _dev(norm["blk_logical"], "blk_logical", torch.int32, dev) if bv else None,
+        _dev(norm["blk_page"], "blk_page", torch.int32, dev) if bv else None,
+        _dev(norm["blk_mask"], "blk_mask", torch.int64, dev) if bv else None,
+        _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0], H,
+        float(scale), num_splits, ws_ptr, ws_bytes, _dev(out, "out", torch.bfloat16, dev),
+        _opt(lse, "lse", torch.float32, dev), _stream(dev)))
+    return out, lse, norm
+
+
+def normalize_and_decode_partial_normalized(topk, req_id, q_pos, block_table, page_size, window,
+                                            num_sinks, q, kv, scale, num_splits, o_norm, m_part,
+                                            l_part, cap=None, norm=None, block_view=True):
+    """normalize_indices(..., defer_block_view=True) and
+    sparse_mla_decode_partial_normalized over its lists in one call; returns
+    norm.  splitkv_merge_with_block_view completes both."""
+    dev = q.device
+    T, top_k = topk.shape
+    H = q.shape[1]
+    if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D_QK:
+        raise ValueError("q must be [T, H, 576] for the T rows of topk")
+    if cap is None:
+        cap = top_k + window + num_sinks
+    if norm is None:
+        norm = _norm_out(T, cap, dev, block_view)
+    args = _norm_args(topk, req_id, q_pos, block_table, page_size, window, num_sinks, cap, norm,
+                      dev)
+    check(lib.stp_normalize_and_decode_partial_normalized(
+        *args, _dev(q, "q", torch.bfloat16, dev), _dev(kv, "kv", torch.bfloat16, dev), kv.shape[0],
+        H, float(scale), num_splits, _dev(o_norm, "o_norm", torch.bfloat16, dev),
+        _dev(m_part, "m_part", torch.float32, dev), _dev(l_part, "l_part", torch.float32, dev),
+        _stream(dev)))
+    return norm
 
 def splitkv_merge(o_part, m_part, l_part, out=None, lse=None):
     """Stage 4: merge split states o [T, S, H, dv], m/l [T, S, H]."""

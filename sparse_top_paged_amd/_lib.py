@@ -60,6 +60,14 @@ SIGNATURES = {
         _p, _p, _i64, _p, _p, _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p]),
     "stp_splitkv_merge": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "stp_splitkv_merge_normalized": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "stp_normalize_and_decode": (ctypes.c_int, [
+        _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+        _p, _p, _p, _p, _p, _p, _p, _p,
+        _p, _p, _i64, _i32, _f32, _i32, _p, _sz, _p, _p, _p]),
+    "stp_normalize_and_decode_partial_normalized": (ctypes.c_int, [
+        _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+        _p, _p, _p, _p, _p,
+        _p, _p, _i64, _i32, _f32, _i32, _p, _p, _p, _p]),
     "stp_splitkv_merge_with_block_view": (ctypes.c_int, [
         _p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
         _p, _p, _p, _p, _p]),

@@ -215,6 +215,24 @@ int check_block_view_args(const char* what, const int32_t* tok_out, const int32_
 // The pass on its own launch (normalize.hip).
 int launch_block_fill(const BlockViewPass& p, int32_t T, hipStream_t stream);
 
+// The size and pointer checks of stp_normalize_indices (normalize.hip).
+int check_normalize_args(const char* what, const int32_t* topk, int32_t top_k,
+                         const int32_t* req_id, const int32_t* q_pos, int32_t T,
+                         const int32_t* block_table, int32_t num_reqs, int32_t max_blocks,
+                         int32_t page_size, int32_t window, int32_t num_sinks, int32_t cap,
+                         const int32_t* tok_out, const int32_t* slot_out,
+                         const int32_t* count_out);
+
+// The normalisation with its block view deferred (blk_indptr nullable, the
+// view's other arrays not needed), after the checks of
+// stp_normalize_indices (normalize.hip).
+int normalize_deferred(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                       const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                       int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t window,
+                       int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+                       int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr,
+                       hipStream_t stream);
+
 // The pass and the normalised split merge of the same T tokens (merge.hip):
 // one launch when the wide merge applies and the pass's LDS fits 64 KiB,
 // otherwise the pass, then the merge.

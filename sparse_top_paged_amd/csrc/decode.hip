@@ -45,6 +45,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "block_view.h"
 #include "stp_internal.h"
 
 namespace {
@@ -148,6 +149,20 @@ struct DecodeArgs {
   int32_t* queue;
   // fp8_ds_mla rows (656 B) instead of kv, for the fp8 row format
   const uint8_t* kv8;
+  // normalisation in the decode launch (kNorm): token t's candidate list is
+  // built from D, W and A as stp_normalize_indices builds it, whose outputs
+  // the workgroups also write
+  const int32_t* topk;
+  const int32_t* req_id;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int top_k, num_reqs, max_blocks, P, window, num_sinks, nwords_alloc;
+  uint64_t pdiv;
+  int32_t* tok_out;
+  int32_t* slot_out;
+  int32_t* count_out;
+  int32_t* dropped_out;
+  int32_t* blk_indptr;
 };
 
 // Output modes of the decode kernel.
@@ -354,6 +369,359 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
   }
 }
 
+// The normalisation of token t inside the decode launch ("5.1.1 · 从索引到
+// Kernel" §1.1 eq. (1), §1.2 eq. (2); "HiSparse" walkthrough, token -> global
+// slot conversion): the same S, slots, count, dropped count and block count
+// as stp_normalize_indices, built by each workgroup of the token for itself
+// so that no launch stands between the index stage and the attention.
+// LDS (ring stages 0 and 1, which the tiles take only after the ids are
+// staged): the position bitmap, the request's page-table row, D, and the
+// offsets of the bitmap's words and 64-word batches in the list.
+//   1. The output waves load the request, the position and D, then the
+//      table row; the score waves enqueue the query rows (issue_q) and wait
+//      for no load until the bitmap is built, so that no wait of theirs
+//      drains the query rows early.
+//   2. While the table row is in flight, the output waves set the positions
+//      of D, W and A within [0, limit] in an LDS bitmap (atomics); then the
+//      positions past each block's last visible slot (all of an unmapped
+//      page) are cleared.  One workgroup per token counts D's dropped
+//      entries.
+//      Then each wave scans its run of 64-word batches, keeping every
+//      word's and batch's offset within the run (tagged with the wave; the
+//      runs' totals place it in the list).
+//   3. The split [lo, lo + len) is the one the static launch cuts for this
+//      workgroup.  The batches that meet it go to the four waves in turn,
+//      one word per lane; each lane writes its bits' positions into the id
+//      list, and words with many bits are emitted by the whole wave.
+//   4. The waves turn positions into slots (-1 past the pool), write
+//      tok_out / slot_out (head group 0), and pad the list with -1 to the tile
+//      edge.  Split 0 of head group 0 writes the count and -(blocks + 1) into
+//      blk_indptr (the deferred block view's state), split 0 of the last head
+//      group the dropped count, split S - 1 the -1 tail.  An LDS-only barrier
+//      hands the ids over.
+constexpr int kDenseWord = 16;  // words with more set bits are emitted wave-wide
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+// LDS bytes of the normalisation: bitmap, table row, D, word offsets and
+// batch offsets.
+__host__ __device__ constexpr int64_t norm_lds_bytes(int64_t nwords, int64_t max_blocks,
+                                                     int64_t top_k) {
+  return nwords * 8 + max_blocks * 4 + top_k * 4 + nwords * 4 + (nwords / 64 + 1) * 4;
+}
+
+template <class IssueQ>
+__device__ __forceinline__ void normalize_split(const DecodeArgs& a, const DecodeLds& L,
+                                                int* s_bad, int t, int sidx, int hg, int& lo_out,
+                                                int& len_out, IssueQ&& issue_q) {
+  using stp::bv::div_p;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool outw = wave >= 2;  // output waves load; score waves enqueue the query rows
+  const int otid = tid - 128;   // thread index among the output waves
+  lds_u64* bm = (lds_u64*)L.tiles;
+  lds_i32* tbl = (lds_i32*)(L.tiles + (size_t)a.nwords_alloc * 8);
+  lds_i32* dl = tbl + a.max_blocks;  // D
+  lds_i32* woff = dl + a.top_k;      // each word's offset within its wave's run, tagged
+  lds_i32* red = (lds_i32*)L.stat;   // per-wave totals
+
+  // 1. request, position and D (output waves: the first 2048 entries in
+  //    registers), then the table row in flight while the bitmap is cleared
+  constexpr int kPer = 16;  // entries per output-wave thread per round (2048)
+  const int32_t* drow = a.topk + (int64_t)t * a.top_k;
+  const int r = a.req_id[t];
+  const int q = a.q_pos[t];
+  int dv[kPer];
+  if (outw) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int k = otid + 128 * u;
+      dv[u] = k < a.top_k ? drow[k] : -1;
+    }
+  }
+  const bool pad = r < 0 || r >= a.num_reqs || q < 0;
+  const int P = a.P;
+  const int limit = pad ? -1 : min(q, a.max_blocks * P - 1);  // last visible position
+  const int nwords = limit >= 0 ? (limit >> 6) + 1 : 0;
+  const int used_blocks = limit >= 0 ? div_p(limit, a.pdiv) + 1 : 0;
+  const int32_t* g_table = a.block_table + (int64_t)(pad ? 0 : r) * a.max_blocks;
+  int tv[kPer];
+  if (outw) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int k = otid + 128 * u;
+      tv[u] = k < used_blocks ? g_table[k] : -1;
+    }
+  } else {
+    issue_q();
+  }
+  // (the whole bitmap: the score waves do not wait for the position, whose
+  // load would drain their query rows first)
+  for (int w = tid; w < a.nwords_alloc; w += kThreads) bm[w] = 0ull;
+  if (tid == 0) {
+    s_bad[0] = 0;
+    s_bad[1] = 0;
+  }
+  lds_barrier();  // bitmap clear
+
+  // 2. the output waves set the positions of D, W and A within [0, limit]
+  //    in the bitmap while the table row is in flight, then stage the table
+  //    row (and D, for the workgroup that counts the dropped entries)
+  // (32-bit atomics on the 64-bit words' halves)
+  lds_i32* bm32 = (lds_i32*)L.tiles;
+  auto set_bit = [&](int p) {
+    __hip_atomic_fetch_or(&bm32[p >> 5], 1 << (p & 31), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  const bool drop_writer = hg == a.G - 1 && sidx == 0;
+  if (outw) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if ((unsigned)dv[u] <= (unsigned)limit) set_bit(dv[u]);
+    if (!pad) {
+      if (a.window > 0)
+        for (int p = max(0, q - a.window + 1) + otid; p <= min(q, limit); p += 128) set_bit(p);
+      const int na = min(min(a.num_sinks, q + 1), limit + 1);
+      for (int p = otid; p < na; p += 128) set_bit(p);
+    }
+    if (drop_writer) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int k = otid + 128 * u;
+        if (k < a.top_k) dl[k] = dv[u];
+      }
+    }
+    for (int k0 = kPer * 128; k0 < a.top_k; k0 += kPer * 128) {  // D past 2048 entries
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int k = k0 + otid + 128 * u;
+        dv[u] = k < a.top_k ? drow[k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int k = k0 + otid + 128 * u;
+        if ((unsigned)dv[u] <= (unsigned)limit) set_bit(dv[u]);
+        if (drop_writer && k < a.top_k) dl[k] = dv[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int k = otid + 128 * u;
+      if (k < used_blocks) tbl[k] = tv[u];
+    }
+    for (int k0 = kPer * 128; k0 < used_blocks; k0 += kPer * 128) {  // rows past 2048 blocks
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int k = k0 + otid + 128 * u;
+        tv[u] = k < used_blocks ? g_table[k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int k = k0 + otid + 128 * u;
+        if (k < used_blocks) tbl[k] = tv[u];
+      }
+    }
+  }
+  lds_barrier();  // candidate bitmap, table row and D staged
+
+  // drop the positions that are not visible: block b keeps offsets up to its
+  // page's last slot within int32 (none for an unmapped page).  The
+  // workgroup that writes the dropped count also counts D's entries >= 0
+  // that are not visible.
+  // the last visible offset of block b (-1: none)
+  auto last_off = [&](int b) {
+    const int page = tbl[b];
+    if (page < 0) return -1;
+    const int64_t room = (int64_t)INT32_MAX - (int64_t)page * P;
+    return room >= P - 1 ? P - 1 : (int)max(room, (int64_t)-1);
+  };
+  for (int b = tid; b < used_blocks; b += kThreads) {
+    const int keep = last_off(b);
+    if (keep < P - 1) {
+      const int c0p = b * P + keep + 1, c1p = min((b + 1) * P, limit + 1);  // [c0p, c1p) dropped
+      for (int wd = c0p >> 5; wd <= (c1p - 1) >> 5 && c0p < c1p; ++wd) {
+        const int lo32 = max(c0p, wd * 32) - wd * 32, hi32 = min(c1p, wd * 32 + 32) - wd * 32;
+        const uint32_t m = (hi32 - lo32 == 32 ? 0xffffffffu : ((1u << (hi32 - lo32)) - 1u)) << lo32;
+        __hip_atomic_fetch_and(&bm32[wd], (int)~m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+  }
+  int my_drop = 0;
+  if (drop_writer && !pad) {
+    for (int k = tid; k < a.top_k; k += kThreads) {
+      const int p = dl[k];
+      if (p >= 0) {
+        const bool in = p <= limit;
+        const int b = div_p(in ? p : 0, a.pdiv);
+        my_drop += (in && p - b * P <= last_off(b)) ? 0 : 1;
+      }
+    }
+  }
+  lds_barrier();  // bitmap complete
+
+  // counts: each wave scans its run of 64-word batches; a word's (and a
+  // batch's) offset is stored within the run, tagged with the wave, and the
+  // runs' totals turn it into the list position where it is read
+  const bool writer = hg == 0 && sidx == 0;
+  const int nbatch = (nwords + 63) >> 6;
+  const int bpw = (nbatch + 3) >> 2;
+  const int bb0 = min(nbatch, wave * bpw), bb1 = min(nbatch, bb0 + bpw);
+  lds_i32* bstart = woff + a.nwords_alloc;  // [nbatch] batch offsets, tagged
+  int run = 0;
+  for (int bb = bb0; bb < bb1; ++bb) {
+    const int w = bb * 64 + lane;
+    const int c = w < nwords ? __popcll(bm[w]) : 0;
+    const int incl = stp::wave_incl_sum(c);
+    if (w < nwords) woff[w] = (run + incl - c) | (wave << 24);
+    if (lane == 0) bstart[bb] = run | (wave << 24);
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  int my_blocks = 0;
+  if (drop_writer) my_drop = stp::wave_sum(my_drop);
+  if (writer) {
+    for (int b = tid; b < used_blocks; b += kThreads) {
+      const int blo = b * P, bhi = min(blo + P, limit + 1);
+      const int w0 = blo >> 6, w1 = (bhi - 1) >> 6, sh = blo & 63;
+      uint64_t acc = bm[w0] >> sh;
+      if (w1 != w0) acc |= bm[w1] << (64 - sh);
+      const int nbits = bhi - blo;
+      if (nbits < 64) acc &= (1ull << nbits) - 1;
+      my_blocks += acc ? 1 : 0;
+    }
+    my_blocks = stp::wave_sum(my_blocks);
+  }
+  if (lane == 0) {
+    red[wave] = run;
+    red[4 + wave] = my_blocks;
+    red[8 + wave] = my_drop;
+  }
+  lds_barrier();  // word and batch offsets, wave totals
+  const int c0 = red[0], c1 = red[1], c2 = red[2];
+  const int n = __builtin_amdgcn_readfirstlane(c0 + c1 + c2 + red[3]);
+  // a tagged offset -> its position in the list
+  auto untag = [&](int e) {
+    const int ow = e >> 24;
+    return (e & 0xffffff) + (ow > 0 ? c0 : 0) + (ow > 1 ? c1 : 0) + (ow > 2 ? c2 : 0);
+  };
+
+  // 3. this workgroup's split, as the static launch cuts the list: the
+  //    positions of the batches that meet it go into the id list, batch
+  //    bb_first + i to wave i % 4, one word per lane
+  const int chunk = (n + a.S - 1) / a.S;
+  const int lo = min(n, sidx * chunk);
+  const int len = min(n, lo + chunk) - lo;
+  const int hi_pos = lo + len;
+  const int ntiles = (len + kTileRows - 1) / kTileRows;
+  int bb_first = 0;  // the last batch that starts at or before lo
+  for (int b0 = 0; b0 < nbatch; b0 += 64) {
+    const int bb = b0 + lane;
+    bb_first += __popcll(__ballot(bb < nbatch && untag(bstart[bb]) <= lo));
+  }
+  bb_first = max(0, bb_first - 1);
+  for (int bb = bb_first + wave; len > 0 && bb < nbatch; bb += 4) {
+    const int w = bb * 64 + lane;
+    const uint64_t x = w < nwords ? (uint64_t)bm[w] : 0ull;
+    const int e = w < nwords ? woff[w] : 0;
+    if (untag(__builtin_amdgcn_readfirstlane(bstart[bb])) >= hi_pos) break;
+    int off = w < nwords ? untag(e) : n;
+    const int c = __popcll(x);
+    const bool meets = c > 0 && off < hi_pos && off + c > lo;
+    // sparse words: the owning lane walks the bits of both halves at once
+    // (two independent chains), writing to a scratch slot past the list for
+    // a position outside the split
+    if (__ballot(meets && c < kDenseWord)) {
+      const bool sparse = meets && c < kDenseWord;
+      uint32_t blo = sparse ? (uint32_t)x : 0u, bhi = sparse ? (uint32_t)(x >> 32) : 0u;
+      int olo = off - lo, ohi = off - lo + __popc((uint32_t)x);
+      const int plo = w * 64, phi = w * 64 + 32;
+      lds_i32* ids = (lds_i32*)L.ids;
+      while (blo | bhi) {  // branch-free body: an empty half writes the scratch slot
+        const bool vlo = blo != 0, vhi = bhi != 0;
+        ids[vlo && (unsigned)olo < (unsigned)len ? olo : kIdsMax] = plo + (int)__ffs(blo) - 1;
+        ids[vhi && (unsigned)ohi < (unsigned)len ? ohi : kIdsMax] = phi + (int)__ffs(bhi) - 1;
+        blo &= blo - 1;
+        bhi &= bhi - 1;
+        olo += vlo ? 1 : 0;
+        ohi += vhi ? 1 : 0;
+      }
+    }
+    // dense words: one lane per bit
+    uint64_t dense = __ballot(meets && c >= kDenseWord);
+    while (dense) {
+      const int src = __builtin_ctzll(dense);
+      dense &= dense - 1;
+      const uint32_t xlo = __builtin_amdgcn_readlane((uint32_t)x, src);
+      const uint32_t xhi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), src);
+      const int woff0 = __builtin_amdgcn_readlane(off, src);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi(xhi, __builtin_amdgcn_mbcnt_lo(xlo, 0u));
+      const bool mine = ((lane < 32 ? xlo >> lane : xhi >> (lane - 32)) & 1u) != 0;
+      const int pos = woff0 + (int)below;
+      if (mine && pos >= lo && pos < hi_pos) L.ids[pos - lo] = (bb * 64 + src) * 64 + lane;
+    }
+  }
+  lds_barrier();  // positions of the split in the id list
+
+  // 4. positions -> slots, the lists and the token's scalars
+  {
+    int32_t* tok_row = a.tok_out + (int64_t)t * a.cap;
+    int32_t* slot_row = a.slot_out + (int64_t)t * a.cap;
+    int bad = 0;
+    constexpr int kCB = 3;  // entries per thread with their LDS reads together
+    for (int k0 = 0; k0 < ntiles * kTileRows; k0 += kCB * kThreads) {
+      int pv[kCB], bv[kCB], pg[kCB];
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        const int k = k0 + tid + kThreads * u;
+        pv[u] = k < len ? L.ids[k] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        bv[u] = div_p(pv[u], a.pdiv);
+        pg[u] = tbl[bv[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        const int k = k0 + tid + kThreads * u;
+        if (k < ntiles * kTileRows) {
+          int id = -1;
+          if (k < len) {
+            const int slot = pg[u] * P + (pv[u] - bv[u] * P);
+            const bool valid = slot < a.kv_rows;
+            id = valid ? slot : -1;
+            bad |= valid ? 0 : 1;
+            if (hg == 0) {
+              tok_row[lo + k] = pv[u];
+              slot_row[lo + k] = slot;
+            }
+          }
+          L.ids[k] = id;
+        }
+      }
+    }
+    if (__ballot(bad) != 0 && lane == 0) s_bad[0] = 1;
+    if (hg == 0 && sidx == a.S - 1)
+      for (int k = n + tid; k < a.cap; k += kThreads) {
+        tok_row[k] = -1;
+        slot_row[k] = -1;
+      }
+    if (writer && tid == 0) {
+      int nb = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) nb += red[4 + w];
+      a.count_out[t] = n;
+      if (a.blk_indptr) a.blk_indptr[t + 1] = -(nb + 1);
+    }
+    if (drop_writer && tid == 0 && a.dropped_out) {
+      int dropped = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dropped += red[8 + w];
+      a.dropped_out[t] = dropped;
+    }
+  }
+  lo_out = __builtin_amdgcn_readfirstlane(lo);
+  len_out = __builtin_amdgcn_readfirstlane(len);
+  lds_barrier();  // ids and s_bad visible; stages 0 and 1 free for the tiles
+}
+
 // One work item: token t, candidate positions lo .. lo + len - 1 of its list,
 // head group hg; split partials go to slot `part` ([part][H][512]).  kFp8:
 // the rows are fp8_ds_mla rows (a.kv8), dequantised on their way into the
@@ -363,10 +731,10 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
 // iteration i the slot of tile i - 1 (whose ids every wave is done with after
 // B(i)) takes tile i + kIdTiles - 1's ids by LDS DMA, as they are in
 // memory: position and range checks then happen where ids are read.
-template <int kMode, bool kFp8 = false, bool kLong = false>
+template <int kMode, bool kFp8 = false, bool kLong = false, bool kNorm = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
-                                            int hg, int64_t part) {
+                                            int hg, int64_t part, int sidx = 0) {
   // opaque per call, so that nothing derived from the thread index is hoisted
   // out of the queue launch's item loop (it would stay live across the whole
   // item and push the registers into spills)
@@ -376,7 +744,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   const int wave = tid >> 6;
   const bool score = wave < 2;
   const int j = wave & 1;
-  const int ntiles = (len + kTileRows - 1) / kTileRows;
 
   // Row loads go straight to LDS (global_load_lds), one 8-row group per wave
   // instruction sequence: lane keeps row lane / 8 of the group and, in block
@@ -389,7 +756,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   // Score wave j's 32 query rows go to ring stage 2 + j, in the tile layout
   // (coalesced like any tile; read back as MFMA fragments before B(0), after
   // which the stage carries tiles again).
-  if (score) {
+  auto issue_q = [&]() {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int head = hg * kHeadsPerWG + 32 * j + grp * kGroupRows + (lane >> 3);
@@ -398,13 +765,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
           ld_col;
       load_row_chunks<0>(src, group_dst(2 + j, grp));
     }
-  }
+  };
+  // kNorm: the split's range and ids come from the token's normalisation,
+  // which enqueues the query rows itself
+  if constexpr (kNorm)
+    normalize_split(a, L, s_bad, t, sidx, hg, lo, len, issue_q);
+  else if (score)
+    issue_q();
+  const int ntiles = (len + kTileRows - 1) / kTileRows;
 
   // candidate ids of this split, -1 for invalid ones and up to the tile edge;
   // read by the output waves, whose load queue is empty here (the score
   // waves' queue holds the query rows), and handed over with an LDS-only
   // barrier so that nobody waits for the query rows yet
-  if (!score) {
+  if (!kNorm && !score) {
     // every load first, then the stores: one round trip instead of one per
     // 128 ids
     constexpr int kPer = (kIdsMax + 127) / 128;
@@ -427,7 +801,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     const int wbad = __ballot(bad) != 0 ? 1 : 0;
     if (lane == 0) s_bad[j] = wbad;
   }
-  lds_barrier();
+  if constexpr (!kNorm) lds_barrier();
   // a split with an invalid id masks every tile, otherwise only its last tile
   // (the rows past its end) needs a mask (a long split: every tile, its later
   // ids are not seen before their turn)
@@ -893,14 +1267,14 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
 // slot is -1); the others write partial states for the merge.  A workgroup ends
 // when no queue has an unclaimed item (every queue is finite and its head
 // only grows, so every workgroup exits).
-template <int kMode, bool kQueue, bool kFp8 = false, bool kLong = false>
+template <int kMode, bool kQueue, bool kFp8 = false, bool kLong = false, bool kNorm = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_mla_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char s_tiles[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) char s_pbuf[2 * 2 * 2 * 1024];
   __shared__ __attribute__((aligned(16))) float s_alpha[2 * 64];
   __shared__ __attribute__((aligned(16))) float s_stat[3 * 64];
-  __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax];
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[kIdsMax + 4];  // + a scratch slot
   __shared__ int s_bad[2];
   const DecodeLds L{(lds_t*)s_tiles, (lds_t*)s_pbuf, s_alpha, s_stat, s_ids};
   // the zero row's address, fetched once: inside the loops its GOT load (a
@@ -918,13 +1292,18 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const int s = rem / a.G;
     const int hg = rem - s * a.G;
     if (t >= a.T) return;
-    int n = a.counts ? a.counts[t] : a.cap;
-    n = min(max(n, 0), a.cap);
-    const int chunk = (n + a.S - 1) / a.S;
-    const int lo = min(n, s * chunk);
-    const int len = min(n, lo + chunk) - lo;
-    decode_item<kMode, kFp8, kLong>(a, L, s_bad, zero_row, t, lo, len, hg,
-                                    (int64_t)t * a.S + s);
+    if constexpr (kNorm) {
+      decode_item<kMode, false, false, true>(a, L, s_bad, zero_row, t, 0, 0, hg,
+                                             (int64_t)t * a.S + s, s);
+    } else {
+      int n = a.counts ? a.counts[t] : a.cap;
+      n = min(max(n, 0), a.cap);
+      const int chunk = (n + a.S - 1) / a.S;
+      const int lo = min(n, s * chunk);
+      const int len = min(n, lo + chunk) - lo;
+      decode_item<kMode, kFp8, kLong>(a, L, s_bad, zero_row, t, lo, len, hg,
+                                      (int64_t)t * a.S + s);
+    }
   } else {
     const int grid = gridDim.x;
     const int x = blockIdx.x & 7;
@@ -1100,6 +1479,82 @@ int launch_decode(int mode, const uint16_t* q, const uint16_t* kv, int64_t kv_ro
   return stp::check_launch("sparse_mla_decode_kernel");
 }
 
+// The normalisation's arguments for the launches that carry it.
+struct NormCall {
+  const int32_t* topk;
+  int32_t top_k;
+  const int32_t* req_id;
+  const int32_t* q_pos;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks, page_size, window, num_sinks;
+  int32_t* tok_out;
+  int32_t* slot_out;
+  int32_t* count_out;
+  int32_t* dropped_out;
+  int32_t* blk_indptr;
+  int32_t* blk_logical;
+  int32_t* blk_page;
+  uint64_t* blk_mask;
+};
+
+// Whether the normalisation fits in the decode launch: splits within the
+// LDS id list, the bitmap and the page-table row within ring stages 0 and 1.
+bool norm_fits(const NormCall& nc, int32_t cap, int32_t S) {
+  const int64_t nwords = max((int64_t)1, ((int64_t)nc.max_blocks * nc.page_size + 63) / 64);
+  return (cap + S - 1) / S <= kIdsMax &&
+         norm_lds_bytes(nwords, nc.max_blocks, nc.top_k) <= 2 * (int64_t)kTileBytes;
+}
+
+// The normalisation of T tokens and the decode of their lists in one launch
+// (norm_fits must hold): mode kOutFinal (S = 1) or kOutPartialBf16.  The
+// block view is left deferred (blk_indptr holds the per-token state).
+int launch_norm_decode(int mode, const NormCall& nc, const uint16_t* q, const uint16_t* kv,
+                       int64_t kv_rows, int32_t cap, int32_t T, int32_t H, float scale, int32_t S,
+                       void* o_part, float* m_part, float* l_part, uint16_t* out, float* lse,
+                       hipStream_t stream) {
+  DecodeArgs a{};
+  a.q = q;
+  a.kv = kv;
+  a.kv_rows = kv_rows;
+  a.cap = cap;
+  a.T = T;
+  a.H = H;
+  a.scale_log2 = scale * kLog2e;
+  a.S = S;
+  a.G = (H + kHeadsPerWG - 1) / kHeadsPerWG;
+  a.o_part = o_part;
+  a.m_part = m_part;
+  a.l_part = l_part;
+  a.out = out;
+  a.lse = lse;
+  a.topk = nc.topk;
+  a.top_k = nc.top_k;
+  a.req_id = nc.req_id;
+  a.q_pos = nc.q_pos;
+  a.block_table = nc.block_table;
+  a.num_reqs = (nc.num_reqs == 0 || nc.max_blocks == 0) ? 0 : nc.num_reqs;
+  a.max_blocks = nc.max_blocks;
+  a.P = nc.page_size;
+  a.window = nc.window;
+  a.num_sinks = nc.num_sinks;
+  a.nwords_alloc = max(1, (int)(((int64_t)nc.max_blocks * nc.page_size + 63) / 64));
+  a.pdiv = ((1ull << 32) + (uint64_t)nc.page_size - 1) / (uint64_t)nc.page_size;
+  a.tok_out = nc.tok_out;
+  a.slot_out = nc.slot_out;
+  a.count_out = nc.count_out;
+  a.dropped_out = nc.dropped_out;
+  a.blk_indptr = nc.blk_indptr;
+  const int64_t blocks = (int64_t)8 * ((T + 7) / 8) * S * a.G;
+  if (blocks > INT32_MAX) return stp::fail(STP_ERR_INVALID_ARG, "normalize_and_decode: grid too large");
+  if (mode == kOutFinal)
+    sparse_mla_decode_kernel<kOutFinal, false, false, false, true>
+        <<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+  else
+    sparse_mla_decode_kernel<kOutPartialBf16, false, false, false, true>
+        <<<(unsigned)blocks, kThreads, 0, stream>>>(a);
+  return stp::check_launch("sparse_mla_decode_kernel (with normalisation)");
+}
+
 int check_common(const uint16_t* q, const uint16_t* kv, int64_t kv_rows, const int32_t* row_ids,
                  int32_t cap, int32_t T, int32_t H, float scale) {
   using stp::fail;
@@ -1261,6 +1716,112 @@ extern "C" int stp_sparse_mla_decode_partial_normalized(
     return stp::fail(STP_ERR_INVALID_ARG, "sparse_mla_decode_partial_normalized: null output");
   return launch_decode(kOutPartialBf16, q, kv, kv_rows, row_ids, counts, cap, T, H, scale,
                        num_splits, (float*)o_norm, m_part, l_part, nullptr, nullptr, stream);
+}
+
+// Normalisation and decode in one call.  The decode launch builds each
+// token's list itself when norm_fits holds; otherwise the normalisation runs
+// first as its own launch.  The block view (when asked for) is completed by
+// the merge launch, or by its own launch after a single-pass decode.
+namespace {
+
+int check_norm_call(const char* what, const NormCall& nc, int32_t T, int32_t cap) {
+  return stp::check_normalize_args(what, nc.topk, nc.top_k, nc.req_id, nc.q_pos, T,
+                                   nc.block_table, nc.num_reqs, nc.max_blocks, nc.page_size,
+                                   nc.window, nc.num_sinks, cap, nc.tok_out, nc.slot_out,
+                                   nc.count_out);
+}
+
+// Normalisation (block view deferred) and a decode of mode kOutFinal or
+// kOutPartialBf16 over the lists it writes: one launch or two.
+int norm_then_decode(int mode, const NormCall& nc, const uint16_t* q, const uint16_t* kv,
+                     int64_t kv_rows, int32_t cap, int32_t T, int32_t H, float scale, int32_t S,
+                     void* o_part, float* m_part, float* l_part, uint16_t* out, float* lse,
+                     hipStream_t stream) {
+  if (norm_fits(nc, cap, S))
+    return launch_norm_decode(mode, nc, q, kv, kv_rows, cap, T, H, scale, S, o_part, m_part,
+                              l_part, out, lse, stream);
+  if (int rc = stp::normalize_deferred(nc.topk, nc.top_k, nc.req_id, nc.q_pos, T, nc.block_table,
+                                       nc.num_reqs, nc.max_blocks, nc.page_size, nc.window,
+                                       nc.num_sinks, cap, nc.tok_out, nc.slot_out, nc.count_out,
+                                       nc.dropped_out, nc.blk_indptr, stream))
+    return rc;
+  return launch_decode(mode, q, kv, kv_rows, nc.slot_out, nc.count_out, cap, T, H, scale, S,
+                       (float*)o_part, m_part, l_part, out, lse, stream);
+}
+
+stp::BlockViewPass block_view_pass(const NormCall& nc, int32_t cap) {
+  return {nc.tok_out,    nc.slot_out,    nc.req_id,   nc.q_pos,      nc.block_table,
+          nc.num_reqs,   nc.max_blocks,  nc.page_size, cap,          nc.blk_indptr,
+          nc.blk_logical, nc.blk_page,   nc.blk_mask};
+}
+
+}  // namespace
+
+extern "C" int stp_normalize_and_decode(
+    const int32_t* topk, int32_t top_k, const int32_t* req_id, const int32_t* q_pos, int32_t T,
+    const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+    int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+    int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr, int32_t* blk_logical,
+    int32_t* blk_page, uint64_t* blk_mask, const uint16_t* q, const uint16_t* kv,
+    int64_t kv_rows, int32_t H, float scale, int32_t num_splits, void* workspace,
+    size_t workspace_bytes, uint16_t* out, float* lse, hipStream_t stream) {
+  using stp::fail;
+  const NormCall nc{topk,       top_k,     req_id,    q_pos,     block_table, num_reqs,
+                    max_blocks, page_size, window,    num_sinks, tok_out,     slot_out,
+                    count_out,  dropped_out, blk_indptr, blk_logical, blk_page, blk_mask};
+  if (int rc = check_norm_call("normalize_and_decode", nc, T, cap)) return rc;
+  if (int rc = check_common(q, kv, kv_rows, slot_out, cap, T, H, scale)) return rc;
+  if (num_splits < 0) return fail(STP_ERR_INVALID_ARG, "normalize_and_decode: num_splits < 0");
+  if (T == 0) return STP_OK;
+  if (!out) return fail(STP_ERR_INVALID_ARG, "normalize_and_decode: null out");
+  if (blk_indptr && (!blk_logical || !blk_page || !blk_mask))
+    return fail(STP_ERR_INVALID_ARG, "normalize_and_decode: block view arrays missing");
+  const int32_t S = choose_splits(T, H, cap, num_splits);
+  if (S == 1) {
+    if (int rc = norm_then_decode(kOutFinal, nc, q, kv, kv_rows, cap, T, H, scale, 1, nullptr,
+                                  nullptr, nullptr, out, lse, stream))
+      return rc;
+    return blk_indptr ? stp::launch_block_fill(block_view_pass(nc, cap), T, stream) : STP_OK;
+  }
+  const size_t need = stp_sparse_mla_decode_workspace(T, H, cap, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(STP_ERR_WORKSPACE, "normalize_and_decode: workspace of %zu bytes needed, %zu given",
+                need, workspace_bytes);
+  const size_t n = (size_t)T * S * H;
+  char* ws = (char*)workspace;
+  uint16_t* o_norm = (uint16_t*)ws;
+  float* m_part = (float*)(ws + align256(n * kDV * 2));
+  float* l_part = (float*)(ws + align256(n * kDV * 2) + align256(n * 4));
+  if (int rc = norm_then_decode(kOutPartialBf16, nc, q, kv, kv_rows, cap, T, H, scale, S, o_norm,
+                                m_part, l_part, nullptr, nullptr, stream))
+    return rc;
+  if (blk_indptr)
+    return stp::launch_merge_block_view(o_norm, m_part, l_part, T, S, H, kDV, out, lse,
+                                        block_view_pass(nc, cap), stream);
+  return stp::launch_merge_normalized(o_norm, m_part, l_part, T, S, H, kDV, out, lse, stream);
+}
+
+extern "C" int stp_normalize_and_decode_partial_normalized(
+    const int32_t* topk, int32_t top_k, const int32_t* req_id, const int32_t* q_pos, int32_t T,
+    const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int32_t page_size,
+    int32_t window, int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+    int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr, const uint16_t* q,
+    const uint16_t* kv, int64_t kv_rows, int32_t H, float scale, int32_t num_splits,
+    uint16_t* o_norm, float* m_part, float* l_part, hipStream_t stream) {
+  using stp::fail;
+  const NormCall nc{topk,       top_k,     req_id,    q_pos,     block_table, num_reqs,
+                    max_blocks, page_size, window,    num_sinks, tok_out,     slot_out,
+                    count_out,  dropped_out, blk_indptr, nullptr, nullptr,    nullptr};
+  if (int rc = check_norm_call("normalize_and_decode_partial_normalized", nc, T, cap)) return rc;
+  if (int rc = check_common(q, kv, kv_rows, slot_out, cap, T, H, scale)) return rc;
+  if (num_splits < 1)
+    return fail(STP_ERR_INVALID_ARG,
+                "normalize_and_decode_partial_normalized: num_splits must be >= 1");
+  if (T == 0) return STP_OK;
+  if (!o_norm || !m_part || !l_part)
+    return fail(STP_ERR_INVALID_ARG, "normalize_and_decode_partial_normalized: null output");
+  return norm_then_decode(kOutPartialBf16, nc, q, kv, kv_rows, cap, T, H, scale, num_splits,
+                          o_norm, m_part, l_part, nullptr, nullptr, stream);
 }
 
 // fp8_ds_mla rows: the same launch and split path, the rows dequantised on

@@ -377,6 +377,33 @@ int check_block_view_args(const char* what, const int32_t* tok_out, const int32_
 
 }  // namespace stp
 
+namespace stp {
+
+int check_normalize_args(const char* what, const int32_t* topk, int32_t top_k,
+                         const int32_t* req_id, const int32_t* q_pos, int32_t T,
+                         const int32_t* block_table, int32_t num_reqs, int32_t max_blocks,
+                         int32_t page_size, int32_t window, int32_t num_sinks, int32_t cap,
+                         const int32_t* tok_out, const int32_t* slot_out,
+                         const int32_t* count_out) {
+  if (T < 0 || top_k < 0 || num_reqs < 0 || max_blocks < 0 || window < 0 || num_sinks < 0 ||
+      cap < 0)
+    return fail(STP_ERR_INVALID_ARG, "%s: negative size", what);
+  if (page_size < 1 || page_size > 64)
+    return fail(STP_ERR_INVALID_ARG, "%s: page_size %d not in [1, 64]", what, page_size);
+  if ((int64_t)cap < (int64_t)top_k + window + num_sinks)
+    return fail(STP_ERR_INVALID_ARG, "%s: cap %d < top_k + window + num_sinks", what, cap);
+  if ((int64_t)max_blocks * page_size > kMaxPositions)
+    return fail(STP_ERR_INVALID_ARG, "%s: max_blocks * page_size exceeds %d positions", what,
+                kMaxPositions);
+  if (T == 0) return STP_OK;
+  if (!req_id || !q_pos || !tok_out || !slot_out || !count_out || (top_k > 0 && !topk) ||
+      (num_reqs > 0 && max_blocks > 0 && !block_table))
+    return fail(STP_ERR_INVALID_ARG, "%s: null pointer", what);
+  return STP_OK;
+}
+
+}  // namespace stp
+
 static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req_id,
                           const int32_t* q_pos, int32_t T, const int32_t* block_table,
                           int32_t num_reqs, int32_t max_blocks, int32_t page_size,
@@ -385,22 +412,12 @@ static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req
                           int32_t* blk_indptr, int32_t* blk_logical, int32_t* blk_page,
                           uint64_t* blk_mask, hipStream_t stream, bool defer_fill) {
   using stp::fail;
-  if (T < 0 || top_k < 0 || num_reqs < 0 || max_blocks < 0 || window < 0 || num_sinks < 0 ||
-      cap < 0)
-    return fail(STP_ERR_INVALID_ARG, "normalize_indices: negative size");
-  if (page_size < 1 || page_size > 64)
-    return fail(STP_ERR_INVALID_ARG, "normalize_indices: page_size %d not in [1, 64]", page_size);
-  if ((int64_t)cap < (int64_t)top_k + window + num_sinks)
-    return fail(STP_ERR_INVALID_ARG, "normalize_indices: cap %d < top_k + window + num_sinks",
-                cap);
-  if ((int64_t)max_blocks * page_size > kMaxPositions)
-    return fail(STP_ERR_INVALID_ARG,
-                "normalize_indices: max_blocks * page_size exceeds %d positions", kMaxPositions);
+  if (int rc = stp::check_normalize_args("normalize_indices", topk, top_k, req_id, q_pos, T,
+                                         block_table, num_reqs, max_blocks, page_size, window,
+                                         num_sinks, cap, tok_out, slot_out, count_out))
+    return rc;
   if (T == 0) return STP_OK;
-  if (!req_id || !q_pos || !tok_out || !slot_out || !count_out || (top_k > 0 && !topk) ||
-      (num_reqs > 0 && max_blocks > 0 && !block_table))
-    return fail(STP_ERR_INVALID_ARG, "normalize_indices: null pointer");
-  if (blk_indptr && (!blk_logical || !blk_page || !blk_mask))
+  if (blk_indptr && !defer_fill && (!blk_logical || !blk_page || !blk_mask))
     return fail(STP_ERR_INVALID_ARG, "normalize_indices: block view arrays missing");
   if (num_reqs == 0 || max_blocks == 0) {
     // No request has a mapped page: every token is a padding row.
@@ -436,6 +453,21 @@ static int normalize_impl(const int32_t* topk, int32_t top_k, const int32_t* req
                                   T, stream);
   return STP_OK;
 }
+
+namespace stp {
+
+int normalize_deferred(const int32_t* topk, int32_t top_k, const int32_t* req_id,
+                       const int32_t* q_pos, int32_t T, const int32_t* block_table,
+                       int32_t num_reqs, int32_t max_blocks, int32_t page_size, int32_t window,
+                       int32_t num_sinks, int32_t cap, int32_t* tok_out, int32_t* slot_out,
+                       int32_t* count_out, int32_t* dropped_out, int32_t* blk_indptr,
+                       hipStream_t stream) {
+  return normalize_impl(topk, top_k, req_id, q_pos, T, block_table, num_reqs, max_blocks,
+                        page_size, window, num_sinks, cap, tok_out, slot_out, count_out,
+                        dropped_out, blk_indptr, nullptr, nullptr, nullptr, stream, true);
+}
+
+}  // namespace stp
 
 extern "C" int stp_normalize_indices(const int32_t* topk, int32_t top_k, const int32_t* req_id,
                                      const int32_t* q_pos, int32_t T,
