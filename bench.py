@@ -1231,6 +1231,27 @@ def main():
 
     roof_avg_us = throughput_us(dec_only, n_roof, args.sets)
     plain_avg_us = throughput_us(plain_decode, n_roof, args.sets)
+
+    # the same step as separate launches (normalisation with its block view
+    # deferred, the decode over its lists, merge with block view), timed back
+    # to back like the fused one, for the comparison
+    def step_fused(k):
+        step(k)
+
+    def step_separate(k):
+        nb = stp.normalize_indices(topks[k], req, qpos, table, c0.page_size, c0.window,
+                                   c0.num_sinks, cap, out=norm[k], defer_block_view=S > 1)
+        if S > 1:
+            stp.sparse_mla_decode_partial_normalized(q, kv, nb["slot"], nb["count"], c0.scale, S,
+                                                     o_norm, m_part, l_part)
+            stp.splitkv_merge_with_block_view(o_norm, m_part, l_part, nb, req, qpos, table,
+                                              c0.page_size, out=out, lse=lse)
+        else:
+            stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
+            stp.block_view_fill(nb, req, qpos, table, c0.page_size)
+
+    fused_step_us = throughput_us(step_fused, n_roof, args.sets)
+    separate_step_us = throughput_us(step_separate, n_roof, args.sets)
     merge_avg_us = throughput_us(merge_only, n_roof, args.sets) if S > 1 else 0.0
     roof_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                  torch.cuda.Event(enable_timing=True)) for _ in range(n_roof)]
@@ -1313,6 +1334,8 @@ def main():
         },
         "step_launches": "decode with the normalisation in its launch, merge with block view"
                          if S > 1 else "decode with the normalisation in its launch, block view",
+        "step_back_to_back_us": {"fused": round(fused_step_us, 3),
+                                 "separate_launches": round(separate_step_us, 3)},
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
         "ceilings": ceilings,
         "decode_vs_ceilings": None if ceilings is None else {

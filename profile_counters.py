@@ -14,7 +14,8 @@ median duration of its dispatches, with the timeline split into phases at
 the first dispatch of each "kernel@grid" marker given (a benchmark that runs
 several workloads one after the other).
 
-`counters` averages every counter per dispatch for the decode kernel and the
+`counters` averages every counter per dispatch for the decode kernels (the
+launch that builds its own candidate lists apart from the plain one) and the
 row-gather diagnostic (whose launches come in two runs of equal length: the
 decode's placement first, then each row read once) and derives the figures
 quoted beside the benchmark.
@@ -153,8 +154,8 @@ def counters(out, command, *paths):
     for path in paths:
         for r in csv.DictReader(open(path)):
             k = short_name(r["Kernel_Name"])
-            if DECODE_KERNEL in k:
-                k = "sparse_mla_decode_kernel"
+            if DECODE_KERNEL in k:  # the launch that builds its lists, or the plain one
+                k = DECODE_KERNEL + (" (with normalisation)" if k.endswith("true>") else "")
             elif "row_gather" in k:  # the register or the LDS-ring variant
                 k = "row_gather_kernel"
             else:
