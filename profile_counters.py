@@ -15,8 +15,8 @@ the first dispatch of each "kernel@grid" marker given (a benchmark that runs
 several workloads one after the other).
 
 `counters` averages every counter per dispatch for the decode kernels (the
-launch that builds its own candidate lists apart from the plain one) and the
-row-gather diagnostic (whose launches come in two runs of equal length: the
+launch that builds its own candidate lists apart from the plain one), the
+dense decode and extend kernels and the row-gather diagnostic (whose launches come in two runs of equal length: the
 decode's placement first, then each row read once) and derives the figures
 quoted beside the benchmark.
 
@@ -34,6 +34,7 @@ import sys
 from collections import defaultdict
 
 DECODE_KERNEL = "sparse_mla_decode_kernel"
+OTHER_KERNELS = ("extend_attention_kernel", "paged_gqa_decode_kernel")
 COPY_BYTES = 256 << 20
 
 
@@ -158,7 +159,7 @@ def counters(out, command, *paths):
                 k = DECODE_KERNEL + (" (with normalisation)" if k.endswith("true>") else "")
             elif "row_gather" in k:  # the register or the LDS-ring variant
                 k = "row_gather_kernel"
-            else:
+            elif not any(name in k for name in OTHER_KERNELS):
                 continue
             d = groups[k][(path, int(r["Dispatch_Id"]))]
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
@@ -185,6 +186,9 @@ def counters(out, command, *paths):
         if "TCP_TCC_READ_REQ_sum" in m and m["TCP_TCC_READ_REQ_sum"]:
             lines.append(f"  -> mean L2 round trip seen by the L1 (cycles)  "
                          f"{m.get('TCP_TCC_READ_REQ_LATENCY_sum', 0) / m['TCP_TCC_READ_REQ_sum']:.0f}")
+        if "SQ_INSTS_VALU" in m and m.get("SQ_INSTS_MFMA"):
+            lines.append(f"  -> VALU instructions per MFMA                  "
+                         f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
             lines.append(f"  -> bf16 MFMA work (GFLOP, 512 flop per MOP)     "
                          f"{m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f}")
