@@ -351,9 +351,8 @@ constexpr int kHeadStride = kDV * 2 + 16;
 
 // All four waves copy the staged rows out, one whole 1 KiB head row per
 // store instruction: the final output, or the split's normalised partial.
-template <int kMode>
 __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeLds& L, int t,
-                                              int64_t part, int hg, int tid) {
+                                              int64_t part, int hg, int tid, bool final_out) {
 #pragma unroll 4
   for (int it = 0; it < 64 * 64 / kThreads; ++it) {
     const int idx = it * kThreads + tid;    // 64 lanes per head row of 1 KiB
@@ -362,9 +361,8 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
     if (head >= a.H) continue;
     const uintx4 v =
         *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
-    uint16_t* orow = kMode == kOutFinal
-                         ? a.out + ((int64_t)t * a.H + head) * kDV
-                         : (uint16_t*)a.o_part + (part * a.H + head) * kDV;
+    uint16_t* orow = final_out ? a.out + ((int64_t)t * a.H + head) * kDV
+                               : (uint16_t*)a.o_part + (part * a.H + head) * kDV;
     *(uintx4*)(orow + c * 8) = v;
   }
 }
@@ -731,10 +729,15 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
 // iteration i the slot of tile i - 1 (whose ids every wave is done with after
 // B(i)) takes tile i + kIdTiles - 1's ids by LDS DMA, as they are in
 // memory: position and range checks then happen where ids are read.
+// final_out (kOutFinal / kOutPartialBf16 epilogues only): the final output
+// and lse rather than the split's normalised partial and (m, l); a run-time
+// flag, so that a launch that writes both kinds (the queue launch) holds one
+// copy of the item.
 template <int kMode, bool kFp8 = false, bool kLong = false, bool kNorm = false>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
-                                            int hg, int64_t part, int sidx = 0) {
+                                            int hg, int64_t part, int sidx = 0,
+                                            bool final_out = kMode == kOutFinal) {
   // opaque per call, so that nothing derived from the thread index is hoisted
   // out of the queue launch's item loop (it would stay live across the whole
   // item and push the registers into spills)
@@ -937,7 +940,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     lds_barrier();  // statistics published
     if (kMode == kOutPartialF32) return;
     lds_barrier();  // output rows staged by the output waves
-    copy_out_rows<kMode>(a, L, t, part, hg, tid);
+    copy_out_rows(a, L, t, part, hg, tid, final_out);
     return;
   }
 
@@ -1231,7 +1234,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       }
   }
   lds_barrier();  // output rows staged
-  copy_out_rows<kMode>(a, L, t, part, hg, tid);
+  copy_out_rows(a, L, t, part, hg, tid, final_out);
   if (lane < 32) {
     // lse / (m, l): output wave j covers heads 32 j .. 32 j + 31, one lane each
     const int hl = 32 * j + (lane & 31);
@@ -1239,7 +1242,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     if (head < a.H) {
       const float m_ref = L.stat[hl], m_true = L.stat[64 + hl], l_tot = L.stat[128 + hl];
       const bool live = m_true != -INFINITY;
-      if (kMode == kOutFinal) {
+      if (final_out) {
         if (a.lse)
           a.lse[(int64_t)t * a.H + head] = live ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       } else {
@@ -1312,24 +1315,18 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     // pre-assigned, one to each workgroup of block id = q (mod 8) (no atomic
     // for a workgroup's first item), the rest are claimed with the queue head
     // (an atomic counter from 0) as item pre(q) + head
-    int qc[8];
-#pragma unroll
-    for (int y = 0; y < 8; ++y) qc[y] = a.qcount[y];
     const int idx = blockIdx.x >> 3;  // the pre-assigned item in queue x
     int4 e0 = make_int4(-1, 0, 0, 0);
     if (threadIdx.x == 0 && idx / a.G < a.qcap)  // read together with the counts
       e0 = *(const int4*)(a.qent + 4 * ((int64_t)x * a.qcap + idx / a.G));
-    auto qsel = [&](int q) {  // qc[q] without dynamic register indexing
-      int v = qc[0];
-#pragma unroll
-      for (int y = 1; y < 8; ++y) v = y == q ? qc[y] : v;
-      return v;
-    };
-    auto items = [&](int q) { return a.G * qsel(q); };
+    // the queue counts are read where they are used (by the claiming thread),
+    // so that nothing of them stays live across an item
+    auto items = [&](int q) { return a.G * a.qcount[q]; };
     auto pre = [&](int q) { return (grid - q + 7) >> 3; };
     bool dynamic = false;  // does any queue hold items beyond the pre-assigned ones?
 #pragma unroll
-    for (int y = 0; y < 8; ++y) dynamic |= a.G * qc[y] > ((grid - y + 7) >> 3);
+    for (int y = 0; y < 8; ++y) dynamic |= items(y) > pre(y);
+    dynamic = __builtin_amdgcn_readfirstlane(dynamic ? 1 : 0) != 0;
     int qi = 0;  // queues x, x + 1, ... (mod 8) before qi are exhausted
     bool first = true;
     __shared__ int s_ent[5];
@@ -1391,10 +1388,9 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       const int len = __builtin_amdgcn_readfirstlane(s_ent[2]);
       const int part = __builtin_amdgcn_readfirstlane(s_ent[3]);
       const int hg = __builtin_amdgcn_readfirstlane(s_ent[4]);
-      if (part < 0)  // the row's only task: its output is final
-        decode_item<kOutFinal>(a, L, s_bad, zero_row, row, lo, len, hg, 0);
-      else
-        decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, hg, (int64_t)part);
+      // a row's only task (slot -1) writes the row's final output itself
+      decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, hg, part < 0 ? 0 : (int64_t)part, 0,
+                         part < 0);
     }
   }
 }
