@@ -106,6 +106,37 @@ def test_host_side_validation():
                8, fake, fake, fake, fake, None) == STP_ERR_INVALID_ARG
     assert mbv(None, None, None, 0, 2, 4, 512, None, None, None, None, None, None, None, 0, 0, 16,
                8, None, None, None, None, None) == 0  # T = 0
+    # normalisation and decode in one call: both sets of checks before any launch
+    nd = lib.stp_normalize_and_decode
+    ndp = lib.stp_normalize_and_decode_partial_normalized
+    norm_ok = [fake, 8, fake, fake, 2, fake, 1, 4, 16, 2, 1, 11, fake, fake, fake, None, None]
+    bad_page = list(norm_ok)
+    bad_page[8] = 65
+    assert nd(*bad_page, None, None, None, fake, fake, 100, 16, 0.04, 1, None, 0, fake, None,
+              None) == STP_ERR_INVALID_ARG
+    assert b"page_size" in lib.stp_last_error()
+    small_cap = list(norm_ok)
+    small_cap[11] = 10  # < top_k + window + sinks
+    assert nd(*small_cap, None, None, None, fake, fake, 100, 16, 0.04, 1, None, 0, fake, None,
+              None) == STP_ERR_INVALID_ARG
+    assert nd(*norm_ok, None, None, None, fake, fake, 100, 16, float("nan"), 1, None, 0, fake,
+              None, None) == STP_ERR_INVALID_ARG
+    assert nd(*norm_ok, None, None, None, fake, fake, 100, 16, 0.04, 1, None, 0, None, None,
+              None) == STP_ERR_INVALID_ARG  # null out
+    with_view = list(norm_ok)
+    with_view[16] = fake  # blk_indptr without the other arrays
+    assert nd(*with_view, None, None, None, fake, fake, 100, 16, 0.04, 1, None, 0, fake, None,
+              None) == STP_ERR_INVALID_ARG
+    assert nd(*norm_ok, None, None, None, fake, fake, 100, 16, 0.04, 4, None, 0, fake, None,
+              None) == STP_ERR_WORKSPACE  # a split path without its workspace
+    assert ndp(*norm_ok, fake, fake, 100, 16, 0.04, 0, fake, fake, fake,
+               None) == STP_ERR_INVALID_ARG  # num_splits must be >= 1
+    assert ndp(*norm_ok, fake, fake, 100, 16, 0.04, 2, None, fake, fake,
+               None) == STP_ERR_INVALID_ARG
+    empty = list(norm_ok)
+    empty[4] = 0  # T = 0: nothing to do
+    assert nd(*empty, None, None, None, fake, fake, 100, 16, 0.04, 4, None, 0, None, None,
+              None) == 0
     # 16-byte row rule of the hot buffer (656 passes, 1000 fails)
     assert lib.stp_hot_lookup_swapin(None, 0, None, 1000, None, 0, None, None, None, 16, 17, 0, 0,
                                      None, None, None, None) == STP_ERR_INVALID_ARG
