@@ -33,6 +33,7 @@ otherwise be counted in every step.
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import sys
@@ -1253,8 +1254,17 @@ def main():
             stp.sparse_mla_decode(q, kv, nb["slot"], nb["count"], c0.scale, 1, out=out, lse=lse)
             stp.block_view_fill(nb, req, qpos, table, c0.page_size)
 
+    # both step forms enqueued back to back as the timed steps are; a1 alone
+    # (block view deferred) is too short to hide the host's launch cost, so
+    # its launches are captured in a HIP graph (16 over the rotated sets)
     fused_step_us = throughput_us(step_fused, n_roof, args.sets)
     separate_step_us = throughput_us(step_separate, n_roof, args.sets)
+    it_sets = itertools.cycle(range(args.sets))
+    norm_alone_us = graph_us(
+        lambda: stp.normalize_indices(topks[(k := next(it_sets))], req, qpos, table,
+                                      c0.page_size, c0.window, c0.num_sinks, cap, out=norm[k],
+                                      defer_block_view=True),
+        reps=2 * args.sets)
     merge_avg_us = throughput_us(merge_only, n_roof, args.sets) if S > 1 else 0.0
     roof_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                  torch.cuda.Event(enable_timing=True)) for _ in range(n_roof)]
@@ -1338,7 +1348,8 @@ def main():
         "step_launches": "decode with the normalisation in its launch, merge with block view"
                          if S > 1 else "decode with the normalisation in its launch, block view",
         "step_back_to_back_us": {"fused": round(fused_step_us, 3),
-                                 "separate_launches": round(separate_step_us, 3)},
+                                 "separate_launches": round(separate_step_us, 3),
+                                 "normalise_alone_graph": round(norm_alone_us, 3)},
         "effective_kv_gbps": round(kv_bytes / step_s / 1e9, 1),
         "ceilings": ceilings,
         "decode_vs_ceilings": None if ceilings is None else {

@@ -472,9 +472,10 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
   };
   const bool drop_writer = hg == a.G - 1 && sidx == 0;
   if (outw) {
+    // (limit < 0 for a padding row: nothing is set)
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
-      if ((unsigned)dv[u] <= (unsigned)limit) set_bit(dv[u]);
+      if (dv[u] >= 0 && dv[u] <= limit) set_bit(dv[u]);
     if (!pad) {
       if (a.window > 0)
         for (int p = max(0, q - a.window + 1) + otid; p <= min(q, limit); p += 128) set_bit(p);
@@ -497,7 +498,7 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int k = k0 + otid + 128 * u;
-        if ((unsigned)dv[u] <= (unsigned)limit) set_bit(dv[u]);
+        if (dv[u] >= 0 && dv[u] <= limit) set_bit(dv[u]);
         if (drop_writer && k < a.top_k) dl[k] = dv[u];
       }
     }
