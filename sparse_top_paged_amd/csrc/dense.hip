@@ -425,7 +425,6 @@ constexpr int kIdxChunk = 2048;  // slot ids staged in LDS at a time
 struct ExtLds {
   char tiles[kExtStages * kStageBytes];
   int32_t idx[kIdxChunk];
-  uint8_t ok[kExtStages][kTile];
 };
 
 struct ExtArgs {
@@ -487,10 +486,10 @@ void extend_attention_kernel(ExtArgs a) {
   // tile loads in flight).
   const int my_key0 = 16 * wave + (lane >> 4);  // + 4 u, the keys this lane loads
   int chunk = -1;
-  auto ensure_chunk = [&](int j) {  // all threads, before tile j's issue
+  auto ensure_chunk = [&](int j) {  // all threads, before tile j's ids are read
     const int c = j * kTile / kIdxChunk;
     if (c != chunk) {
-      __syncthreads();  // every issue from the current chunk is done
+      __syncthreads();  // every read of the current chunk is done
       for (int i = tid; i < kIdxChunk; i += kThreads) {
         const int e = c * kIdxChunk + i;
         L.idx[i] = e < jmax ? a.kvi[k_base + e] : -1;
@@ -499,21 +498,24 @@ void extend_attention_kernel(ExtArgs a) {
       __syncthreads();
     }
   };
-  auto issue = [&](int j) {
+  // Slot ids of tile j, read one iteration before the tile is issued (so
+  // that the LDS round trip overlaps a tile's compute): this lane's four
+  // keys (sl) and whether key `lane` of the tile is real (ok).
+  auto read_ids = [&](int j, int64_t (&sl)[4], bool& ok) {
     ensure_chunk(j);
-    const int stage = j % kExtStages;
-    int64_t sl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = j * kTile + my_key0 + 4 * u - chunk * kIdxChunk;
       const int64_t sv = (e >= 0 && e < kIdxChunk) ? L.idx[e] : -1;
       sl[u] = (sv >= 0 && sv < a.slots) ? sv : -1;
     }
+    const int e = j * kTile + lane - chunk * kIdxChunk;
+    const int64_t sv = (e >= 0 && e < kIdxChunk) ? L.idx[e] : -1;
+    ok = sv >= 0 && sv < a.slots;
+  };
+  auto issue = [&](int j, const int64_t (&sl)[4]) {
     issue_kv_rows((const uint8_t*)a.k, (const uint8_t*)a.v, head_bytes, g, zero_row,
-                  tiles_base + stage * kStageBytes, wave, lane, sl);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if ((lane & 15) == 0) L.ok[stage][my_key0 + 4 * u] = sl[u] >= 0 ? 1 : 0;
+                  tiles_base + (j % kExtStages) * kStageBytes, wave, lane, sl);
   };
 
   // Q^T fragments (B operand of S^T = K Q^T): query i0 + lane % 32, values
@@ -629,15 +631,27 @@ void extend_attention_kernel(ExtArgs a) {
         }
   };
 
-  // prologue: tile 0 in flight
-  if (ntiles > 0) issue(0);
+  // prologue: tile 0 in flight, tile 1's ids read
+  int64_t sl[4];
+  bool ok = false;
+  uint64_t okm_next = 0;
+  if (ntiles > 0) {
+    read_ids(0, sl, ok);
+    issue(0, sl);
+    okm_next = __ballot(ok);
+  }
+  if (ntiles > 1) read_ids(1, sl, ok);
   for (int it = 0; it < ntiles; ++it) {
     wait_vmcnt<0>();  // this wave's loads of tile it
     lds_barrier();    // tile it visible; every wave is done with tile it - 1
-    if (it + 1 < ntiles) issue(it + 1);  // into tile it - 1's stage
+    const uint64_t okm = okm_next;  // the keys of tile it that are real
+    if (it + 1 < ntiles) {
+      issue(it + 1, sl);  // into tile it - 1's stage
+      okm_next = __ballot(ok);
+    }
+    if (it + 2 < ntiles) read_ids(it + 2, sl, ok);
     const int stage = it % kExtStages;
     const int j0 = it * kTile;
-    const uint64_t okm = __ballot(L.ok[stage][lane] != 0);
     // no mask needed when every key is real and visible to every query
     const bool full = okm == ~0ull && j0 + kTile - 1 <= i0 + prefix && i0 + kQBlock <= Lq;
     if (active) tile(stage, j0, okm, !full);
