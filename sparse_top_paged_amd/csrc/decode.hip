@@ -734,7 +734,8 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
 // and lse rather than the split's normalised partial and (m, l); a run-time
 // flag, so that a launch that writes both kinds (the queue launch) holds one
 // copy of the item.
-template <int kMode, bool kFp8 = false, bool kLong = false, bool kNorm = false>
+template <int kMode, bool kFp8 = false, bool kLong = false, bool kNorm = false,
+          bool kPeel = true>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds& L, int* s_bad,
                                             const uint8_t* zero_row, int t, int lo, int len,
                                             int hg, int64_t part, int sidx = 0,
@@ -1046,29 +1047,45 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // load instructions of tile i+3 are spread between the MFMAs, one per MFMA
     // pair, so that the wave never stalls on a full load queue.  Past the last
     // tile nothing is loaded (and the wait before the barrier drains the queue).
-    for (int i = 1; i <= ntiles; ++i) {
+    // kPeel: the iterations that load (i + 3 < ntiles) and the last three,
+    // which do not, run as two loops, so that no load sits behind a branch
+    // (kLoads 1 and 0); otherwise one loop tests each load (kLoads 2, fewer
+    // registers where the item itself sits in a loop).
+    auto iteration = [&](int i, auto loads) {
+      constexpr int kLoads = decltype(loads)::value;
       refill_ids(i);  // (kLong) lands before B(i+1): the wait below leaves only tile i+3's loads
-      const bool real = i + 3 < ntiles;
-      const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row + ld_col;
-      const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row + ld_col;
+      const bool real = kLoads == 1 || (kLoads == 2 && i + 3 < ntiles);
+      const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row;
+      const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row;
       const int st3 = (i + 3) % kStages;
       const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
       auto load_chunk = [&](auto c) {
         constexpr int kC = decltype(c)::value;
-        if (!real) return;
-        if constexpr (kC < kSlotsPerThread)
+        if (kLoads == 0 || !real)
+          return;
+        else if constexpr (kC < kSlotsPerThread)
           load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
         else
           load_lds_16<(kC - kSlotsPerThread) * 128>(src1,
                                                     dst1 + (kC - kSlotsPerThread) * (1024 - 128));
       };
-      if (pv_iteration(i, load_chunk)) break;
+      if (pv_iteration(i, load_chunk)) return true;
       // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
       if (real)
         wait_vmcnt<2 * kSlotsPerThread>();
       else
         wait_vmcnt<0>();
       lds_barrier();  // B(i+1)
+      return false;
+    };
+    int i = 1;
+    if constexpr (kPeel) {
+      for (; i + 3 < ntiles; ++i) iteration(i, std::integral_constant<int, 1>{});
+      for (; i <= ntiles; ++i)
+        if (iteration(i, std::integral_constant<int, 0>{})) break;
+    } else {
+      for (; i <= ntiles; ++i)
+        if (iteration(i, std::integral_constant<int, 2>{})) break;
     }
   } else {
     // fp8 rows through registers: tile t is loaded during iteration t - 3
@@ -1297,15 +1314,16 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
     const int hg = rem - s * a.G;
     if (t >= a.T) return;
     if constexpr (kNorm) {
-      decode_item<kMode, false, false, true>(a, L, s_bad, zero_row, t, 0, 0, hg,
-                                             (int64_t)t * a.S + s, s);
+      decode_item<kMode, false, false, true, kMode != kOutPartialF32>(
+          a, L, s_bad, zero_row, t, 0, 0, hg, (int64_t)t * a.S + s, s);
     } else {
       int n = a.counts ? a.counts[t] : a.cap;
       n = min(max(n, 0), a.cap);
       const int chunk = (n + a.S - 1) / a.S;
       const int lo = min(n, s * chunk);
       const int len = min(n, lo + chunk) - lo;
-      decode_item<kMode, kFp8, kLong>(a, L, s_bad, zero_row, t, lo, len, hg,
+      decode_item<kMode, kFp8, kLong, false, kMode != kOutPartialF32>(a, L, s_bad, zero_row, t,
+                                                                     lo, len, hg,
                                       (int64_t)t * a.S + s);
     }
   } else {
@@ -1390,7 +1408,8 @@ void sparse_mla_decode_kernel(DecodeArgs a) {
       const int part = __builtin_amdgcn_readfirstlane(s_ent[3]);
       const int hg = __builtin_amdgcn_readfirstlane(s_ent[4]);
       // a row's only task (slot -1) writes the row's final output itself
-      decode_item<kMode>(a, L, s_bad, zero_row, row, lo, len, hg, part < 0 ? 0 : (int64_t)part, 0,
+      decode_item<kMode, false, false, false, false>(a, L, s_bad, zero_row, row, lo, len, hg,
+                                                     part < 0 ? 0 : (int64_t)part, 0,
                          part < 0);
     }
   }
