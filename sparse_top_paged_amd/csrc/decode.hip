@@ -345,25 +345,38 @@ __device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next
   }
 }
 
-// bf16 output rows staged in the tile ring as [64 heads][512] (head stride
-// 1040 B, so the 32 heads of a staging store hit different banks).
-constexpr int kHeadStride = kDV * 2 + 16;
+// The output waves stage O^T as it is, fp32 rows [64 heads][512] in the
+// tile ring (head stride 2064 B, so the 32 heads of a staging store hit
+// different banks); all four waves then scale each row by 1 / l of its head,
+// round it to bf16 and write it out (the final output, or the split's
+// normalised partial): wave w takes heads w, w + 4, ..., one row per step,
+// lane c values 4 c .. 4 c + 3 and 256 + 4 c .. 256 + 4 c + 3, so that the
+// LDS reads and the two 512-byte stores of a step are each contiguous.
+constexpr int kHeadStrideF = kDV * 4 + 16;
+static_assert(kHeadsPerWG * kHeadStrideF <= kStages * kTileBytes, "fp32 staging fits the ring");
 
-// All four waves copy the staged rows out, one whole 1 KiB head row per
-// store instruction: the final output, or the split's normalised partial.
 __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeLds& L, int t,
                                               int64_t part, int hg, int tid, bool final_out) {
+  const int lane = tid & 63, wave = tid >> 6;
+  // 1 / l of head `lane` (0 for a head that saw no candidate)
+  const float l_lane = L.stat[128 + lane];
+  const float inv_lane = l_lane > 0.f ? 1.f / l_lane : 0.f;
 #pragma unroll 4
-  for (int it = 0; it < 64 * 64 / kThreads; ++it) {
-    const int idx = it * kThreads + tid;    // 64 lanes per head row of 1 KiB
-    const int hl = idx >> 6, c = idx & 63;  // head, 16-byte chunk
+  for (int it = 0; it < kHeadsPerWG / 4; ++it) {
+    const int hl = 4 * it + wave;
     const int head = hg * kHeadsPerWG + hl;
-    if (head >= a.H) continue;
-    const uintx4 v =
-        *(const __attribute__((address_space(3))) uintx4*)(L.tiles + hl * kHeadStride + c * 16);
+    if (head >= a.H) break;  // heads past H come last
+    const float inv = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), hl));
+    const lds_t* row = L.tiles + hl * kHeadStrideF + lane * 16;
+    const floatx4 x0 = *(const __attribute__((address_space(3))) floatx4*)(row);
+    const floatx4 x1 = *(const __attribute__((address_space(3))) floatx4*)(row + 1024);
     uint16_t* orow = final_out ? a.out + ((int64_t)t * a.H + head) * kDV
                                : (uint16_t*)a.o_part + (part * a.H + head) * kDV;
-    *(uintx4*)(orow + c * 8) = v;
+    *(uintx2*)(orow + 4 * lane) =
+        uintx2{stp::pack_bf16x2(x0[0] * inv, x0[1] * inv), stp::pack_bf16x2(x0[2] * inv, x0[3] * inv)};
+    *(uintx2*)(orow + 256 + 4 * lane) =
+        uintx2{stp::pack_bf16x2(x1[0] * inv, x1[1] * inv), stp::pack_bf16x2(x1[2] * inv, x1[3] * inv)};
   }
 }
 
@@ -1233,23 +1246,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     return;
   }
 
-  // bf16 o / l (the final output, or a normalised split partial), staged
-  // through the idle tile ring, then written out by all four waves.
+  // bf16 o / l (the final output, or a normalised split partial): O^T staged
+  // in fp32 through the idle tile ring, then scaled, rounded and written out
+  // by all four waves.
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int hl = 32 * hb + (lane & 31);
-    const float l_tot = L.stat[128 + hl];
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    lds_t* hrow = L.tiles + hl * kHeadStride + dv_lane * 2;
+    lds_t* hrow = L.tiles + hl * kHeadStrideF + dv_lane * 4;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const uint32_t w0 = stp::pack_bf16x2(o[hb][mb][4 * rq] * inv, o[hb][mb][4 * rq + 1] * inv);
-        const uint32_t w1 = stp::pack_bf16x2(o[hb][mb][4 * rq + 2] * inv, o[hb][mb][4 * rq + 3] * inv);
-        *(__attribute__((address_space(3))) uintx2*)(hrow + (32 * mb + 8 * rq) * 2) =
-            uintx2{w0, w1};
-      }
+      for (int rq = 0; rq < 4; ++rq)
+        *(__attribute__((address_space(3))) floatx4*)(hrow + (32 * mb + 8 * rq) * 4) =
+            floatx4{o[hb][mb][4 * rq], o[hb][mb][4 * rq + 1], o[hb][mb][4 * rq + 2],
+                    o[hb][mb][4 * rq + 3]};
   }
   lds_barrier();  // output rows staged
   copy_out_rows(a, L, t, part, hg, tid, final_out);
