@@ -350,8 +350,8 @@ __device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next
 // different banks); all four waves then scale each row by 1 / l of its head,
 // round it to bf16 and write it out (the final output, or the split's
 // normalised partial): wave w takes heads w, w + 4, ..., one row per step,
-// lane c values 4 c .. 4 c + 3 and 256 + 4 c .. 256 + 4 c + 3, so that the
-// LDS reads and the two 512-byte stores of a step are each contiguous.
+// lane c values 8 c .. 8 c + 7, so that a step's store writes the whole
+// 1 KiB row.
 constexpr int kHeadStrideF = kDV * 4 + 16;
 static_assert(kHeadsPerWG * kHeadStrideF <= kStages * kTileBytes, "fp32 staging fits the ring");
 
@@ -368,15 +368,14 @@ __device__ __forceinline__ void copy_out_rows(const DecodeArgs& a, const DecodeL
     if (head >= a.H) break;  // heads past H come last
     const float inv = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), hl));
-    const lds_t* row = L.tiles + hl * kHeadStrideF + lane * 16;
+    const lds_t* row = L.tiles + hl * kHeadStrideF + lane * 32;
     const floatx4 x0 = *(const __attribute__((address_space(3))) floatx4*)(row);
-    const floatx4 x1 = *(const __attribute__((address_space(3))) floatx4*)(row + 1024);
+    const floatx4 x1 = *(const __attribute__((address_space(3))) floatx4*)(row + 16);
     uint16_t* orow = final_out ? a.out + ((int64_t)t * a.H + head) * kDV
                                : (uint16_t*)a.o_part + (part * a.H + head) * kDV;
-    *(uintx2*)(orow + 4 * lane) =
-        uintx2{stp::pack_bf16x2(x0[0] * inv, x0[1] * inv), stp::pack_bf16x2(x0[2] * inv, x0[3] * inv)};
-    *(uintx2*)(orow + 256 + 4 * lane) =
-        uintx2{stp::pack_bf16x2(x1[0] * inv, x1[1] * inv), stp::pack_bf16x2(x1[2] * inv, x1[3] * inv)};
+    *(uintx4*)(orow + 8 * lane) =
+        uintx4{stp::pack_bf16x2(x0[0] * inv, x0[1] * inv), stp::pack_bf16x2(x0[2] * inv, x0[3] * inv),
+               stp::pack_bf16x2(x1[0] * inv, x1[1] * inv), stp::pack_bf16x2(x1[2] * inv, x1[3] * inv)};
   }
 }
 
