@@ -1060,20 +1060,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // pair, so that the wave never stalls on a full load queue.  Past the last
     // tile nothing is loaded (and the wait before the barrier drains the queue).
     // kPeel: the iterations that load (i + 3 < ntiles) and the last three,
-    // which do not, run as two loops, so that no load sits behind a branch
-    // (kLoads 1 and 0); otherwise one loop tests each load (kLoads 2, fewer
-    // registers where the item itself sits in a loop).
+    // which do not, run as two loops (kLoads 1 and 0); otherwise one loop
+    // loads the zero row past the last tile (kLoads 2, into the free stage:
+    // fewer registers where the item itself sits in a loop).  Either way no
+    // load sits behind a branch.
     auto iteration = [&](int i, auto loads) {
       constexpr int kLoads = decltype(loads)::value;
       refill_ids(i);  // (kLong) lands before B(i+1): the wait below leaves only tile i+3's loads
       const bool real = kLoads == 1 || (kLoads == 2 && i + 3 < ntiles);
-      const uint8_t* src0 = real ? row_src(i + 3, 2 * j) : zero_row;
-      const uint8_t* src1 = real ? row_src(i + 3, 2 * j + 1) : zero_row;
+      // (kLoads 2) past the end the ids of the last tile are read, not used
+      const int ti = kLoads == 2 ? min(i + 3, ntiles - 1) : i + 3;
+      const uint8_t* src0 = kLoads == 0 ? zero_row : row_src(ti, 2 * j);
+      const uint8_t* src1 = kLoads == 0 ? zero_row : row_src(ti, 2 * j + 1);
+      if (kLoads == 2 && !real) {
+        src0 = zero_row + ld_col;
+        src1 = zero_row + ld_col;
+      }
       const int st3 = (i + 3) % kStages;
       const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
       auto load_chunk = [&](auto c) {
         constexpr int kC = decltype(c)::value;
-        if (kLoads == 0 || !real)
+        if constexpr (kLoads == 0)
           return;
         else if constexpr (kC < kSlotsPerThread)
           load_lds_16<kC * 128>(src0, dst0 + kC * (1024 - 128));
@@ -1083,10 +1090,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       };
       if (pv_iteration(i, load_chunk)) return true;
       // tile i+2 must have landed before B(i+1) (tile i+3 may stay in flight)
-      if (real)
-        wait_vmcnt<2 * kSlotsPerThread>();
-      else
+      if constexpr (kLoads == 0)
         wait_vmcnt<0>();
+      else
+        wait_vmcnt<2 * kSlotsPerThread>();
       lds_barrier();  // B(i+1)
       return false;
     };
