@@ -434,20 +434,28 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
   lds_i32* woff = dl + a.top_k;      // each word's offset within its wave's run, tagged
   lds_i32* red = (lds_i32*)L.stat;   // per-wave totals
 
-  // 1. request, position and D (output waves: the first 2048 entries in
-  //    registers), then the table row in flight while the bitmap is cleared
+  // 1. D (output waves: the first 2048 entries in registers), the request
+  //    and the position in one round trip (D does not depend on them), then
+  //    the table row in flight while the bitmap is cleared
   constexpr int kPer = 16;  // entries per output-wave thread per round (2048)
+  // (every wave issues the same loads, with no branch around them, so that
+  // the wait for r and q can leave the D loads in flight; the score waves'
+  // copies of D go unused)
   const int32_t* drow = a.topk + (int64_t)t * a.top_k;
-  const int r = a.req_id[t];
-  const int q = a.q_pos[t];
+  const int r_ld = a.req_id[t];
+  const int q_ld = a.q_pos[t];
+  // (top_k = 0: every load reads the request id, an in-bounds word)
+  const int32_t* dsrc = a.top_k > 0 ? drow : a.req_id + t;
+  const int dlast = max(a.top_k - 1, 0);
   int dv[kPer];
-  if (outw) {
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int k = otid + 128 * u;
-      dv[u] = k < a.top_k ? drow[k] : -1;
-    }
-  }
+  for (int u = 0; u < kPer; ++u) dv[u] = dsrc[min((tid & 127) + 128 * u, dlast)];
+  __builtin_amdgcn_sched_barrier(0);  // the D loads go out before the wait for r and q
+  const int r = __builtin_amdgcn_readfirstlane(r_ld);
+  const int q = __builtin_amdgcn_readfirstlane(q_ld);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (otid + 128 * u >= a.top_k) dv[u] = -1;
   const bool pad = r < 0 || r >= a.num_reqs || q < 0;
   const int P = a.P;
   const int limit = pad ? -1 : min(q, a.max_blocks * P - 1);  // last visible position
@@ -456,11 +464,11 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
   const int32_t* g_table = a.block_table + (int64_t)(pad ? 0 : r) * a.max_blocks;
   int tv[kPer];
   if (outw) {
+    // no branch per load (used_blocks = 0: the request id again)
+    const int32_t* tsrc = used_blocks > 0 ? g_table : a.req_id + t;
+    const int tlast = max(used_blocks - 1, 0);
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int k = otid + 128 * u;
-      tv[u] = k < used_blocks ? g_table[k] : -1;
-    }
+    for (int u = 0; u < kPer; ++u) tv[u] = tsrc[min(otid + 128 * u, tlast)];
   } else {
     issue_q();
   }
@@ -558,12 +566,30 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
   }
   int my_drop = 0;
   if (drop_writer && !pad) {
-    for (int k = tid; k < a.top_k; k += kThreads) {
-      const int p = dl[k];
-      if (p >= 0) {
-        const bool in = p <= limit;
-        const int b = div_p(in ? p : 0, a.pdiv);
-        my_drop += (in && p - b * P <= last_off(b)) ? 0 : 1;
+    // eight entries per thread at a time, their LDS reads issued together
+    constexpr int kDU = 8;
+    for (int k0 = 0; k0 < a.top_k; k0 += kDU * kThreads) {
+      int p[kDU], b[kDU], pg[kDU];
+#pragma unroll
+      for (int u = 0; u < kDU; ++u) {
+        const int k = k0 + tid + kThreads * u;
+        p[u] = k < a.top_k ? dl[k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kDU; ++u) {
+        b[u] = div_p(p[u] >= 0 && p[u] <= limit ? p[u] : 0, a.pdiv);
+        pg[u] = tbl[b[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kDU; ++u) {
+        if (p[u] < 0) continue;
+        const bool in = p[u] <= limit;
+        int keep = -1;  // last visible offset of block b (as last_off)
+        if (pg[u] >= 0) {
+          const int64_t room = (int64_t)INT32_MAX - (int64_t)pg[u] * P;
+          keep = room >= P - 1 ? P - 1 : (int)max(room, (int64_t)-1);
+        }
+        my_drop += (in && p[u] - b[u] * P <= keep) ? 0 : 1;
       }
     }
   }
