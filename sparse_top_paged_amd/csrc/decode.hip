@@ -502,7 +502,7 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
       const int na = min(min(a.num_sinks, q + 1), limit + 1);
       for (int p = otid; p < na; p += 128) set_bit(p);
     }
-    if (drop_writer) {
+    if (drop_writer && a.top_k > kPer * 128) {  // (a shorter D stays in registers)
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int k = otid + 128 * u;
@@ -564,36 +564,28 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
       }
     }
   }
+  lds_barrier();  // bitmap complete
+
+  // D's dropped entries (the workgroup that writes the count): an entry >= 0
+  // is kept iff it is at most the limit and its bit survived the clearing
+  // above, which removed exactly the positions past their block's last
+  // visible slot.  A D of at most 2048 entries is still in the output
+  // waves' registers; a longer one was staged in LDS.
   int my_drop = 0;
   if (drop_writer && !pad) {
-    // eight entries per thread at a time, their LDS reads issued together
-    constexpr int kDU = 8;
-    for (int k0 = 0; k0 < a.top_k; k0 += kDU * kThreads) {
-      int p[kDU], b[kDU], pg[kDU];
+    auto dropped = [&](int p) {
+      if (p < 0) return 0;
+      return (p <= limit && ((bm32[p >> 5] >> (p & 31)) & 1) != 0) ? 0 : 1;
+    };
+    if (a.top_k <= kPer * 128) {
+      if (outw) {
 #pragma unroll
-      for (int u = 0; u < kDU; ++u) {
-        const int k = k0 + tid + kThreads * u;
-        p[u] = k < a.top_k ? dl[k] : -1;
+        for (int u = 0; u < kPer; ++u) my_drop += dropped(dv[u]);
       }
-#pragma unroll
-      for (int u = 0; u < kDU; ++u) {
-        b[u] = div_p(p[u] >= 0 && p[u] <= limit ? p[u] : 0, a.pdiv);
-        pg[u] = tbl[b[u]];
-      }
-#pragma unroll
-      for (int u = 0; u < kDU; ++u) {
-        if (p[u] < 0) continue;
-        const bool in = p[u] <= limit;
-        int keep = -1;  // last visible offset of block b (as last_off)
-        if (pg[u] >= 0) {
-          const int64_t room = (int64_t)INT32_MAX - (int64_t)pg[u] * P;
-          keep = room >= P - 1 ? P - 1 : (int)max(room, (int64_t)-1);
-        }
-        my_drop += (in && p[u] - b[u] * P <= keep) ? 0 : 1;
-      }
+    } else {
+      for (int k = tid; k < a.top_k; k += kThreads) my_drop += dropped(dl[k]);
     }
   }
-  lds_barrier();  // bitmap complete
 
   // counts: each wave scans its run of 64-word batches; a word's (and a
   // batch's) offset is stored within the run, tagged with the wave, and the

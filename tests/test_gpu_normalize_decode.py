@@ -7,8 +7,9 @@ the attention at the bf16 bar.  Covered: the single launch (splits within the
 LDS id list, bitmap and table row within two ring stages) at the
 DeepSeek-shaped size and on small ragged batches with padding rows,
 unmapped pages, invalid ids, slots past the pool, one and two head groups and
-a single pass; the two-launch forms (a single pass over more ids than the
-list holds, a bitmap past 72 KiB)."""
+a single pass, a top-k list longer than the 2048 entries the output waves
+hold in registers; the two-launch forms (a single pass over more ids than
+the list holds, a bitmap past 72 KiB)."""
 
 import numpy as np
 import pytest
@@ -129,6 +130,14 @@ def test_bitmap_past_two_ring_stages():
     c, q, kv = _small(13, 3, 16, 2, rows=200000, R=2, ctx=300000, top_k=400, window=50, sinks=2,
                       page_size=1, unmapped_frac=0.01)
     _run(c, q, kv, 2, oracle_tokens=(0,))
+
+
+def test_topk_longer_than_one_register_round():
+    # 2600 top-k entries: past the 2048 the output waves hold in registers,
+    # so D is staged in LDS for the dropped count
+    c, q, kv = _small(16, 4, 16, 4, R=2, ctx=20000, top_k=2600, window=64, sinks=4,
+                      page_size=64, unmapped_frac=0.02)
+    _run(c, q, kv, 4, oracle_tokens=(0, 3))
 
 
 def test_empty_batch():
