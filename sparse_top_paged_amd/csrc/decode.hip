@@ -98,9 +98,9 @@ constexpr int kFp8ScaleOff = 512;
 constexpr int kFp8RopeOff = 528;
 
 struct Fp8Rows {
-  uintx4 lat[2][4];  // [h][line]
-  floatx4 scl[2];    // [h]
-  uintx4 rope[2];    // [h]
+  uintx4 lat[4];  // [line]
+  floatx4 scl;
+  uintx4 rope;
 };
 
 // bf16(f32(code) * scale) of the eight codes in (w0, w1), packed in order
@@ -271,12 +271,12 @@ __device__ __forceinline__ void qk_tile(const lds_t* stage, const int (&k_base)[
 // exponent's FMA; exp2(-inf) = 0 covers masked rows), since VALU work beyond
 // about four instructions per MFMA slows the MFMA stream.  Branch-free.
 // Requires scale_log2 > 0, so that max(z) * scale = max(z * scale).
-template <bool kNext, bool kMasked>
+template <bool kNext, bool kMasked, typename StepFn>
 __device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next,
                                            const int (&k_base)[4],
                                            const bf16x8 (&qf)[kQKSteps], const SAcc& cur,
                                            SAcc& nxt, uint32_t vmask, float scale_log2, int buf,
-                                           int j, int lane, ScoreState& st) {
+                                           int j, int lane, ScoreState& st, StepFn&& step_fn) {
   shortx8 kf[kKRing];
   if constexpr (kNext) {
     nxt.c0 = floatx16{};
@@ -341,6 +341,7 @@ __device__ __forceinline__ void score_step(const DecodeLds& L, const lds_t* next
       row_exp(ks - 17);
     else if (ks == 33)
       publish();
+    step_fn(ks);
     if constexpr (kNext) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -887,6 +888,75 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     }
   }
 
+  // fp8 rows: each wave stages one row group of every tile through its
+  // registers (score wave j group 2 j + 1, output wave j group 2 j): lane l
+  // takes row l / 8 of the group and, of it, 16-byte chunk l % 8 of each
+  // 128-byte latent line, its RoPE chunk and the four scales.  Tile t is
+  // loaded one iteration before it is dequantised into its ring stage (in
+  // the window between B(t - 2) and B(t - 1); stage (t - 2) % 4 is then
+  // free: tile t - 4's V^T was read in iteration t - 4 and its K before);
+  // tiles 0 and 1 are written before B(0).  Past the last tile the zero row
+  // is loaded, so every iteration does the same work.
+  const int f8_grp = score ? 2 * j + 1 : 2 * j;
+  const int rl = lane >> 3, u8 = lane & 7;
+  auto fp8_row = [&](int tile) {
+    const int id = tile < ntiles ? id_at(tile, f8_grp * kGroupRows + rl) : -1;
+    return id >= 0 ? a.kv8 + (int64_t)id * kFp8RowBytes : zero_row;
+  };
+  // LDS offsets in a stage: latent chunk 16 line + 2 u + half of group row
+  // rl sits in block 2 line + u / 4 at position ((2 u + half) % 8) ^ rl;
+  // RoPE chunk u in block 8 at position u ^ rl
+  int lat_off[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+    lat_off[half] = f8_grp * kGroupBytes + (u8 >> 2) * 1024 + rl * 128 +
+                    ((((2 * u8 + half) & 7) ^ rl) << 4);
+  const int rope_off = f8_grp * kGroupBytes + 8 * 1024 + rl * 128 + ((u8 ^ rl) << 4);
+  // global (not flat) loads: a flat load also counts against the LDS
+  // counter, so every LDS wait would wait for the rows in flight too
+  typedef const __attribute__((address_space(1))) uintx4 g_uintx4;
+  typedef const __attribute__((address_space(1))) floatx4 g_floatx4;
+  auto load_latent = [&](Fp8Rows& b, int line, const uint8_t* p) {
+    b.lat[line] = *(g_uintx4*)(p + 128 * line + 16 * u8);
+  };
+  auto load_rope = [&](Fp8Rows& b, const uint8_t* p) {
+    b.rope = *(g_uintx4*)(p + kFp8RopeOff + 16 * u8);
+  };
+  auto load_scales = [&](floatx4& sc, const uint8_t* p) { sc = *(g_floatx4*)(p + kFp8ScaleOff); };
+  auto load_all = [&](Fp8Rows& b, int tile) {
+    const uint8_t* p = fp8_row(tile);
+    load_scales(b.scl, p);
+#pragma unroll
+    for (int line = 0; line < 4; ++line) load_latent(b, line, p);
+    load_rope(b, p);
+  };
+  auto store_half = [&](const Fp8Rows& b, int line, int half, lds_t* stage) {
+    const uintx4 d = b.lat[line];
+    const uintx4 w = half ? dequant8(d[2], d[3], b.scl[line]) : dequant8(d[0], d[1], b.scl[line]);
+    *(__attribute__((address_space(3))) uintx4*)(stage + 2 * line * 1024 + lat_off[half]) = w;
+  };
+  auto store_rope = [&](const Fp8Rows& b, lds_t* stage) {
+    *(__attribute__((address_space(3))) uintx4*)(stage + rope_off) = b.rope;
+  };
+  auto store_all = [&](const Fp8Rows& b, lds_t* stage) {
+#pragma unroll
+    for (int line = 0; line < 4; ++line) {
+      store_half(b, line, 0, stage);
+      store_half(b, line, 1, stage);
+    }
+    store_rope(b, stage);
+  };
+  Fp8Rows fb;  // (fp8) the tile being staged
+  // tiles 0 and 1 into stages 0 and 1, tile 2 loaded (before B(0))
+  auto fp8_prologue = [&]() {
+    Fp8Rows f0;
+    load_all(f0, 0);
+    load_all(fb, 1);
+    store_all(f0, L.tiles);
+    store_all(fb, L.tiles + kTileBytes);
+    load_all(fb, 2);
+  };
+
   // Pipeline over the ring of kStages = 4 tiles, with P(i) the published P^T
   // of tile i (pbuf[i % 2]) and B(i) the i-th workgroup barrier:
   //   prologue: query rows (stages 2, 3) and tiles 0, 1 enqueued and landed;
@@ -925,6 +995,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     }
     ScoreState st{-INFINITY, -INFINITY, 0.f};
     SAcc acc_a, acc_b;
+    if constexpr (kFp8) fp8_prologue();  // (stages 0 and 1; Q^T is in registers)
     lds_barrier();  // B(0): tiles 0 and 1 visible, Q^T read out of stages 2 and 3
     if (ntiles > 0) qk_tile(L.tiles, k_base, qf, acc_a);
     // iteration i: softmax of tile i (S^T in registers) with the QK of tile
@@ -933,17 +1004,37 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
     // last tile peeled off, so that the loop body holds one straight-line
     // variant of the step (a branch between variants would let the compiler
     // hoist their common softmax arithmetic out of the MFMA stream).
+    // (fp8 rows) iteration i also dequantises this wave's group of tile
+    // i + 2 into its stage and loads tile i + 3 into the same registers: a
+    // half line every fourth MFMA (the line reloaded after its second half),
+    // the RoPE chunk after, the new scales into registers of their own
     auto full = [&](auto masked, int i, const SAcc& cur, SAcc& nxt) {
       constexpr bool kMasked = decltype(masked)::value;
+      lds_t* stage = L.tiles + ((i + 2) % kStages) * kTileBytes;
+      const uint8_t* pn = kFp8 ? fp8_row(i + 3) : zero_row;
+      floatx4 nscl;
+      if constexpr (kFp8) load_scales(nscl, pn);
       score_step<true, kMasked>(L, L.tiles + ((i + 1) % kStages) * kTileBytes, k_base, qf, cur,
                                 nxt, kMasked ? tile_mask(i) : ~0u, a.scale_log2, i & 1, j, lane,
-                                st);
+                                st, [&](int ks) {
+                                  if constexpr (kFp8) {
+                                    if (ks >= 2 && ks <= 30 && (ks & 3) == 2) {
+                                      const int n = (ks - 2) >> 2, line = n >> 1, half = n & 1;
+                                      store_half(fb, line, half, stage);
+                                      if (half) load_latent(fb, line, pn);
+                                    } else if (ks == 34) {
+                                      store_rope(fb, stage);
+                                      load_rope(fb, pn);
+                                    }
+                                  }
+                                });
+      if constexpr (kFp8) fb.scl = nscl;
       lds_barrier();
     };
     auto last = [&](int i, const SAcc& cur) {
       SAcc none;
       score_step<false, true>(L, L.tiles, k_base, qf, cur, none, tile_mask(i), a.scale_log2,
-                              i & 1, j, lane, st);
+                              i & 1, j, lane, st, [](int) {});
       lds_barrier();
     };
     auto run = [&](auto masked) {
@@ -1125,78 +1216,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
         if (iteration(i, std::integral_constant<int, 2>{})) break;
     }
   } else {
-    // fp8 rows through registers: tile t is loaded during iteration t - 3
-    // (into one buffer of registers, a line at a time as the previous tile's
-    // line leaves it) and dequantised into its ring stage during iteration
-    // t - 2 (stage (t - 2) % 4 is then free: tile t - 4's V^T was read in
-    // iteration t - 4 and its K before).  Tiles 0 and 1 are written before
-    // B(0), tile 2 between B(0) and B(1); past the last tile the zero row is
-    // loaded, so every iteration does the same work.
-    const int rl = lane >> 3, u = lane & 7;
-    auto fp8_row = [&](int tile, int h) {
-      const int id = tile < ntiles ? id_at(tile, (2 * j + h) * kGroupRows + rl) : -1;
-      return id >= 0 ? a.kv8 + (int64_t)id * kFp8RowBytes : zero_row;
-    };
-    // LDS offsets in a stage: latent chunk 16 line + 2 u + half of group row
-    // rl sits in block 2 line + u / 4 at position ((2 u + half) % 8) ^ rl;
-    // RoPE chunk u in block 8 at position u ^ rl
-    int lat_off[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-      lat_off[half] = (u >> 2) * 1024 + rl * 128 + ((((2 * u + half) & 7) ^ rl) << 4);
-    const int rope_off = 8 * 1024 + rl * 128 + ((u ^ rl) << 4);
-    // global (not flat) loads: a flat load also counts against the LDS
-    // counter, so every LDS wait would wait for the rows in flight too
-    typedef const __attribute__((address_space(1))) uintx4 g_uintx4;
-    typedef const __attribute__((address_space(1))) floatx4 g_floatx4;
-    auto load_latent = [&](Fp8Rows& b, int h, int line, const uint8_t* p) {
-      b.lat[h][line] = *(g_uintx4*)(p + 128 * line + 16 * u);
-    };
-    auto load_rope = [&](Fp8Rows& b, int h, const uint8_t* p) {
-      b.rope[h] = *(g_uintx4*)(p + kFp8RopeOff + 16 * u);
-    };
-    auto load_scales = [&](floatx4& sc, const uint8_t* p) { sc = *(g_floatx4*)(p + kFp8ScaleOff); };
-    auto load_all = [&](Fp8Rows& b, int tile) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint8_t* p = fp8_row(tile, h);
-        load_scales(b.scl[h], p);
-#pragma unroll
-        for (int line = 0; line < 4; ++line) load_latent(b, h, line, p);
-        load_rope(b, h, p);
-      }
-    };
-    auto store_half = [&](const Fp8Rows& b, int h, int line, int half, lds_t* stage) {
-      const uintx4 d = b.lat[h][line];
-      const uintx4 w = half ? dequant8(d[2], d[3], b.scl[h][line])
-                            : dequant8(d[0], d[1], b.scl[h][line]);
-      *(__attribute__((address_space(3))) uintx4*)(
-          stage + (2 * j + h) * kGroupBytes + 2 * line * 1024 + lat_off[half]) = w;
-    };
-    auto store_rope = [&](const Fp8Rows& b, int h, lds_t* stage) {
-      *(__attribute__((address_space(3))) uintx4*)(stage + (2 * j + h) * kGroupBytes +
-                                                    rope_off) = b.rope[h];
-    };
-    auto store_all = [&](const Fp8Rows& b, lds_t* stage) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int line = 0; line < 4; ++line) {
-          store_half(b, h, line, 0, stage);
-          store_half(b, h, line, 1, stage);
-        }
-        store_rope(b, h, stage);
-      }
-    };
-    Fp8Rows fb;
-    {
-      Fp8Rows f0;  // prologue only
-      load_all(f0, 0);
-      load_all(fb, 1);
-      store_all(f0, L.tiles);
-    }
-    store_all(fb, L.tiles + kTileBytes);
-    load_all(fb, 2);
+    // fp8 rows (this wave's group 2 j, see above)
+    fp8_prologue();
     lds_barrier();  // B(0): tiles 0 and 1 written, stages 2 and 3 free again
     if (ntiles > 0) {
       store_all(fb, L.tiles + 2 * kTileBytes);
@@ -1205,37 +1226,33 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       lds_barrier();  // B(1): P(0) published, tile 2 written
     }
     // iteration i: dequantise tile i+2 into its stage while loading tile i+3
-    // into the same registers: tile i+3's scales first (into registers of
-    // their own, taken over at the end), then a latent half-line per MFMA
-    // pair (the line reloaded after its second half), the RoPE chunks after
+    // into the same registers: the scales first (into registers of their
+    // own, taken over at the end), then a half line on every other MFMA
+    // pair (the line reloaded after its second half), the RoPE chunk after
     // the last pair
     for (int i = 1; i <= ntiles; ++i) {
       refill_ids(i);
       lds_t* stage = L.tiles + ((i + 2) % kStages) * kTileBytes;
-      const uint8_t* p0 = fp8_row(i + 3, 0);
-      const uint8_t* p1 = fp8_row(i + 3, 1);
-      floatx4 nscl[2];
-      load_scales(nscl[0], p0);
-      load_scales(nscl[1], p1);
+      const uint8_t* pn = fp8_row(i + 3);
+      floatx4 nscl;
+      load_scales(nscl, pn);
       auto step = [&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        if constexpr (k < 16) {
-          constexpr int h = k >> 3, line = (k >> 1) & 3, half = k & 1;
-          store_half(fb, h, line, half, stage);
-          if constexpr (half == 1) load_latent(fb, h, line, h ? p1 : p0);
-        } else {
-          constexpr int h = k - 16;
-          store_rope(fb, h, stage);
-          load_rope(fb, h, h ? p1 : p0);
+        if constexpr (k < 16 && k % 2 == 0) {
+          constexpr int n = k / 2, line = n >> 1, half = n & 1;
+          store_half(fb, line, half, stage);
+          if constexpr (half == 1) load_latent(fb, line, pn);
+        } else if constexpr (k == 16) {
+          store_rope(fb, stage);
+          load_rope(fb, pn);
         }
       };
       const bool last = pv_iteration(i, step);
-      fb.scl[0] = nscl[0];
-      fb.scl[1] = nscl[1];
+      fb.scl = nscl;
       if (last) break;
       // (kLong) the id refill of the previous iteration has landed: only this
-      // iteration's 12 row loads may still be in flight
-      if constexpr (kLong) wait_vmcnt<12>();
+      // iteration's six row loads may still be in flight
+      if constexpr (kLong) wait_vmcnt<6>();
       lds_barrier();  // B(i+1): tile i+2 written
     }
   }
