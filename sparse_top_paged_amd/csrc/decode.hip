@@ -40,7 +40,9 @@
 // output waves issue tile loads, three tiles ahead, spread between their
 // MFMAs.  One LDS-only workgroup barrier per tile hands over P^T, publishes
 // the next tile and frees a ring stage.  Invalid candidates load a zero row
-// and are masked to -inf before the exponent.
+// and are masked to -inf before the exponent.  At the end the output waves
+// stage O^T in fp32 through the idle ring, and all four waves scale, round
+// and write the rows.
 
 #include <mutex>
 #include <type_traits>
@@ -86,13 +88,14 @@ typedef __attribute__((address_space(3))) shortx8 lds_shortx8;
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytes] = {};
 
 // fp8_ds_mla rows: 512 E4M3 latent codes, four float32 scales (one per 128
-// values), 64 bf16 RoPE values.  The output waves stage them through
-// registers and write the dequantised row, bf16(f32(code) * scale) for the
-// latent values and the RoPE values as they are, into the tile layout of the
-// ring, so that every later step is the bf16 path's.  Output wave j handles
-// the 16 rows of its two groups 2 j + h (h = 0, 1): lane l takes row l / 8 of
-// the group and, of it, 16-byte chunk l % 8 of each 128-byte latent line
-// (codes 128 line + 16 (l % 8) .. + 15), RoPE chunk l % 8 and the four scales.
+// values), 64 bf16 RoPE values.  The waves stage them through registers and
+// write the dequantised row, bf16(f32(code) * scale) for the latent values
+// and the RoPE values as they are, into the tile layout of the ring, so that
+// every later step is the bf16 path's.  Each wave handles one 8-row group of
+// a tile (score wave j group 2 j + 1, output wave j group 2 j): lane l takes
+// row l / 8 of the group and, of it, 16-byte chunk l % 8 of each 128-byte
+// latent line (codes 128 line + 16 (l % 8) .. + 15), RoPE chunk l % 8 and
+// the four scales.
 constexpr int kFp8RowBytes = 656;
 constexpr int kFp8ScaleOff = 512;
 constexpr int kFp8RopeOff = 528;
@@ -874,8 +877,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   auto issue_group = [&](int i, int st, int grp) {
     load_row_chunks<0>(row_src(i, grp), group_dst(st, grp));
   };
-  // Only the output waves load tiles (two row groups each), so the score
-  // waves -- the longer path per tile -- never wait on load issue.
+  // Only the output waves load tiles (two row groups each); the score waves'
+  // QK MFMAs and softmax stay free of load issue (one group from every wave
+  // measured no faster).
   auto issue = [&](int i, int st) {
     issue_group(i, st, 2 * j);
     issue_group(i, st, 2 * j + 1);
