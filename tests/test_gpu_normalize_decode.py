@@ -140,6 +140,12 @@ def test_topk_longer_than_one_register_round():
     _run(c, q, kv, 4, oracle_tokens=(0, 3))
 
 
+def test_no_topk_entries():
+    # top_k = 0: the window and the sinks alone
+    c, q, kv = _small(17, 5, 16, 2, R=2, ctx=600, top_k=0, window=40, sinks=3, page_size=16)
+    _run(c, q, kv, 2, oracle_tokens=(0, 4))
+
+
 def test_empty_batch():
     c, q, kv = _small(14, 0, 16, 2, R=1, ctx=100, top_k=8, window=2, sinks=1, page_size=16)
     _run(c, q, kv, 2)
