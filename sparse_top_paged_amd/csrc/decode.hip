@@ -1151,10 +1151,24 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   };
 
   if constexpr (!kFp8) {
+    // ids of this lane's two rows of the tile that the next iteration
+    // enqueues (clamped to the last tile), read one iteration ahead: the
+    // loop's first MFMA then waits for P^T and the factors only, not for
+    // two id round trips before them
+    int nid[2];
+    auto read_next_ids = [&](int tile) {
+      const int tc = min(tile, ntiles - 1);
+      nid[0] = id_at(tc, 2 * j * kGroupRows + (lane >> 3));
+      nid[1] = id_at(tc, (2 * j + 1) * kGroupRows + (lane >> 3));
+    };
+    auto id_src = [&](int id) {
+      return (id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : zero_row) + ld_col;
+    };
     wait_vmcnt<0>();  // tiles 0 and 1
     lds_barrier();    // B(0): stages 2 and 3 are free again
     if (ntiles > 0) {
       if (ntiles > 2) issue(2, 2);
+      read_next_ids(4);
       read_v(L.tiles, v0, v1);
       // tile 2 must have landed before B(1) (tile 3 may stay in flight)
       if (ntiles > 3) {
@@ -1181,10 +1195,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       constexpr int kLoads = decltype(loads)::value;
       refill_ids(i);  // (kLong) lands before B(i+1): the wait below leaves only tile i+3's loads
       const bool real = kLoads == 1 || (kLoads == 2 && i + 3 < ntiles);
-      // (kLoads 2) past the end the ids of the last tile are read, not used
-      const int ti = kLoads == 2 ? min(i + 3, ntiles - 1) : i + 3;
-      const uint8_t* src0 = kLoads == 0 ? zero_row : row_src(ti, 2 * j);
-      const uint8_t* src1 = kLoads == 0 ? zero_row : row_src(ti, 2 * j + 1);
+      // tile i+3's ids (kLoads 2: past the end those of the last tile, not
+      // used)
+      const uint8_t* src0 = kLoads == 0 ? zero_row : id_src(nid[0]);
+      const uint8_t* src1 = kLoads == 0 ? zero_row : id_src(nid[1]);
       if (kLoads == 2 && !real) {
         src0 = zero_row + ld_col;
         src1 = zero_row + ld_col;
@@ -1193,6 +1207,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
       const uint32_t dst0 = group_dst(st3, 2 * j), dst1 = group_dst(st3, 2 * j + 1);
       auto load_chunk = [&](auto c) {
         constexpr int kC = decltype(c)::value;
+        if constexpr (kLoads != 0 && kC == 1) read_next_ids(i + 4);
         if constexpr (kLoads == 0)
           return;
         else if constexpr (kC < kSlotsPerThread)
