@@ -424,16 +424,25 @@ __host__ __device__ constexpr int64_t norm_lds_bytes(int64_t nwords, int64_t max
   return nwords * 8 + max_blocks * 4 + top_k * 4 + nwords * 4 + (nwords / 64 + 1) * 4;
 }
 
-template <class IssueQ>
+// Whether the normalisation's LDS fits in ring stage 1 alone, which leaves
+// stage 0 free for tile 0 while the list is still being finished.
+__device__ __forceinline__ bool norm_in_stage1(const DecodeArgs& a) {
+  return norm_lds_bytes(a.nwords_alloc, a.max_blocks, a.top_k) <= kTileBytes;
+}
+
+template <class IssueQ, class IssueT0>
 __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const DecodeLds& L,
                                                 int* s_bad, int t, int sidx, int hg, int& lo_out,
-                                                int& len_out, IssueQ&& issue_q) {
+                                                int& len_out, IssueQ&& issue_q,
+                                                IssueT0&& issue_tile0) {
   using stp::bv::div_p;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool outw = wave >= 2;  // output waves load; score waves enqueue the query rows
   const int otid = tid - 128;   // thread index among the output waves
-  lds_u64* bm = (lds_u64*)L.tiles;
-  lds_i32* tbl = (lds_i32*)(L.tiles + (size_t)a.nwords_alloc * 8);
+  const bool early = norm_in_stage1(a);
+  lds_t* nbase = L.tiles + (early ? kTileBytes : 0);
+  lds_u64* bm = (lds_u64*)nbase;
+  lds_i32* tbl = (lds_i32*)(nbase + (size_t)a.nwords_alloc * 8);
   lds_i32* dl = tbl + a.max_blocks;  // D
   lds_i32* woff = dl + a.top_k;      // each word's offset within its wave's run, tagged
   lds_i32* red = (lds_i32*)L.stat;   // per-wave totals
@@ -489,7 +498,7 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
   //    in the bitmap while the table row is in flight, then stage the table
   //    row (and D, for the workgroup that counts the dropped entries)
   // (32-bit atomics on the 64-bit words' halves)
-  lds_i32* bm32 = (lds_i32*)L.tiles;
+  lds_i32* bm32 = (lds_i32*)nbase;
   auto set_bit = [&](int p) {
     __hip_atomic_fetch_or(&bm32[p >> 5], 1 << (p & 31), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -698,13 +707,39 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
     int32_t* tok_row = a.tok_out + (int64_t)t * a.cap;
     int32_t* slot_row = a.slot_out + (int64_t)t * a.cap;
     int bad = 0;
+    // (normalisation in stage 1) tile 0 first: output wave j turns rows
+    // 16 j .. 16 j + 15 into slots and enqueues them into stage 0 at once,
+    // so that the gather of the first tile overlaps the rest of the list;
+    // the same wave then writes those entries (no other wave touches them)
+    const bool first_done = early && len > 0;
+    if (first_done && outw)
+      issue_tile0([&](int k) {
+        int id = -1;
+        if (k < len) {
+          const int p = L.ids[k];
+          const int b = div_p(p, a.pdiv);
+          const int slot = tbl[b] * P + (p - b * P);
+          const bool valid = slot < a.kv_rows;
+          id = valid ? slot : -1;
+          if ((lane & 7) == 0) {  // one lane per row
+            bad |= valid ? 0 : 1;
+            if (hg == 0) {
+              tok_row[lo + k] = p;
+              slot_row[lo + k] = slot;
+            }
+          }
+        }
+        if ((lane & 7) == 0) L.ids[k] = id;
+        return id;
+      });
+    const int k_from = first_done ? kTileRows : 0;  // entries this loop still converts
     constexpr int kCB = 3;  // entries per thread with their LDS reads together
     for (int k0 = 0; k0 < ntiles * kTileRows; k0 += kCB * kThreads) {
       int pv[kCB], bv[kCB], pg[kCB];
 #pragma unroll
       for (int u = 0; u < kCB; ++u) {
         const int k = k0 + tid + kThreads * u;
-        pv[u] = k < len ? L.ids[k] : 0;
+        pv[u] = k < len && k >= k_from ? L.ids[k] : 0;
       }
 #pragma unroll
       for (int u = 0; u < kCB; ++u) {
@@ -714,7 +749,7 @@ __device__ __forceinline__ void normalize_split(const DecodeArgs& a, const Decod
 #pragma unroll
       for (int u = 0; u < kCB; ++u) {
         const int k = k0 + tid + kThreads * u;
-        if (k < ntiles * kTileRows) {
+        if (k < ntiles * kTileRows && k >= k_from) {
           int id = -1;
           if (k < len) {
             const int slot = pg[u] * P + (pv[u] - bv[u] * P);
@@ -807,10 +842,25 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   };
   // kNorm: the split's range and ids come from the token's normalisation,
   // which enqueues the query rows itself
-  if constexpr (kNorm)
-    normalize_split(a, L, s_bad, t, sidx, hg, lo, len, issue_q);
-  else if (score)
+  // (kNorm, normalisation in stage 1) tile 0's rows from their ids, given
+  // by row
+  auto issue_tile0 = [&](auto&& id_of_row) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int grp = 2 * j + g;
+      const int id = id_of_row(grp * kGroupRows + (lane >> 3));
+      load_row_chunks<0>((id >= 0 ? (const uint8_t*)a.kv + (int64_t)id * kRowBytes : zero_row) +
+                             ld_col,
+                         group_dst(0, grp));
+    }
+  };
+  bool tile0_issued = false;
+  if constexpr (kNorm) {
+    normalize_split(a, L, s_bad, t, sidx, hg, lo, len, issue_q, issue_tile0);
+    tile0_issued = norm_in_stage1(a);
+  } else if (score) {
     issue_q();
+  }
   const int ntiles = (len + kTileRows - 1) / kTileRows;
 
   // candidate ids of this split, -1 for invalid ones and up to the tile edge;
@@ -887,7 +937,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, const DecodeLds
   auto tile_mask = [&](int i) { return (uint32_t)__ballot(id_at(i, lane & 31) >= 0); };
   if constexpr (!kFp8) {
     if (!score) {
-      if (ntiles > 0) issue(0, 0);
+      if (ntiles > 0 && !tile0_issued) issue(0, 0);
       if (ntiles > 1) issue(1, 1);
     }
   }

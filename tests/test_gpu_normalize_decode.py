@@ -132,6 +132,19 @@ def test_bitmap_past_two_ring_stages():
     _run(c, q, kv, 2, oracle_tokens=(0,))
 
 
+def test_bitmap_in_two_ring_stages():
+    # 100,000 positions and 3200 top-k entries: bitmap, table row, D and the
+    # word offsets take more than one ring stage (37,376 B) and at most two,
+    # so tile 0 waits for the finished list instead of loading during it
+    c, q, kv = _small(18, 3, 16, 4, R=2, ctx=100000, top_k=3200, window=64, sinks=4,
+                      page_size=64, unmapped_frac=0.01)
+    max_blocks = c.block_table.shape[1]
+    nwords = (max_blocks * c.page_size + 63) // 64
+    lds = nwords * 8 + max_blocks * 4 + 3200 * 4 + nwords * 4 + (nwords // 64 + 1) * 4
+    assert 37376 < lds <= 2 * 37376
+    _run(c, q, kv, 4, oracle_tokens=(0, 2))
+
+
 def test_topk_longer_than_one_register_round():
     # 2600 top-k entries: past the 2048 the output waves hold in registers,
     # so D is staged in LDS for the dropped count
