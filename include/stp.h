@@ -408,8 +408,11 @@ int stp_sparse_mla_decode_partial_normalized(const uint16_t* q, const uint16_t* 
  * requirements and errors are those of the two calls; the workspace is
  * stp_sparse_mla_decode_workspace(T, H, cap, num_splits) bytes.
  * When every split fits the decode's LDS id list (ceil(cap / S) <= 1120) and
- * the per-token bitmap and page-table row fit 72 KiB
- * (8 * ceil(max_blocks * page_size / 64) + 4 * max_blocks bytes), each decode
+ * the per-token bitmap, page-table row, top-k list and word offsets fit two
+ * of the decode's LDS ring stages (12 * nw + 4 * max_blocks + 4 * top_k +
+ * 4 * (nw / 64 + 1) <= 74,752 bytes, nw = ceil(max_blocks * page_size / 64);
+ * within one stage, 37,376 bytes, the first tile's rows load while the list
+ * is finished), each decode
  * workgroup builds its token's list in LDS and stages its split's slots
  * directly (head group 0 also writes tok_out / slot_out for its split), so
  * no launch stands between the two stages; otherwise the normalisation runs
