@@ -145,6 +145,18 @@ def test_bitmap_in_two_ring_stages():
     _run(c, q, kv, 4, oracle_tokens=(0, 2))
 
 
+def test_slots_past_int32():
+    # pages at the top of the int32 slot range (page size 48): offsets whose
+    # slot would pass 2^31 - 1 are dropped, whole pages and page tails
+    c = workloads.int32_edge_case()
+    rng = np.random.default_rng(19 + 7)
+    q = bf16_dev(workloads.normal_bf16(rng, (c.T, 16, 576)))
+    kv = bf16_dev(workloads.normal_bf16(rng, (c.kv_rows, 576)))
+    for splits in (1, 3):
+        print(f"[normalize_and_decode] int32 edge splits={splits}", flush=True)
+        _run(c, q, kv, splits, oracle_tokens=(0, 1, 2))
+
+
 def test_topk_longer_than_one_register_round():
     # 2600 top-k entries: past the 2048 the output waves hold in registers,
     # so D is staged in LDS for the dropped count

@@ -79,6 +79,43 @@ def test_brute_force_small(seed):
             assert res["slot"][i, j] == c.block_table[r][t // c.page_size] * c.page_size + t % c.page_size
 
 
+def _brute_force_int32(topk_row, q, window, sinks, table_row, P):
+    """Positions 0..q that are members, mapped, and whose slot page * P +
+    offset is at most 2^31 - 1; D entries >= 0 failing any of those count as
+    dropped."""
+    def visible(t):
+        b = t // P
+        if t > q or b >= len(table_row) or table_row[b] < 0:
+            return False
+        return int(table_row[b]) * P + t % P <= 2**31 - 1
+    D = [int(t) for t in topk_row]
+    S = [t for t in range(q + 1)
+         if ((t in D) or (window > 0 and q - window < t) or (t < sinks)) and visible(t)]
+    dropped = sum(1 for t in D if t >= 0 and not visible(t))
+    return S, dropped
+
+
+def test_slots_past_int32_are_dropped():
+    c = workloads.int32_edge_case()
+    res = oracle.normalize(c.topk, c.req_id, c.q_pos, c.window, c.num_sinks, c.block_table,
+                           c.page_size, c.cap)
+    lost = 0
+    for i in range(c.T):
+        r = c.req_id[i]
+        S, nd = _brute_force_int32(c.topk[i], int(c.q_pos[i]), c.window, c.num_sinks,
+                                   c.block_table[r], c.page_size)
+        n = res["count"][i]
+        assert list(res["tok"][i, :n]) == S
+        assert res["dropped"][i] == nd
+        slots = [int(c.block_table[r][t // 48]) * 48 + t % 48 for t in S]
+        assert list(res["slot"][i, :n]) == slots and max(slots, default=0) <= 2**31 - 1
+        if r == 0:  # the sinks sit in page 0's kept offsets; page 1 contributes nothing
+            assert all(t < 32 or t >= 96 for t in S) and {0, 1, 2} <= set(S)
+            lost += sum(1 for t in range(32, min(96, int(c.q_pos[i]) + 1))
+                        if t in set(int(x) for x in c.topk[i]))
+    assert lost > 0  # the case does exercise the rule
+
+
 def test_duplicates_count_once_and_order_free():
     c = workloads.random_small_case(5, T=2, R=2, ctx=200, top_k=30)
     base = oracle.normalize(c.topk, c.req_id, c.q_pos, c.window, c.num_sinks, c.block_table,

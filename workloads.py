@@ -163,6 +163,21 @@ def ragged_case(seed=2100, batch=128, n_long=8, short_ctx=96, long_ctx=32768, he
                       extra={"contexts": ctxs, "variant": variant})
 
 
+def int32_edge_case():
+    """A small batch whose tables hold pages at the top of the int32 slot
+    range (page size 48): page (2^31 - 1) // 48 keeps offsets 0..31 within
+    int32 and loses 32..47, the page after it loses all 48."""
+    c = random_small_case(19, T=6, heads=16, R=2, ctx=400, top_k=80, window=5, sinks=3,
+                                    page_size=48, unmapped_frac=0.0)
+    top = (2**31 - 1) // 48
+    c.block_table[0, 0] = top        # slots top*48 .. top*48 + 31 fit, + 32 .. + 47 do not
+    c.block_table[0, 1] = top + 1    # no slot of this page fits
+    c.block_table[1, 2] = top + 5
+    c.req_id[:3] = [0, 1, 0]
+    c.q_pos[:3] = [350, 380, 47]
+    return c
+
+
 def clustered_topk(rng, ctx, top_k, run=16):
     """top_k ids as top_k/run non-overlapping runs of `run` consecutive tokens."""
     nruns = top_k // run
