@@ -1102,8 +1102,9 @@ def gqa_cpu_baseline(c, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path "
+              "has no multi-GPU mode (it would shard by request, with no exchange).",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
